@@ -1,0 +1,216 @@
+"""HIP path vs the fp64 oracle, element by element, through the C ABI.
+
+Bars: max|gpu - oracle| / max|oracle| <= 2e-2 for bf16 inputs (fp32 state and
+accumulation), <= 1e-4 for fp32 inputs; the same bound separately for final
+states.  Integer-like outputs (the conv-state shift) are compared bit-exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from state_space_sequence_ssd_amd import inputs, ssd
+from tests.gpu_helpers import BF, DEV, gpu_layer, oracle_layer, rel, split_xbc, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+TOL = {True: 2e-2, False: 1e-4}
+
+
+def W(name, batch, L, H, G, bf16=True, conv=False, init=0.0, lens=None):
+    if lens is not None:
+        L = int(np.sum(lens))
+    return inputs.ScanWorkload(name, batch, L, H, G, bf16=bf16, conv=conv, final_state=True,
+                               packed_lengths=None if lens is None else np.asarray(lens),
+                               init_std=init)
+
+
+SMALL = [
+    # (workload, seg_chunks)
+    (W("bf16_conv_b2_l300_h16_g4_init", 2, 300, 16, 4, conv=True, init=0.3), 0),
+    (W("bf16_b1_l129_h8_g2", 1, 129, 8, 2), 0),
+    (W("bf16_b3_l128_h4_g4", 3, 128, 4, 4), 0),
+    (W("bf16_b1_l1_h8_g1_init", 1, 1, 8, 1, init=0.3), 0),
+    (W("bf16_seg1_b1_l700_h8_g2_init", 1, 700, 8, 2, init=0.3), 1),
+    (W("bf16_seg2_conv_b2_l1000_h8_g8", 2, 1000, 8, 8, conv=True), 2),
+    (W("bf16_packed_h8_g2_init", 1, 0, 8, 2, init=0.3, lens=[1, 3, 200, 129, 128, 64, 300, 2]), 0),
+    (W("bf16_packed_seg1_h8_g2_init", 1, 0, 8, 2, init=0.3, lens=[1, 3, 200, 129, 128, 64, 300, 2]), 1),
+    (W("bf16_packed_conv_h16_g8", 1, 0, 16, 8, conv=True, lens=[77, 5, 260]), 0),
+    (inputs.tiny_fp32(), 0),
+    (W("fp32_conv_b2_l200_h8_g2_init", 2, 200, 8, 2, bf16=False, conv=True, init=0.3), 0),
+    (W("fp32_seg1_b1_l300_h4_g1_init", 1, 300, 4, 1, bf16=False, init=0.3), 1),
+    (W("fp32_packed_h4_g2_init", 1, 0, 4, 2, bf16=False, init=0.3, lens=[130, 1, 7, 128]), 0),
+]
+
+
+@pytest.mark.parametrize("w,seg", SMALL, ids=[f"{w.name}" for w, _ in SMALL])
+def test_layer_small(w, seg):
+    print(f"case {w.name} seg_chunks={seg}", flush=True)
+    d = inputs.make_scan_inputs(w, seed=11)
+    y, fs = gpu_layer(d, w, seg_chunks=seg)
+    ry, rf = oracle_layer(d, w)
+    ey, ef = rel(to_np(y), ry), rel(to_np(fs), rf)
+    print(f"  y rel err {ey:.3e}  final-state rel err {ef:.3e}")
+    assert ey <= TOL[w.bf16] and ef <= TOL[w.bf16]
+
+
+def test_empty_sequence_keeps_initial_state():
+    w = W("bf16_l0", 2, 0, 8, 2, init=0.3)
+    d = inputs.make_scan_inputs(w, seed=3)
+    y, fs = gpu_layer(d, w)
+    assert y.numel() == 0
+    assert torch.equal(fs.cpu(), torch.from_numpy(d["initial_state"]))
+
+
+def test_repeat_runs_bitwise_identical():
+    w = W("bf16_conv_b2_l600_h16_g4", 2, 600, 16, 4, conv=True, init=0.3)
+    d = inputs.make_scan_inputs(w, seed=13)
+    y1, f1 = gpu_layer(d, w, seg_chunks=2)
+    y2, f2 = gpu_layer(d, w, seg_chunks=2)
+    assert torch.equal(y1, y2) and torch.equal(f1, f2)
+
+
+def test_segmentation_invariance():
+    """Different segment splits of one sequence agree with each other and the oracle."""
+    w = W("bf16_b1_l1500_h8_g2_init", 1, 1500, 8, 2, init=0.3)
+    d = inputs.make_scan_inputs(w, seed=17)
+    ry, rf = oracle_layer(d, w)
+    for seg in (0, 1, 3, 12):
+        y, fs = gpu_layer(d, w, seg_chunks=seg)
+        assert rel(to_np(y), ry) <= 2e-2 and rel(to_np(fs), rf) <= 2e-2, seg
+
+
+# ---------------------------------------------------------------------------
+# conv alone (bf16 + fp32, packed, conv state in/out)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("bf16", [True, False])
+def test_conv_states_and_packing(bf16):
+    r = np.random.default_rng(5)
+    CH, lens = 48, [2, 40, 1, 70]
+    L = sum(lens)
+    x = inputs.normal((1, L, CH), 1.0, 7, 1, bf16)
+    w = (r.standard_normal((CH, 4)) * 0.5).astype(np.float32)
+    b = (r.standard_normal(CH) * 0.1).astype(np.float32)
+    st_in = inputs.normal((len(lens), 3, CH), 1.0, 7, 2, bf16)
+    seq = np.repeat(np.arange(len(lens), dtype=np.int32), lens)
+    dt = BF if bf16 else torch.float32
+    so = torch.zeros((len(lens), 3, CH), dtype=dt, device=DEV)
+    out = ssd.ssd_conv1d_silu(to_dev(x, dt), to_dev(w), bias=to_dev(b), seq_idx=to_dev(seq),
+                              num_seqs=len(lens), conv_state_in=to_dev(st_in, dt), conv_state_out=so)
+    torch.cuda.synchronize()
+    ref, rso = oracle.conv1d_silu(x, w, bias=b, seq_idx=seq, num_seqs=len(lens), conv_state_in=st_in,
+                                  want_state_out=True)
+    assert rel(to_np(out), ref) <= TOL[bf16]
+    assert np.array_equal(to_np(so), rso), "conv state export must be exact"
+
+
+def test_conv_batch_mode_strided_input():
+    """conv on a strided view (token stride > channels), batch rows, no state."""
+    H, G = 8, 2
+    w_ = W("c", 3, 333, H, G, conv=True)
+    d = inputs.make_scan_inputs(w_, seed=9)
+    CD = w_.conv_dim
+    big = torch.zeros((3, 333, CD + 64), dtype=BF, device=DEV)
+    big[..., 16:16 + CD] = to_dev(d["xBC"], BF)
+    xv = big[..., 16:16 + CD]
+    out = ssd.ssd_conv1d_silu(xv, to_dev(d["conv_w"]))
+    torch.cuda.synchronize()
+    ref = oracle.conv1d_silu(d["xBC"], d["conv_w"])
+    assert rel(to_np(out), ref) <= 2e-2
+
+
+# ---------------------------------------------------------------------------
+# decode step
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("bf16,conv", [(True, True), (True, False), (False, True), (False, False)])
+def test_decode_small(bf16, conv):
+    w = inputs.DecodeWorkload("dec", 3, 16, 4, 1, bf16=bf16)
+    d = inputs.make_decode_small_inputs(w, seed=21, layer=0)
+    st = inputs.decode_state_host(w, 21, 0)
+    dt = BF if bf16 else torch.float32
+    state = to_dev(st)
+    cs = to_dev(d["conv_state"], dt) if conv else None
+    y = ssd.ssd_decode_step(to_dev(d["xBC"], dt), to_dev(d["dt"], dt), to_dev(d["A"]), state,
+                            w.nheads, w.ngroups, dt_bias=to_dev(d["dt_bias"]), D=to_dev(d["D"]),
+                            conv_state=cs, conv_weight=to_dev(d["conv_w"]) if conv else None)
+    torch.cuda.synchronize()
+    ry, rs, rc = oracle.decode_step(d["xBC"], d["dt"], d["dt_bias"], d["A"], d["D"], st, w.nheads,
+                                    64, 128, w.ngroups, conv_w=d["conv_w"] if conv else None,
+                                    conv_state=d["conv_state"] if conv else None)
+    assert rel(to_np(y), ry) <= TOL[bf16]
+    assert rel(to_np(state), rs) <= TOL[bf16]
+    if conv:
+        assert np.array_equal(to_np(cs), rc)
+
+
+def test_prefill_then_decode_chain():
+    """GPU prefill of L tokens (conv state + final state out) then GPU decode of
+    token L == oracle prefill of L+1 tokens."""
+    H, G, L = 8, 2, 257
+    w = W("chain", 1, L + 1, H, G, conv=True, init=0.3)
+    d = inputs.make_scan_inputs(w, seed=23)
+    xbc = to_dev(d["xBC"], BF)
+    cso = torch.zeros((1, 3, w.conv_dim), dtype=BF, device=DEV)
+    v = ssd.ssd_conv1d_silu(xbc[:, :L], to_dev(d["conv_w"]), conv_state_out=cso)
+    x, B, C = split_xbc(v, H, G)
+    fs = torch.zeros((1, H, 64, 128), device=DEV)
+    ssd.ssd_chunk_scan_fwd(x, to_dev(d["dt"], BF)[:, :L], to_dev(d["A"]), B, C,
+                           dt_bias=to_dev(d["dt_bias"]), D=to_dev(d["D"]),
+                           initial_state=to_dev(d["initial_state"]), final_state=fs)
+    yd = ssd.ssd_decode_step(xbc[:, L].contiguous(), to_dev(d["dt"], BF)[:, L].contiguous(), to_dev(d["A"]),
+                             fs, H, G, dt_bias=to_dev(d["dt_bias"]), D=to_dev(d["D"]), conv_state=cso,
+                             conv_weight=to_dev(d["conv_w"]))
+    torch.cuda.synchronize()
+    ry, rf = oracle_layer(d, w)
+    assert rel(to_np(yd), ry[:, L]) <= 2e-2
+    assert rel(to_np(fs), rf) <= 2e-2
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, in the launch configuration the benchmark times,
+# checked on sampled heads / rows that the oracle computes exactly
+# ---------------------------------------------------------------------------
+def _full(w, heads, rows=None):
+    print(f"case {w.name} heads={heads} rows={rows}", flush=True)
+    d = inputs.make_scan_inputs(w, seed=1)
+    y, fs = gpu_layer(d, w)
+    ry, rf = oracle_layer(d, w, heads=heads, rows=rows)
+    yg = to_np(y[rows if rows is not None else slice(None)][:, :, heads])
+    fg = to_np(fs[rows if rows is not None else slice(None)][:, heads])
+    ey, ef = rel(yg, ry), rel(fg, rf)
+    print(f"  y rel err {ey:.3e}  final-state rel err {ef:.3e}")
+    assert np.all(np.isfinite(to_np(y))), "non-finite output"
+    assert ey <= 2e-2 and ef <= 2e-2
+
+
+def test_full_nemotron_h_8b_sampled():
+    _full(inputs.nemotron_h_8b(), heads=[0, 17, 64, 127], rows=[0, 3])
+
+
+def test_full_nemotron3_nano_sampled():
+    _full(inputs.nemotron3_nano(), heads=[0, 31, 63])
+
+
+def test_full_packed_3b_sampled():
+    _full(inputs.packed_3b(), heads=[0, 21, 39])
+
+
+def test_full_decode_layer_sampled():
+    w = inputs.decode_29_layers()
+    d = inputs.make_decode_small_inputs(w, seed=4, layer=0)
+    state = inputs.decode_state_device(w, 4, 0, DEV)
+    rows = [0, 131, 255]
+    st_rows = state[rows].cpu().numpy()
+    cs = to_dev(d["conv_state"], BF)
+    y = ssd.ssd_decode_step(to_dev(d["xBC"], BF), to_dev(d["dt"], BF), to_dev(d["A"]), state,
+                            w.nheads, w.ngroups, dt_bias=to_dev(d["dt_bias"]), D=to_dev(d["D"]),
+                            conv_state=cs, conv_weight=to_dev(d["conv_w"]))
+    torch.cuda.synchronize()
+    ry, rs, rc = oracle.decode_step(d["xBC"][rows], d["dt"][rows], d["dt_bias"], d["A"], d["D"], st_rows,
+                                    w.nheads, 64, 128, w.ngroups, conv_w=d["conv_w"],
+                                    conv_state=d["conv_state"][rows])
+    assert rel(to_np(y[rows]), ry) <= 2e-2
+    assert rel(to_np(state[rows]), rs) <= 2e-2
+    # the conv-state shift of every row is exact
+    full_shift = np.concatenate([d["conv_state"][:, 1:], d["xBC"][:, None, :]], axis=1)
+    assert np.array_equal(to_np(cs), full_shift)
