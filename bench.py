@@ -1,0 +1,320 @@
+"""Benchmark of the Mamba-2 SSD layer hot path on one MI355X.
+
+One step = one pass of the prefill hot path over one batch of the
+Nemotron-H 8B layer shape (batch 4 x 4096 tokens, 128 heads x 64, d_state
+128, 8 groups): the depthwise conv1d(4)+SiLU on x|B|C, then the chunked SSD
+scan (chunk 128) writing y and the final states.  Inputs are synthetic and
+already resident in HBM.  The headline value is layer tokens/s.
+
+The decode step at batch 256 through 29 Mamba-2 layers (1 GiB fp32 state per
+layer) is timed in the same run and reported as HBM GB/s.
+
+Per-kernel times come from HIP events recorded on the stream the kernels
+run on (torch's current stream, which the C ABI launches on).
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+PROFILES = os.path.join(ROOT, "profiles")
+SCAN_SOURCES = ["chunk_scan.hip", "common.h", "kernels.h"]
+CONV_SOURCES = ["conv1d_silu.hip", "common.h", "kernels.h"]
+DECODE_SOURCES = ["decode_step.hip", "common.h", "kernels.h"]
+
+
+def source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "state_space_sequence_ssd_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel_tag, files):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, or None
+    when the kernel source changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"traffic_{kernel_tag}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != source_hash(files):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def scan_algorithmic_bytes(w, with_final=True):
+    """Each input / output tensor of the scan moved once (chunk states excluded)."""
+    T = w.batch * w.seqlen
+    H, G, P, N = w.nheads, w.ngroups, w.headdim, w.dstate
+    per_tok = 2 * (H * P) * 2 + 2 * (G * N) * 2 + H * 2      # x, y, B, C, dt (bf16)
+    states = w.num_seqs * H * P * N * 4 if with_final else 0
+    return T * per_tok + states + 3 * H * 4
+
+
+def scan_flops(w):
+    """Useful flops: causal triangles counted once, C B^T once per (chunk, group)."""
+    T = w.batch * w.seqlen
+    H, G, P, N, Q = w.nheads, w.ngroups, w.headdim, w.dstate, w.chunk
+    return T * (G * (Q + 1) * N + H * (Q + 1) * P + 4 * H * P * N)
+
+
+def conv_algorithmic_bytes(w):
+    return w.batch * w.seqlen * w.conv_dim * 2 * 2 + w.conv_dim * 4 * 4
+
+
+def decode_algorithmic_bytes(dw):
+    H, G, P, N = dw.nheads, dw.ngroups, dw.headdim, dw.dstate
+    CD = dw.conv_dim
+    b = dw.batch
+    return (2 * b * H * P * N * 4            # state read + write
+            + b * CD * 2                     # token
+            + 2 * b * (dw.conv_width - 1) * CD * 2   # conv state read + write
+            + b * H * P * 2 + b * H * 2      # y, dt
+            + CD * dw.conv_width * 4 + 3 * H * 4)
+
+
+def cpu_baseline(w, d, max_heads):
+    """The fp64 oracle (as it stands) on a bounded sample of the same workload:
+    batch row 0, all tokens, the first `max_heads` heads with their groups'
+    conv channels.  Scaled to whole-layer tokens/s by the head fraction."""
+    import numpy as np
+    import oracle
+    H, G, P, N = w.nheads, w.ngroups, w.headdim, w.dstate
+    heads = list(range(max_heads))
+    hpg = H // G
+    groups = sorted({h // hpg for h in heads})
+    xch = np.arange(0, max_heads * P)
+    bch = np.concatenate([H * P + np.arange(g * N, (g + 1) * N) for g in groups])
+    cch = np.concatenate([H * P + G * N + np.arange(g * N, (g + 1) * N) for g in groups])
+    ch = np.concatenate([xch, bch, cch])
+    xbc = np.ascontiguousarray(d["xBC"][:1][..., ch])
+    cw = d["conv_w"][ch]
+    t0 = time.perf_counter()
+    v = oracle.conv1d_silu(xbc, cw)
+    L = w.seqlen
+    x = v[..., :len(xch)].reshape(1, L, max_heads, P)
+    B = v[..., len(xch):len(xch) + len(bch)].reshape(1, L, len(groups), N)
+    C = v[..., len(xch) + len(bch):].reshape(1, L, len(groups), N)
+    oracle.ssd_scan(x, d["dt"][:1][:, :, heads], d["dt_bias"][heads], d["A"][heads], B, C,
+                    d["D"][heads], want_final_state=True)
+    el = time.perf_counter() - t0
+    tokens_equiv = L * (max_heads / H)
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    return {"value": tokens_equiv / el, "unit": "tokens/s/layer", "cores": min(threads, max_heads),
+            "kind": "oracle",
+            "sample": f"batch row 0 of 4, {L} tokens, {max_heads} of {H} heads (+ their conv "
+                      f"channels), fp64 sequential recurrence, {el:.1f} s; scaled by heads",
+            "seconds": el}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle timing (profiler runs)")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
+    ap.add_argument("--cpu-heads", type=int, default=32)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for HBM counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from state_space_sequence_ssd_amd import inputs, ssd
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ssd.load_library()
+    bf = torch.bfloat16
+
+    # ---------------- prefill workload (Nemotron-H 8B layer shape) ----------------
+    w = inputs.nemotron_h_8b()
+    d = inputs.make_scan_inputs(w, seed=1)
+    H, G, P, N = w.nheads, w.ngroups, w.headdim, w.dstate
+    xbc = torch.from_numpy(d["xBC"]).to(dev, bf)
+    conv_w = torch.from_numpy(d["conv_w"]).to(dev)
+    dt = torch.from_numpy(d["dt"]).to(dev, bf)
+    A = torch.from_numpy(d["A"]).to(dev)
+    D = torch.from_numpy(d["D"]).to(dev)
+    dt_bias = torch.from_numpy(d["dt_bias"]).to(dev)
+    conv_out = torch.empty_like(xbc)
+    x = conv_out[..., :H * P].view(w.batch, w.seqlen, H, P)
+    Bm = conv_out[..., H * P:H * P + G * N].view(w.batch, w.seqlen, G, N)
+    Cm = conv_out[..., H * P + G * N:].view(w.batch, w.seqlen, G, N)
+    y = torch.empty((w.batch, w.seqlen, H, P), dtype=bf, device=dev)
+    fs = torch.empty((w.batch, H, P, N), dtype=torch.float32, device=dev)
+    ws_bytes = ssd.ssd_chunk_scan_workspace_size(x, dt, A, Bm, Cm)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        ssd.ssd_conv1d_silu(xbc, conv_w, out=conv_out)
+        if ev is not None:
+            ev[1].record(stream)
+        ssd.ssd_chunk_scan_fwd(x, dt, A, Bm, Cm, dt_bias=dt_bias, D=D, final_state=fs, y=y,
+                               workspace=ws)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    conv_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    scan_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    ms_per_step = total_ms / args.steps
+    tokens = w.batch * w.seqlen
+    value = tokens / (ms_per_step / 1e3)
+
+    conv_avg, scan_avg = float(np.mean(conv_ms)), float(np.mean(scan_ms))
+    scan_bytes = scan_algorithmic_bytes(w)
+    conv_bytes = conv_algorithmic_bytes(w)
+    kernels = {
+        "ssd_chunk_scan_fwd": {
+            "avg_ms": scan_avg, "median_ms": float(np.median(scan_ms)),
+            "algorithmic_bytes": scan_bytes, "gbs": scan_bytes / (scan_avg * 1e-3) / 1e9,
+            "hbm_frac": scan_bytes / (scan_avg * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "useful_tflops": scan_flops(w) / (scan_avg * 1e-3) / 1e12,
+            "tokens_per_s": tokens / (scan_avg * 1e-3),
+            "traffic": read_traffic("chunk_scan_nemotron_h_8b", SCAN_SOURCES)},
+        "ssd_conv1d_silu": {
+            "avg_ms": conv_avg, "median_ms": float(np.median(conv_ms)),
+            "algorithmic_bytes": conv_bytes, "gbs": conv_bytes / (conv_avg * 1e-3) / 1e9,
+            "hbm_frac": conv_bytes / (conv_avg * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "traffic": read_traffic("conv1d_silu_nemotron_h_8b", CONV_SOURCES)},
+    }
+    dom_name = max(kernels, key=lambda k: kernels[k]["avg_ms"])
+    dom = kernels[dom_name]
+    roofline = {"kernel": dom_name, "bound": "hbm", "achieved": round(dom["gbs"], 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom["gbs"] / HBM_PEAK_GBS, 4),
+                "traffic": dom["traffic"]}
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    # ---------------- decode: batch 256 through 29 layers ----------------
+    decode = None
+    if not args.no_decode:
+        dw = inputs.decode_29_layers()
+        layers = []
+        for l in range(dw.layers):
+            dd = inputs.make_decode_small_inputs(dw, seed=4, layer=l)
+            layers.append({
+                "xBC": torch.from_numpy(dd["xBC"]).to(dev, bf),
+                "dt": torch.from_numpy(dd["dt"]).to(dev, bf),
+                "conv_state": torch.from_numpy(dd["conv_state"]).to(dev, bf),
+                "conv_w": torch.from_numpy(dd["conv_w"]).to(dev),
+                "A": torch.from_numpy(dd["A"]).to(dev), "D": torch.from_numpy(dd["D"]).to(dev),
+                "dt_bias": torch.from_numpy(dd["dt_bias"]).to(dev),
+                "state": inputs.decode_state_device(dw, 4, l, dev),
+                "y": torch.empty((dw.batch, dw.nheads, dw.headdim), dtype=bf, device=dev)})
+
+        def dstep(ev=None):
+            for li, L_ in enumerate(layers):
+                if ev is not None and li == 0:
+                    ev[0].record(stream)
+                ssd.ssd_decode_step(L_["xBC"], L_["dt"], L_["A"], L_["state"], dw.nheads, dw.ngroups,
+                                    dt_bias=L_["dt_bias"], D=L_["D"], conv_state=L_["conv_state"],
+                                    conv_weight=L_["conv_w"], y=L_["y"])
+                if ev is not None and li == 0:
+                    ev[1].record(stream)
+
+        for _ in range(2):
+            dstep()
+        torch.cuda.synchronize()
+        devs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.decode_steps)]
+        d0 = torch.cuda.Event(enable_timing=True)
+        d1 = torch.cuda.Event(enable_timing=True)
+        d0.record(stream)
+        for i in range(args.decode_steps):
+            dstep(devs[i])
+        d1.record(stream)
+        torch.cuda.synchronize()
+        dms = d0.elapsed_time(d1) / args.decode_steps
+        one_layer_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in devs]))
+        dbytes = decode_algorithmic_bytes(dw)
+        gbs = dbytes * dw.layers / (dms * 1e-3) / 1e9
+        decode = {"metric": "decode-step HBM GB/s", "value": round(gbs, 1), "unit": "GB/s",
+                  "frac": round(gbs / HBM_PEAK_GBS, 4), "ms_per_29_layers": round(dms, 4),
+                  "tokens_per_s": round(dw.batch / (dms * 1e-3), 1),
+                  "layer_kernel_avg_ms": round(one_layer_ms, 4),
+                  "algorithmic_bytes_per_layer": dbytes,
+                  "traffic": read_traffic("decode_step_b256_h128", DECODE_SOURCES),
+                  "workload": dw.name}
+        del layers
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, d, args.cpu_heads)
+
+    line = {
+        "metric": "SSD scan tokens/s/layer @Nemotron-H-8B shape; decode-step HBM GB/s",
+        "value": round(value, 1),
+        "unit": "tokens/s/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seqlen, "nheads": H,
+                   "headdim": P, "dstate": N, "ngroups": G, "chunk": w.chunk,
+                   "step": "conv1d(4)+SiLU then chunked SSD scan with final states",
+                   "parallelism": "single GPU"},
+        "wall_s_timed": round(wall, 4),
+        "roofline": roofline,
+        "cpu_baseline": None if cpu is None else {k: v for k, v in cpu.items() if k != "seconds"},
+        "kernels": kernels,
+        "decode": decode,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

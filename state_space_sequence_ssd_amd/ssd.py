@@ -158,11 +158,12 @@ def _scan_args(x, dt, A, B, C, dt_bias, D, seq_idx, num_seqs, initial_state, fin
                chunk_size, seg_chunks) -> SsdScanArgs:
     batch, L, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
-    for t, name, inner in ((x, "x", P), (y, "y", P), (B, "B", N), (C, "C", N)):
-        if t is not None and (t.stride(3) != 1 or t.stride(2) != inner):
-            raise ValueError(f"{name}: the last two dims must be packed (strides ({inner}, 1))")
-    if dt.stride(2) != 1:
-        raise ValueError("dt: head dim must be unit-stride")
+    if L > 0:
+        for t, name, inner in ((x, "x", P), (y, "y", P), (B, "B", N), (C, "C", N)):
+            if t is not None and (t.stride(3) != 1 or t.stride(2) != inner):
+                raise ValueError(f"{name}: the last two dims must be packed (strides ({inner}, 1))")
+        if dt.stride(2) != 1:
+            raise ValueError("dt: head dim must be unit-stride")
     a = SsdScanArgs()
     a.struct_size = ctypes.sizeof(SsdScanArgs)
     a.dtype = _dtype_code(x)
