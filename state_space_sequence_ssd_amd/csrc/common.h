@@ -19,16 +19,17 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t v) {
   return __uint_as_float(static_cast<uint32_t>(v) << 16);
 }
 
-// Round to nearest even (inputs here are finite).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Round to nearest even: gfx950's v_cvt_pk_bf16_f32.
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
+  return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
 }
 
-// Two floats -> one dword of two bf16 (lo in the low half).
+// Two floats -> one dword of two bf16 (lo in the low half), one instruction.
 __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
