@@ -1,0 +1,571 @@
+// Chunked SSD prefill, bf16 inputs: the fused MFMA chunk kernel for gfx950.
+//
+// Per head, a chunk of Q = 128 tokens with inclusive in-chunk cumulative
+// log-decay cs_i = sum_{k<=i} dt_k A (scalar-times-identity transition of
+// Mamba-2: "Mamba-3: an inference-first state space model"; the block form
+// is the state space duality of "AI Engineering EP6", sec. 8 and 10; chunk
+// 128 from "Nemotron-H style Hybrid Mamba-Transformer 3B feasibility
+// study", sec. 1.4) is
+//
+//   G      = B C^T                                   (C B^T, K = d_state)
+//   M[i][j] = G[j][i] exp(cs_i - cs_j) dt_j  (j < i),  G[i][i] dt_i + D (j = i)
+//   y      = exp(cs_i) (C_i H_prev^T)  +  sum_j M[i][j] x_j
+//   H      = exp(cs_last) H_prev  +  sum_j w_j x_j B_j^T,  w_j = exp(cs_last - cs_j) dt_j
+//
+// and every exponent is a difference cs_i - cs_j with j <= i (<= 0).
+//
+// One workgroup runs one segment of one sequence for one head with 4 waves
+// (one per SIMD).  Wave w owns output rows i in [32w, 32w+32): its w+1 causal
+// C B^T tiles, turned into the decay-masked M in registers and fed straight
+// back as the MFMA operand of the intra-chunk product (the accumulator holds
+// 4+4 rows per lane, used as a permuted K order that the other operand
+// follows), its state->output tiles, and a share of the 8 state tiles dealt
+// 4/3/1/0 so every wave runs 60-64 MFMAs per chunk.  All products are
+// v_mfma_f32_32x32x16_bf16.
+//
+// Memory path, MI355X-specific:
+//   * x and B arrive by global->LDS direct loads (global_load_lds_dwordx4),
+//     double-buffered one chunk ahead, into token-major tiles whose 16-byte
+//     blocks are XOR-swizzled per row; no VGPR staging and no transposing
+//     copies.
+//   * operands whose contraction runs over tokens (B^T and x^T) are read
+//     straight from those token-major tiles with the LDS transpose read
+//     ds_read_b64_tr_b16: in each 16-lane group, lane s points at row
+//     k0 + s/4, columns c0 + 4(s%4)..+3, and lane i then holds rows
+//     k0..k0+3 of column c0 + i -- four K values of its MFMA column.
+//   * the running state stays on chip: fp32 in the owning waves' MFMA
+//     accumulators, bf16 in LDS as the operand of the state->output product.
+//   * C goes global -> registers (each wave its own 32 rows) right after the
+//     k-loop that last reads the current ones.
+#include "scan_items.h"
+
+namespace ssd {
+
+namespace {
+
+constexpr int kThr = 256;  // 4 waves, one per SIMD
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Row swizzles of the 16-byte blocks: conflict-free for 8 (or 16) lanes on
+// consecutive rows of one block, and for the transpose reads (4 consecutive
+// rows x 2 adjacent blocks).
+__device__ __forceinline__ int swz16(int r) { return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8); }
+__device__ __forceinline__ int swz8(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// byte offset of element (row, col) in a 256-byte-row tile (128 bf16) / 128-byte-row tile (64 bf16)
+__device__ __forceinline__ int off256(int row, int col) {
+  return row * 256 + ((((col >> 3) ^ swz16(row))) << 4) + ((col & 7) << 1);
+}
+__device__ __forceinline__ int off128(int row, int col) {
+  return row * 128 + ((((col >> 3) ^ swz8(row))) << 4) + ((col & 7) << 1);
+}
+
+struct Smem {
+  uint8_t B[kChunk * 256];    // B[j][n], token-major
+  uint8_t X[kChunk * 128];    // x[j][p], token-major
+  uint8_t H[kHeadDim * 256];  // running state H[p][n] in bf16
+  float cs[kChunk];
+  float dt[kChunk];
+  float w[kChunk];
+  float v[kChunk];
+  float misc[4];              // exp(cs_last), cs_last
+};
+// two workgroups per CU: each fits in half of the 160 KiB LDS
+static_assert(sizeof(Smem) <= 80 * 1024, "LDS budget of one of two workgroups per CU");
+
+
+// state tiles (n-block nb, p-block pb) of H^T owned by wave w in the full pass
+constexpr int kNS[4] = {4, 3, 1, 0};
+constexpr int kSnb[4][4] = {{0, 0, 1, 1}, {2, 2, 3, 0}, {3, 0, 0, 0}, {0, 0, 0, 0}};
+constexpr int kSpb[4][4] = {{0, 1, 0, 1}, {0, 1, 0, 0}, {1, 0, 0, 0}, {0, 0, 0, 0}};
+constexpr int kDtWave = 3;  // the wave that computes the next chunk's dt / cumsum (no state tiles)
+
+template <bool kFull, int W> struct Cfg {
+  static constexpr int NCB = kFull ? W + 1 : 0;
+  static constexpr int NS = kFull ? kNS[W] : 2;
+  __host__ __device__ static constexpr int nb(int t) { return kFull ? kSnb[W][t] : W; }
+  __host__ __device__ static constexpr int spb(int t) { return kFull ? kSpb[W][t] : t; }
+  __host__ __device__ static constexpr bool uses_spb(int q) {
+    for (int t = 0; t < NS; ++t)
+      if (spb(t) == q) return true;
+    return false;
+  }
+  // distinct n-blocks of the state tiles: one B^T fragment each per k-step.
+  // slots.s[t] = fragment slot of tile t, slots.nb[u] = n-block of slot u.
+  struct Slots {
+    int s[4], nb[4], n;
+  };
+  __host__ __device__ static constexpr Slots make_slots() {
+    Slots r{{0, 0, 0, 0}, {0, 0, 0, 0}, 0};
+    for (int t = 0; t < NS; ++t) {
+      int u = 0;
+      while (u < r.n && r.nb[u] != nb(t)) ++u;
+      if (u == r.n) r.nb[r.n++] = nb(t);
+      r.s[t] = u;
+    }
+    return r;
+  }
+  static constexpr Slots kSlots = make_slots();
+  static constexpr int NNB = kSlots.n;
+  __host__ __device__ static constexpr int slot(int t) { return kSlots.s[t]; }
+  __host__ __device__ static constexpr int slot_nb(int u) { return kSlots.nb[u]; }
+  // every tile's slot holds its own n-block, and slots are all distinct
+  __host__ __device__ static constexpr bool slots_ok() {
+    for (int t = 0; t < NS; ++t)
+      if (slot(t) >= NNB || slot_nb(slot(t)) != nb(t)) return false;
+    for (int u = 0; u < NNB; ++u)
+      for (int v = 0; v < u; ++v)
+        if (slot_nb(u) == slot_nb(v)) return false;
+    return true;
+  }
+};
+static_assert(Cfg<true, 0>::slots_ok() && Cfg<true, 0>::NNB == 2, "state tile slots");
+static_assert(Cfg<true, 1>::slots_ok() && Cfg<true, 1>::NNB == 2, "state tile slots");
+static_assert(Cfg<true, 2>::slots_ok() && Cfg<true, 2>::NNB == 1, "state tile slots");
+static_assert(Cfg<true, 3>::slots_ok() && Cfg<true, 3>::NNB == 0, "state tile slots");
+static_assert(Cfg<false, 0>::slots_ok() && Cfg<false, 0>::NNB == 1, "state tile slots");
+static_assert(Cfg<false, 3>::slots_ok() && Cfg<false, 3>::NNB == 1, "state tile slots");
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x2 tr_read(const uint8_t *p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4 *)(const __attribute__((address_space(3))) uint8_t *)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// 8 K values (token rows k0..k0+7) of this lane's MFMA column c0g + (lane % 16),
+// from a token-major tile, by two transpose reads.
+template <int kRowBytes>
+__device__ __forceinline__ bf16x8 tr_frag(const uint8_t *tile, int k0, int c0g) {
+  const int s16 = threadIdx.x & 15;
+  const int r = k0 + (s16 >> 2);
+  const int col = c0g + 4 * (s16 & 3);
+  const u32x2 lo = tr_read(tile + (kRowBytes == 256 ? off256(r, col) : off128(r, col)));
+  const u32x2 hi = tr_read(tile + (kRowBytes == 256 ? off256(r + 4, col) : off128(r + 4, col)));
+  return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+
+// w_j x_j for the 8 K values of a fragment (K rows k0..k0+7 in element order),
+// rounded to bf16 as the MFMA operand.
+__device__ __forceinline__ bf16x8 scale_frag(bf16x8 x, float4 wa, float4 wb) {
+  const u32x4 u = __builtin_bit_cast(u32x4, x);
+  u32x4 o;
+  o[0] = pack2_bf16(lo_bf16(u[0]) * wa.x, hi_bf16(u[0]) * wa.y);
+  o[1] = pack2_bf16(lo_bf16(u[1]) * wa.z, hi_bf16(u[1]) * wa.w);
+  o[2] = pack2_bf16(lo_bf16(u[2]) * wb.x, hi_bf16(u[2]) * wb.y);
+  o[3] = pack2_bf16(lo_bf16(u[3]) * wb.z, hi_bf16(u[3]) * wb.w);
+  return __builtin_bit_cast(bf16x8, o);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
+// row broadcasts (no LDS traffic).
+__device__ __forceinline__ float wave_incl_scan(float x) {
+#define SSD_DPP_ADD(ctrl, rmask, bc)                                                              \
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), ctrl, rmask, 0xF, bc))
+  SSD_DPP_ADD(0x111, 0xF, true);   // row_shr:1
+  SSD_DPP_ADD(0x112, 0xF, true);   // row_shr:2
+  SSD_DPP_ADD(0x114, 0xF, true);   // row_shr:4
+  SSD_DPP_ADD(0x118, 0xF, true);   // row_shr:8
+  SSD_DPP_ADD(0x142, 0xA, false);  // row_bcast:15 -> rows 1, 3
+  SSD_DPP_ADD(0x143, 0xC, false);  // row_bcast:31 -> rows 2, 3
+#undef SSD_DPP_ADD
+  return x;
+}
+
+// softplus(z) = log(1 + e^z) with log1p accuracy (u = 1 + e rounded; the
+// factor e / (u - 1) corrects the rounding of u).
+__device__ __forceinline__ float softplus_fast(float z) {
+  if (z > 20.f) return z;
+  const float e = __expf(z);
+  const float u = 1.f + e;
+  return u == 1.f ? e : __logf(u) * (e / (u - 1.f));
+}
+
+// dt, cs, w = exp(cs_last - cs) dt and v = exp(cs_r - cs) dt (r = end of the
+// token's 32-block) of one chunk, by one wave (tokens 2 lane, 2 lane + 1).
+__device__ __forceinline__ void chunk_dt_wave(uint32_t raw, int nv, float bias, float A, float *cs,
+                                              float *dt, float *w, float *v, float *misc) {
+  const int lane = threadIdx.x & 63;
+  const int j0 = 2 * lane;
+  const float d0 = j0 < nv ? softplus_fast(lo_bf16(raw) + bias) : 0.f;
+  const float d1 = j0 + 1 < nv ? softplus_fast(hi_bf16(raw) + bias) : 0.f;
+  const float a1 = d1 * A;
+  const float incl = wave_incl_scan(d0 * A + a1);
+  const float cs1 = incl, cs0 = incl - a1;
+  const float total = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), 63));
+  // cs at the last token of this lane's 32-token block: lanes 15, 31, 47, 63
+  const float e0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), 15));
+  const float e1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), 31));
+  const float e2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), 47));
+  const int blk = lane >> 4;
+  const float cr = blk == 0 ? e0 : blk == 1 ? e1 : blk == 2 ? e2 : total;
+  *reinterpret_cast<float2 *>(cs + j0) = make_float2(cs0, cs1);
+  *reinterpret_cast<float2 *>(dt + j0) = make_float2(d0, d1);
+  *reinterpret_cast<float2 *>(w + j0) = make_float2(__expf(total - cs0) * d0, __expf(total - cs1) * d1);
+  *reinterpret_cast<float2 *>(v + j0) = make_float2(__expf(cr - cs0) * d0, __expf(cr - cs1) * d1);
+  if (lane == 0) {
+    misc[0] = __expf(total);
+    misc[1] = total;
+  }
+}
+
+// Lane id through an empty asm: values derived from it are recomputed in
+// every chunk instead of being hoisted out of the chunk loop, where dozens of
+// loop-invariant addresses and masks would hold registers for the whole kernel.
+__device__ __forceinline__ int opaque_lane() {
+  int l = threadIdx.x & 63;
+  asm volatile("" : "+v"(l));
+  return l;
+}
+
+// Where one lane sits in the MFMA layouts, and the per-lane LDS byte offsets
+// of its operands at k-step 0.  The swizzles only look at the low 4 (B tile) /
+// 3 (x tile) bits of a row, so the transpose read k-step s later, 16 rows
+// further, is + 4096 s in B and + 2048 s in x (an immediate offset), and the
+// row-major 16-byte read of column block 2s + hh is the step-0 offset XOR 32 s.
+template <int NCB> struct LaneGeo {
+  int lane, l32, hh, g16, s16;
+  uint32_t oBt[2][2], oXt[2][2], oBr[NCB > 0 ? NCB : 1], oH[2], oYd[2];
+  template <class Cf> __device__ __forceinline__ void init(int ln) {
+    lane = ln;
+    l32 = ln & 31;
+    hh = ln >> 5;
+    g16 = ln >> 4;
+    s16 = ln & 15;
+    const int trr = 8 * hh + (s16 >> 2);            // transpose-read row at step 0
+    const int trc = 16 * (g16 & 1) + 4 * (s16 & 3);  // ... and column within a 32-block
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      oBt[u][0] = off256(trr, 32 * Cf::slot_nb(u) + trc);
+      oBt[u][1] = off256(trr + 4, 32 * Cf::slot_nb(u) + trc);
+      oXt[u][0] = off128(trr, 32 * u + trc);
+      oXt[u][1] = off128(trr + 4, 32 * u + trc);
+      oH[u] = off256(32 * u + l32, 8 * hh);
+      // x^T reads of the intra-chunk product: rows 32 jb + 16 s2 + 4 hh + s16/4 (+8)
+      oYd[u] = off128(4 * hh + (s16 >> 2), 32 * u + trc);
+    }
+#pragma unroll
+    for (int jb = 0; jb < NCB; ++jb) oBr[jb] = off256(32 * jb + l32, 8 * hh);
+  }
+};
+
+__device__ __forceinline__ bf16x8 trd(const uint8_t *tile, uint32_t lo, uint32_t hi) {
+  const u32x2 a = tr_read(tile + lo);
+  const u32x2 b = tr_read(tile + hi);
+  return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
+}
+
+template <bool kFull, int W>
+__device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &plan, char *ws, const Item &it,
+                                         int item, int h, int g, Smem &sm) {
+  using Cf = Cfg<kFull, W>;
+  constexpr int NCB = Cf::NCB, NS = Cf::NS;
+  constexpr int NX = (Cf::uses_spb(0) ? 1 : 0) + (Cf::uses_spb(1) ? 1 : 0);
+  constexpr int NNB = Cf::NNB;
+  constexpr int NF = NX + NNB + (kFull ? NCB + 2 : 0);
+
+  const bf16_t *xg = reinterpret_cast<const bf16_t *>(p.x) + it.boff * p.x_sb + h * kHeadDim;
+  const bf16_t *Bg = reinterpret_cast<const bf16_t *>(p.B) + it.boff * p.B_sb + g * kDState;
+  const bf16_t *Cg = reinterpret_cast<const bf16_t *>(p.C) + it.boff * p.C_sb + g * kDState;
+  const bf16_t *dtg = reinterpret_cast<const bf16_t *>(p.dt) + it.boff * p.dt_sb + h;
+  bf16_t *yg = reinterpret_cast<bf16_t *>(p.y) + it.boff * p.y_sb + h * kHeadDim;
+  const uint32_t xst = (uint32_t)p.x_st, bst = (uint32_t)p.B_st, cst = (uint32_t)p.C_st;
+  const uint32_t dst = (uint32_t)p.dt_st, yst = (uint32_t)p.y_st;
+  const float bias = p.dt_bias ? p.dt_bias[h] : 0.f;
+  const float Ah = p.A[h];
+  const float Dh = p.D ? p.D[h] : 0.f;
+
+  // x / B tiles of one chunk -> LDS by direct loads: wave w fills token rows
+  // [32w, 32w + 32) of both.  Rows past the segment end repeat its last row
+  // (finite values whose every use is cancelled: dt = 0 there).
+  auto issue_tiles = [&](int ln, int c0, int nv) {
+    const int last = nv - 1;
+    const bf16_t *bc = Bg + (int64_t)c0 * p.B_st;
+    const bf16_t *xc = xg + (int64_t)c0 * p.x_st;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 32 * W + 4 * i + (ln >> 4);
+      const int blk = (ln & 15) ^ swz16(r);
+      __builtin_amdgcn_global_load_lds(bc + (uint32_t)min(r, last) * bst + 8 * blk,
+                                       (lds_void *)(sm.B + (32 * W + 4 * i) * 256), 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 32 * W + 8 * i + (ln >> 3);
+      const int blk = (ln & 7) ^ swz8(r);
+      __builtin_amdgcn_global_load_lds(xc + (uint32_t)min(r, last) * xst + 8 * blk,
+                                       (lds_void *)(sm.X + (32 * W + 8 * i) * 128), 16, 0, 0);
+    }
+  };
+  // C rows i of this wave's i-block: this lane's 8 k-steps of the MFMA operand
+  u32x4 cf[8];
+  auto load_c = [&](int ln, int c0, int nv) {
+    const int ci = 32 * W + (ln & 31);
+    const bf16_t *crow = Cg + (int64_t)c0 * p.C_st + (uint32_t)min(ci, nv - 1) * cst + 8 * (ln >> 5);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) cf[s] = *reinterpret_cast<const u32x4 *>(crow + 16 * s);
+  };
+  auto load_dt_raw = [&](int ln, int c0, int nv) -> uint32_t {
+    const bf16_t *dc = dtg + (int64_t)c0 * p.dt_st;
+    const uint32_t lo = dc[(uint32_t)min(2 * ln, nv - 1) * dst];
+    const uint32_t hi = dc[(uint32_t)min(2 * ln + 1, nv - 1) * dst];
+    return lo | (hi << 16);
+  };
+
+  // state tiles H^T (rows n = 32 nb + 8q + 4hh + 0..3, col p = 32 pb + l32)
+  f32x16 hs[NS > 0 ? NS : 1];
+  auto write_state_lds = [&](int ln) {
+    const int l32 = ln & 31, hh = ln >> 5;
+#pragma unroll
+    for (int t = 0; t < NS; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        u32x2 v;
+        v[0] = pack2_bf16(hs[t][4 * q], hs[t][4 * q + 1]);
+        v[1] = pack2_bf16(hs[t][4 * q + 2], hs[t][4 * q + 3]);
+        *reinterpret_cast<u32x2 *>(sm.H + off256(32 * Cf::spb(t) + l32, 32 * Cf::nb(t) + 8 * q + 4 * hh)) = v;
+      }
+  };
+  {
+    const int ln = threadIdx.x & 63, l32 = ln & 31, hh = ln >> 5;
+    const float *entry = nullptr;
+    if (kFull) {
+      if (it.first) entry = p.init ? p.init + ((int64_t)it.row * p.H + h) * kPN : nullptr;
+      else entry = ws_f32(plan, ws, plan.ws_entry_off) + ((int64_t)item * p.H + h) * kPN;
+    }
+#pragma unroll
+    for (int t = 0; t < NS; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float4 e = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (entry)
+          e = *reinterpret_cast<const float4 *>(entry + (32 * Cf::spb(t) + l32) * kDState + 32 * Cf::nb(t) + 8 * q +
+                                                4 * hh);
+        hs[t][4 * q + 0] = e.x; hs[t][4 * q + 1] = e.y;
+        hs[t][4 * q + 2] = e.z; hs[t][4 * q + 3] = e.w;
+      }
+  }
+
+  float logdecay = 0.f;
+  const int ntok = it.tok1 - it.tok0;
+  if (ntok > 0) {
+    const int ln = threadIdx.x & 63;
+    const int nv0 = min(kChunk, ntok);
+    issue_tiles(ln, it.tok0, nv0);
+    if (kFull) load_c(ln, it.tok0, nv0);
+    if (W == kDtWave)
+      chunk_dt_wave(load_dt_raw(ln, it.tok0, nv0), nv0, bias, Ah, sm.cs, sm.dt, sm.w, sm.v, sm.misc);
+    if (kFull) write_state_lds(ln);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
+    __syncthreads();
+  }
+
+  // Per chunk: k-loop and intra-chunk product (every read of the tiles, H and
+  // cs/dt/w/v), barrier A, the next chunk's loads and dt and this chunk's state
+  // into the same buffers, barrier B, then the y stores.  The other workgroup
+  // on the CU runs while this one waits.
+  f32x16 yo[2];
+  for (int c0 = it.tok0; c0 < it.tok1; c0 += kChunk) {
+    LaneGeo<NCB> L;
+    L.template init<Cf>(opaque_lane());
+    const int ci = 32 * W + L.l32;  // this lane's chunk row i (full pass)
+    const int nv = min(kChunk, it.tok1 - c0);
+    const int c1 = c0 + kChunk;
+    const bool has_next = c1 < it.tok1;
+    const int cn = has_next ? c1 : c0;
+    const int nvn = has_next ? min(kChunk, it.tok1 - c1) : nv;
+    uint32_t raw_next = 0;
+    if (W == kDtWave) raw_next = load_dt_raw(L.lane, cn, nvn);
+
+    const float dec = sm.misc[0];
+    logdecay += sm.misc[1];
+#pragma unroll
+    for (int t = 0; t < NS; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) hs[t][r] *= dec;
+
+    f32x16 G[NCB > 0 ? NCB : 1];
+#pragma unroll
+    for (int t = 0; t < NCB; ++t) G[t] = f32x16{};
+    yo[0] = f32x16{}; yo[1] = f32x16{};
+
+    // k-loop: every accumulator chain of this wave, operands double-buffered
+    auto load_frags = [&](int s, bf16x8 *f, float4 *wv) {
+      int k = 0;
+      if (NX > 0) {
+        wv[0] = *reinterpret_cast<const float4 *>(&sm.w[16 * s + 8 * L.hh]);
+        wv[1] = *reinterpret_cast<const float4 *>(&sm.w[16 * s + 8 * L.hh + 4]);
+      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        if (Cf::uses_spb(q)) f[k++] = trd(sm.X, L.oXt[q][0] + 2048 * s, L.oXt[q][1] + 2048 * s);
+#pragma unroll
+      for (int u = 0; u < NNB; ++u) f[k++] = trd(sm.B, L.oBt[u][0] + 4096 * s, L.oBt[u][1] + 4096 * s);
+      if (kFull) {
+#pragma unroll
+        for (int jb = 0; jb < NCB; ++jb) f[k++] = *reinterpret_cast<const bf16x8 *>(sm.B + (L.oBr[jb] ^ (32 * s)));
+#pragma unroll
+        for (int q = 0; q < 2; ++q) f[k++] = *reinterpret_cast<const bf16x8 *>(sm.H + (L.oH[q] ^ (32 * s)));
+      }
+    };
+    auto mfma_step = [&](int s, const bf16x8 *f, const float4 *wv) {
+      int k = 0;
+      bf16x8 xw[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        if (Cf::uses_spb(q)) xw[q] = scale_frag(f[k++], wv[0], wv[1]);
+#pragma unroll
+      for (int t = 0; t < NS; ++t) hs[t] = mfma32(f[k + Cf::slot(t)], xw[Cf::spb(t)], hs[t]);
+      k += NNB;
+      if (kFull) {
+        const bf16x8 cb = __builtin_bit_cast(bf16x8, cf[s]);
+#pragma unroll
+        for (int jb = 0; jb < NCB; ++jb) G[jb] = mfma32(f[k++], cb, G[jb]);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) yo[q] = mfma32(f[k++], cb, yo[q]);
+      }
+    };
+    {
+      bf16x8 fr[2][NF > 0 ? NF : 1];
+      float4 wr[2][2];
+      load_frags(0, fr[0], wr[0]);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        if (s < 7) load_frags(s + 1, fr[(s + 1) & 1], wr[(s + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_step(s, fr[s & 1], wr[s & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // the C fragments of this chunk are dead: fetch the next chunk's now
+    if (kFull) load_c(L.lane, cn, nvn);
+
+    if (kFull) {
+      // y = exp(cs_i) (C H_prev^T) + M x: scale the state->output part, then the
+      // intra-chunk product accumulates on top of it
+      const float cs_i = sm.cs[ci];
+      const float ecs = __expf(cs_i);
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) yo[q][r] *= ecs;
+      // decay mask, dt and D -> bf16 M operand (rows j, col i) in registers,
+      // then y^T[p][i] += sum_j x[j][p] M[j][i]
+#pragma unroll
+      for (int jb = 0; jb < NCB; ++jb) {
+        bf16x8 Mb[2];
+        if (jb < W) {
+          // all j < i: exp(cs_i - cs_j) = exp(cs_i - cs_r) exp(cs_r - cs_j) with r
+          // the last row of block jb; both exponents are <= 0
+          const float u = __expf(cs_i - sm.cs[32 * jb + 31]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float4 v4 = *reinterpret_cast<const float4 *>(&sm.v[32 * jb + 8 * q + 4 * L.hh]);
+            const float vj[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const int r = 4 * q + t;
+              Mb[r >> 3][r & 7] = (__bf16)(G[jb][r] * (u * vj[t]));
+            }
+          }
+        } else {
+          // diagonal block: d = i - j decides between decay, diagonal and zero
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int jq = 32 * jb + 8 * q + 4 * L.hh;
+            const float4 c4 = *reinterpret_cast<const float4 *>(&sm.cs[jq]);
+            const float4 d4 = *reinterpret_cast<const float4 *>(&sm.dt[jq]);
+            const float cj[4] = {c4.x, c4.y, c4.z, c4.w};
+            const float dj[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const int r = 4 * q + t;
+              const int d = ci - (jq + t);
+              const float gv = G[jb][r];
+              const float mv = gv * __expf(fminf(cs_i - cj[t], 0.f)) * dj[t];
+              Mb[r >> 3][r & 7] = (__bf16)(d > 0 ? mv : (d == 0 ? fmaf(gv, dj[t], Dh) : 0.f));
+            }
+          }
+        }
+        // x^T (row p, k = j) in the accumulator's permuted K order: slots 0..3
+        // are rows 16s + 4hh + 0..3, slots 4..7 rows 16s + 8 + 4hh + 0..3
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const uint32_t o = L.oYd[q] + 128 * (32 * jb + 16 * s2);
+            yo[q] = mfma32(trd(sm.X, o, o + 1024), Mb[s2], yo[q]);
+          }
+      }
+    }
+    __syncthreads();  // A: every read of this chunk's tiles, H and cs/dt/w/v is done
+    if (has_next) issue_tiles(L.lane, c1, nvn);
+    if (W == kDtWave && has_next) chunk_dt_wave(raw_next, nvn, bias, Ah, sm.cs, sm.dt, sm.w, sm.v, sm.misc);
+    if (kFull) write_state_lds(L.lane);  // H_c for the next chunk's state->output product
+    __builtin_amdgcn_s_waitcnt(0);       // this wave's direct loads of the next chunk have landed
+    __syncthreads();                     // B: ... and every wave's
+    // y rows i < nv: this lane holds p = 32q + 8 r4 + 4 hh + 0..3 of token c0 + ci
+    if (kFull && ci < nv) {
+      bf16_t *yrow = yg + (int64_t)c0 * p.y_st + (uint32_t)ci * yst;
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          u32x2 v;
+          v[0] = pack2_bf16(yo[q][4 * r4], yo[q][4 * r4 + 1]);
+          v[1] = pack2_bf16(yo[q][4 * r4 + 2], yo[q][4 * r4 + 3]);
+          *reinterpret_cast<u32x2 *>(yrow + 32 * q + 8 * r4 + 4 * L.hh) = v;
+        }
+    }
+  }
+
+  // outputs of the segment
+  const int l32 = threadIdx.x & 31, hh = (threadIdx.x >> 5) & 1;
+  float *out = nullptr;
+  if (kFull) {
+    if (it.last && p.final_state) out = p.final_state + ((int64_t)it.row * p.H + h) * kPN;
+  } else {
+    out = ws_f32(plan, ws, plan.ws_local_off) + ((int64_t)item * p.H + h) * kPN;
+    if (threadIdx.x == 0) ws_f32(plan, ws, plan.ws_decay_off)[(int64_t)item * p.H + h] = logdecay;
+  }
+  if (out) {
+#pragma unroll
+    for (int t = 0; t < NS; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4 *>(out + (32 * Cf::spb(t) + l32) * kDState + 32 * Cf::nb(t) + 8 * q + 4 * hh) =
+            make_float4(hs[t][4 * q], hs[t][4 * q + 1], hs[t][4 * q + 2], hs[t][4 * q + 3]);
+  }
+}
+
+template <bool kFull>
+__global__ __launch_bounds__(kThr, 2) void chunk_scan_bf16_kernel(ScanParams p, ScanPlan plan, char *ws) {
+  __shared__ __attribute__((aligned(16))) Smem sm;
+  int item, h, g;
+  if (!map_workgroup(p, plan, item, h, g)) return;
+  Item it;
+  if (!get_item(p, plan, ws, item, it)) return;
+  if (!kFull && it.last) return;  // the pre-pass only needs segments that have a successor
+  switch (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) {
+    case 0: run_wave<kFull, 0>(p, plan, ws, it, item, h, g, sm); break;
+    case 1: run_wave<kFull, 1>(p, plan, ws, it, item, h, g, sm); break;
+    case 2: run_wave<kFull, 2>(p, plan, ws, it, item, h, g, sm); break;
+    default: run_wave<kFull, 3>(p, plan, ws, it, item, h, g, sm); break;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_chunk_scan_bf16(const ScanParams &p, const ScanPlan &plan, char *ws, unsigned nblk, bool full,
+                                  hipStream_t stream) {
+  if (full) hipLaunchKernelGGL(chunk_scan_bf16_kernel<true>, dim3(nblk), dim3(kThr), 0, stream, p, plan, ws);
+  else hipLaunchKernelGGL(chunk_scan_bf16_kernel<false>, dim3(nblk), dim3(kThr), 0, stream, p, plan, ws);
+  return hipGetLastError();
+}
+
+}  // namespace ssd
