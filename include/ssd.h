@@ -133,7 +133,8 @@ int ssd_conv1d_silu(const ssd_conv_args *args, void *stream);
  * operands); fp32 inputs run an all-fp32 path.
  *
  * Supported: headdim 64, dstate 128, chunk_size 128, dtype F32 or BF16.
- * x, B, C, y 16-byte aligned with strides multiples of 8 elements.
+ * x, B, C, y 16-byte aligned with strides multiples of 8 elements; token
+ * strides below 2^22 elements (SSD_ERR_INVALID_ARG otherwise).
  *
  * seg_chunks: 0 = automatic.  Otherwise each sequence is cut into segments
  * of seg_chunks chunks that run in parallel; the state entering each

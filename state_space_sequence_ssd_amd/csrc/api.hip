@@ -73,6 +73,11 @@ int check_scan(const ssd_scan_args *a, ssd::ScanParams &p) {
     if (a->x_stride_token < xw || a->y_stride_token < xw || a->B_stride_token < bw || a->C_stride_token < bw ||
         a->dt_stride_token < a->nheads)
       return fail(SSD_ERR_INVALID_ARG, "ssd_chunk_scan_fwd: token strides smaller than the packed row width");
+    // the kernels address one chunk's rows with 32-bit byte offsets
+    const int64_t kMaxSt = int64_t(1) << 22;
+    if (a->x_stride_token >= kMaxSt || a->y_stride_token >= kMaxSt || a->B_stride_token >= kMaxSt ||
+        a->C_stride_token >= kMaxSt || a->dt_stride_token >= kMaxSt)
+      return fail(SSD_ERR_INVALID_ARG, "ssd_chunk_scan_fwd: token strides must be below 2^22 elements");
   }
   if ((a->initial_state && !aligned16(a->initial_state)) || (a->final_state && !aligned16(a->final_state)))
     return fail(SSD_ERR_MISALIGNED, "ssd_chunk_scan_fwd: states must be 16-byte aligned");

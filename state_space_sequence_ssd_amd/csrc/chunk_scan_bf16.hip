@@ -77,16 +77,18 @@ static_assert(sizeof(Smem) <= 80 * 1024, "LDS budget of one of two workgroups pe
 
 
 // state tiles (n-block nb, p-block pb) of H^T owned by wave w in the full pass
+// dealt by p-block, so each wave scales one x fragment per k-step
 constexpr int kNS[4] = {4, 3, 1, 0};
-constexpr int kSnb[4][4] = {{0, 0, 1, 1}, {2, 2, 3, 0}, {3, 0, 0, 0}, {0, 0, 0, 0}};
-constexpr int kSpb[4][4] = {{0, 1, 0, 1}, {0, 1, 0, 0}, {1, 0, 0, 0}, {0, 0, 0, 0}};
+constexpr int kSnb[4][4] = {{0, 1, 2, 3}, {0, 1, 2, 0}, {3, 0, 0, 0}, {0, 0, 0, 0}};
+constexpr int kSpb[4][4] = {{0, 0, 0, 0}, {1, 1, 1, 0}, {1, 0, 0, 0}, {0, 0, 0, 0}};
 constexpr int kDtWave = 3;  // the wave that computes the next chunk's dt / cumsum (no state tiles)
 
 template <bool kFull, int W> struct Cfg {
   static constexpr int NCB = kFull ? W + 1 : 0;
   static constexpr int NS = kFull ? kNS[W] : 2;
-  __host__ __device__ static constexpr int nb(int t) { return kFull ? kSnb[W][t] : W; }
-  __host__ __device__ static constexpr int spb(int t) { return kFull ? kSpb[W][t] : t; }
+  // state-only pass: wave w owns n-blocks 2(w%2), 2(w%2)+1 of p-block w/2
+  __host__ __device__ static constexpr int nb(int t) { return kFull ? kSnb[W][t] : 2 * (W % 2) + t; }
+  __host__ __device__ static constexpr int spb(int t) { return kFull ? kSpb[W][t] : W / 2; }
   __host__ __device__ static constexpr bool uses_spb(int q) {
     for (int t = 0; t < NS; ++t)
       if (spb(t) == q) return true;
@@ -121,12 +123,12 @@ template <bool kFull, int W> struct Cfg {
     return true;
   }
 };
-static_assert(Cfg<true, 0>::slots_ok() && Cfg<true, 0>::NNB == 2, "state tile slots");
-static_assert(Cfg<true, 1>::slots_ok() && Cfg<true, 1>::NNB == 2, "state tile slots");
+static_assert(Cfg<true, 0>::slots_ok() && Cfg<true, 0>::NNB == 4, "state tile slots");
+static_assert(Cfg<true, 1>::slots_ok() && Cfg<true, 1>::NNB == 3, "state tile slots");
 static_assert(Cfg<true, 2>::slots_ok() && Cfg<true, 2>::NNB == 1, "state tile slots");
 static_assert(Cfg<true, 3>::slots_ok() && Cfg<true, 3>::NNB == 0, "state tile slots");
-static_assert(Cfg<false, 0>::slots_ok() && Cfg<false, 0>::NNB == 1, "state tile slots");
-static_assert(Cfg<false, 3>::slots_ok() && Cfg<false, 3>::NNB == 1, "state tile slots");
+static_assert(Cfg<false, 0>::slots_ok() && Cfg<false, 0>::NNB == 2, "state tile slots");
+static_assert(Cfg<false, 3>::slots_ok() && Cfg<false, 3>::NNB == 2, "state tile slots");
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -230,7 +232,7 @@ __device__ __forceinline__ int opaque_lane() {
 // row-major 16-byte read of column block 2s + hh is the step-0 offset XOR 32 s.
 template <int NCB> struct LaneGeo {
   int lane, l32, hh, g16, s16;
-  uint32_t oBt[2][2], oXt[2][2], oBr[NCB > 0 ? NCB : 1], oH[2], oYd[2];
+  uint32_t oBt[4][2], oXt[2][2], oBr[NCB > 0 ? NCB : 1], oH[2], oYd[2];
   template <class Cf> __device__ __forceinline__ void init(int ln) {
     lane = ln;
     l32 = ln & 31;
@@ -240,9 +242,12 @@ template <int NCB> struct LaneGeo {
     const int trr = 8 * hh + (s16 >> 2);            // transpose-read row at step 0
     const int trc = 16 * (g16 & 1) + 4 * (s16 & 3);  // ... and column within a 32-block
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < Cf::NNB; ++u) {
       oBt[u][0] = off256(trr, 32 * Cf::slot_nb(u) + trc);
       oBt[u][1] = off256(trr + 4, 32 * Cf::slot_nb(u) + trc);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
       oXt[u][0] = off128(trr, 32 * u + trc);
       oXt[u][1] = off128(trr + 4, 32 * u + trc);
       oH[u] = off256(32 * u + l32, 8 * hh);
@@ -284,6 +289,26 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
   // [32w, 32w + 32) of both.  Rows past the segment end repeat its last row
   // (finite values whose every use is cancelled: dt = 0 there).
   auto issue_tiles = [&](int ln, int c0, int nv) {
+    if (nv == kChunk) {
+      // whole chunk: one per-lane 32-bit byte offset per tile, the row step in
+      // the (uniform) base address
+      const char *bc = reinterpret_cast<const char *>(Bg + (int64_t)c0 * p.B_st);
+      const char *xc = reinterpret_cast<const char *>(xg + (int64_t)c0 * p.x_st);
+      const uint32_t ob = (32 * W + (ln >> 4)) * bst * 2;
+      uint32_t cb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cb[i] = ob + 16 * ((ln & 15) ^ swz16((ln >> 4) + 4 * i));
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        __builtin_amdgcn_global_load_lds(bc + (size_t)(8 * i) * bst + cb[i & 3],
+                                         (lds_void *)(sm.B + (32 * W + 4 * i) * 256), 16, 0, 0);
+      const uint32_t ox = (32 * W + (ln >> 3)) * xst * 2 + 16 * ((ln & 7) ^ swz8(ln >> 3));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_global_load_lds(xc + (size_t)(16 * i) * xst + ox,
+                                         (lds_void *)(sm.X + (32 * W + 8 * i) * 128), 16, 0, 0);
+      return;
+    }
     const int last = nv - 1;
     const bf16_t *bc = Bg + (int64_t)c0 * p.B_st;
     const bf16_t *xc = xg + (int64_t)c0 * p.x_st;

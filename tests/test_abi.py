@@ -81,6 +81,7 @@ def scan_rc(a, ws=None, ws_bytes=1 << 40):
     ("headdim", 32, 2), ("dstate", 64, 2), ("chunk_size", 64, 2), ("seg_chunks", -1, 1),
     ("A", None, 1), ("x", None, 1), ("y", None, 1), ("dt", None, 1),
     ("x", FAKE + 2, 4), ("B_stride_token", 2048 + 2, 4), ("x_stride_token", 1024, 1),
+    ("C_stride_token", 1 << 22, 1), ("dt_stride_token", 1 << 22, 1),
 ])
 def test_scan_argument_errors(field, value, code):
     a = scan_args(**{field: value})
