@@ -46,8 +46,16 @@ namespace {
 constexpr int kThr = 256;  // 4 waves, one per SIMD
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) void lds_void;
+// LDS pointers stay in address space 3 from the kernel entry on: no generic
+// pointer (and no null check per access) between a tile and its ds_* / direct loads.
+#define SSD_LDS __attribute__((address_space(3)))
+typedef SSD_LDS s16x4 lds_s16x4;
+typedef SSD_LDS void lds_void;
+typedef SSD_LDS uint8_t lds_u8;
+typedef SSD_LDS float lds_f32;
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+template <class T> __device__ __forceinline__ T lds_ld(const lds_u8 *p) { return *reinterpret_cast<const SSD_LDS T *>(p); }
+template <class T> __device__ __forceinline__ void lds_st(lds_u8 *p, T v) { *reinterpret_cast<SSD_LDS T *>(p) = v; }
 
 // Row swizzles of the 16-byte blocks: conflict-free for 8 (or 16) lanes on
 // consecutive rows of one block, and for the transpose reads (4 consecutive
@@ -74,6 +82,11 @@ struct Smem {
 };
 // two workgroups per CU: each fits in half of the 160 KiB LDS
 static_assert(sizeof(Smem) <= 80 * 1024, "LDS budget of one of two workgroups per CU");
+
+struct Lds {
+  lds_u8 *B, *X, *H;
+  lds_f32 *cs, *dt, *w, *v, *misc;
+};
 
 
 // state tiles (n-block nb, p-block pb) of H^T owned by wave w in the full pass
@@ -134,33 +147,20 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ u32x2 tr_read(const uint8_t *p) {
-  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_s16x4 *)(const __attribute__((address_space(3))) uint8_t *)p);
+__device__ __forceinline__ u32x2 tr_read(const lds_u8 *p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p);
   return __builtin_bit_cast(u32x2, v);
-}
-
-// 8 K values (token rows k0..k0+7) of this lane's MFMA column c0g + (lane % 16),
-// from a token-major tile, by two transpose reads.
-template <int kRowBytes>
-__device__ __forceinline__ bf16x8 tr_frag(const uint8_t *tile, int k0, int c0g) {
-  const int s16 = threadIdx.x & 15;
-  const int r = k0 + (s16 >> 2);
-  const int col = c0g + 4 * (s16 & 3);
-  const u32x2 lo = tr_read(tile + (kRowBytes == 256 ? off256(r, col) : off128(r, col)));
-  const u32x2 hi = tr_read(tile + (kRowBytes == 256 ? off256(r + 4, col) : off128(r + 4, col)));
-  return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
 }
 
 // w_j x_j for the 8 K values of a fragment (K rows k0..k0+7 in element order),
 // rounded to bf16 as the MFMA operand.
-__device__ __forceinline__ bf16x8 scale_frag(bf16x8 x, float4 wa, float4 wb) {
+__device__ __forceinline__ bf16x8 scale_frag(bf16x8 x, f32x4 wa, f32x4 wb) {
   const u32x4 u = __builtin_bit_cast(u32x4, x);
   u32x4 o;
-  o[0] = pack2_bf16(lo_bf16(u[0]) * wa.x, hi_bf16(u[0]) * wa.y);
-  o[1] = pack2_bf16(lo_bf16(u[1]) * wa.z, hi_bf16(u[1]) * wa.w);
-  o[2] = pack2_bf16(lo_bf16(u[2]) * wb.x, hi_bf16(u[2]) * wb.y);
-  o[3] = pack2_bf16(lo_bf16(u[3]) * wb.z, hi_bf16(u[3]) * wb.w);
+  o[0] = pack2_bf16(lo_bf16(u[0]) * wa[0], hi_bf16(u[0]) * wa[1]);
+  o[1] = pack2_bf16(lo_bf16(u[1]) * wa[2], hi_bf16(u[1]) * wa[3]);
+  o[2] = pack2_bf16(lo_bf16(u[2]) * wb[0], hi_bf16(u[2]) * wb[1]);
+  o[3] = pack2_bf16(lo_bf16(u[3]) * wb[2], hi_bf16(u[3]) * wb[3]);
   return __builtin_bit_cast(bf16x8, o);
 }
 
@@ -190,8 +190,8 @@ __device__ __forceinline__ float softplus_fast(float z) {
 
 // dt, cs, w = exp(cs_last - cs) dt and v = exp(cs_r - cs) dt (r = end of the
 // token's 32-block) of one chunk, by one wave (tokens 2 lane, 2 lane + 1).
-__device__ __forceinline__ void chunk_dt_wave(uint32_t raw, int nv, float bias, float A, float *cs,
-                                              float *dt, float *w, float *v, float *misc) {
+__device__ __forceinline__ void chunk_dt_wave(uint32_t raw, int nv, float bias, float A, lds_f32 *cs,
+                                              lds_f32 *dt, lds_f32 *w, lds_f32 *v, lds_f32 *misc) {
   const int lane = threadIdx.x & 63;
   const int j0 = 2 * lane;
   const float d0 = j0 < nv ? softplus_fast(lo_bf16(raw) + bias) : 0.f;
@@ -206,10 +206,10 @@ __device__ __forceinline__ void chunk_dt_wave(uint32_t raw, int nv, float bias, 
   const float e2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), 47));
   const int blk = lane >> 4;
   const float cr = blk == 0 ? e0 : blk == 1 ? e1 : blk == 2 ? e2 : total;
-  *reinterpret_cast<float2 *>(cs + j0) = make_float2(cs0, cs1);
-  *reinterpret_cast<float2 *>(dt + j0) = make_float2(d0, d1);
-  *reinterpret_cast<float2 *>(w + j0) = make_float2(__expf(total - cs0) * d0, __expf(total - cs1) * d1);
-  *reinterpret_cast<float2 *>(v + j0) = make_float2(__expf(cr - cs0) * d0, __expf(cr - cs1) * d1);
+  *reinterpret_cast<SSD_LDS f32x2 *>(cs + j0) = f32x2{cs0, cs1};
+  *reinterpret_cast<SSD_LDS f32x2 *>(dt + j0) = f32x2{d0, d1};
+  *reinterpret_cast<SSD_LDS f32x2 *>(w + j0) = f32x2{__expf(total - cs0) * d0, __expf(total - cs1) * d1};
+  *reinterpret_cast<SSD_LDS f32x2 *>(v + j0) = f32x2{__expf(cr - cs0) * d0, __expf(cr - cs1) * d1};
   if (lane == 0) {
     misc[0] = __expf(total);
     misc[1] = total;
@@ -259,7 +259,7 @@ template <int NCB> struct LaneGeo {
   }
 };
 
-__device__ __forceinline__ bf16x8 trd(const uint8_t *tile, uint32_t lo, uint32_t hi) {
+__device__ __forceinline__ bf16x8 trd(const lds_u8 *tile, uint32_t lo, uint32_t hi) {
   const u32x2 a = tr_read(tile + lo);
   const u32x2 b = tr_read(tile + hi);
   return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
@@ -267,7 +267,7 @@ __device__ __forceinline__ bf16x8 trd(const uint8_t *tile, uint32_t lo, uint32_t
 
 template <bool kFull, int W>
 __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &plan, char *ws, const Item &it,
-                                         int item, int h, int g, Smem &sm) {
+                                         int item, int h, int g, const Lds &sm) {
   using Cf = Cfg<kFull, W>;
   constexpr int NCB = Cf::NCB, NS = Cf::NS;
   constexpr int NX = (Cf::uses_spb(0) ? 1 : 0) + (Cf::uses_spb(1) ? 1 : 0);
@@ -353,7 +353,7 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
         u32x2 v;
         v[0] = pack2_bf16(hs[t][4 * q], hs[t][4 * q + 1]);
         v[1] = pack2_bf16(hs[t][4 * q + 2], hs[t][4 * q + 3]);
-        *reinterpret_cast<u32x2 *>(sm.H + off256(32 * Cf::spb(t) + l32, 32 * Cf::nb(t) + 8 * q + 4 * hh)) = v;
+        lds_st<u32x2>(sm.H + off256(32 * Cf::spb(t) + l32, 32 * Cf::nb(t) + 8 * q + 4 * hh), v);
       }
   };
   {
@@ -381,11 +381,11 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
   if (ntok > 0) {
     const int ln = threadIdx.x & 63;
     const int nv0 = min(kChunk, ntok);
-    issue_tiles(ln, it.tok0, nv0);
     if (kFull) load_c(ln, it.tok0, nv0);
     if (W == kDtWave)
       chunk_dt_wave(load_dt_raw(ln, it.tok0, nv0), nv0, bias, Ah, sm.cs, sm.dt, sm.w, sm.v, sm.misc);
     if (kFull) write_state_lds(ln);
+    issue_tiles(ln, it.tok0, nv0);  // last, for the same reason as in the loop
     __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
     __syncthreads();
   }
@@ -420,11 +420,11 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
     yo[0] = f32x16{}; yo[1] = f32x16{};
 
     // k-loop: every accumulator chain of this wave, operands double-buffered
-    auto load_frags = [&](int s, bf16x8 *f, float4 *wv) {
+    auto load_frags = [&](int s, bf16x8 *f, f32x4 *wv) {
       int k = 0;
       if (NX > 0) {
-        wv[0] = *reinterpret_cast<const float4 *>(&sm.w[16 * s + 8 * L.hh]);
-        wv[1] = *reinterpret_cast<const float4 *>(&sm.w[16 * s + 8 * L.hh + 4]);
+        wv[0] = lds_ld<f32x4>((const lds_u8 *)&sm.w[16 * s + 8 * L.hh]);
+        wv[1] = lds_ld<f32x4>((const lds_u8 *)&sm.w[16 * s + 8 * L.hh + 4]);
       }
 #pragma unroll
       for (int q = 0; q < 2; ++q)
@@ -433,12 +433,12 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
       for (int u = 0; u < NNB; ++u) f[k++] = trd(sm.B, L.oBt[u][0] + 4096 * s, L.oBt[u][1] + 4096 * s);
       if (kFull) {
 #pragma unroll
-        for (int jb = 0; jb < NCB; ++jb) f[k++] = *reinterpret_cast<const bf16x8 *>(sm.B + (L.oBr[jb] ^ (32 * s)));
+        for (int jb = 0; jb < NCB; ++jb) f[k++] = lds_ld<bf16x8>(sm.B + (L.oBr[jb] ^ (32 * s)));
 #pragma unroll
-        for (int q = 0; q < 2; ++q) f[k++] = *reinterpret_cast<const bf16x8 *>(sm.H + (L.oH[q] ^ (32 * s)));
+        for (int q = 0; q < 2; ++q) f[k++] = lds_ld<bf16x8>(sm.H + (L.oH[q] ^ (32 * s)));
       }
     };
-    auto mfma_step = [&](int s, const bf16x8 *f, const float4 *wv) {
+    auto mfma_step = [&](int s, const bf16x8 *f, const f32x4 *wv) {
       int k = 0;
       bf16x8 xw[2];
 #pragma unroll
@@ -457,7 +457,7 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
     };
     {
       bf16x8 fr[2][NF > 0 ? NF : 1];
-      float4 wr[2][2];
+      f32x4 wr[2][2];
       load_frags(0, fr[0], wr[0]);
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
@@ -490,8 +490,7 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
           const float u = __expf(cs_i - sm.cs[32 * jb + 31]);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const float4 v4 = *reinterpret_cast<const float4 *>(&sm.v[32 * jb + 8 * q + 4 * L.hh]);
-            const float vj[4] = {v4.x, v4.y, v4.z, v4.w};
+            const f32x4 vj = lds_ld<f32x4>((const lds_u8 *)&sm.v[32 * jb + 8 * q + 4 * L.hh]);
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
               const int r = 4 * q + t;
@@ -503,10 +502,8 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int jq = 32 * jb + 8 * q + 4 * L.hh;
-            const float4 c4 = *reinterpret_cast<const float4 *>(&sm.cs[jq]);
-            const float4 d4 = *reinterpret_cast<const float4 *>(&sm.dt[jq]);
-            const float cj[4] = {c4.x, c4.y, c4.z, c4.w};
-            const float dj[4] = {d4.x, d4.y, d4.z, d4.w};
+            const f32x4 cj = lds_ld<f32x4>((const lds_u8 *)&sm.cs[jq]);
+            const f32x4 dj = lds_ld<f32x4>((const lds_u8 *)&sm.dt[jq]);
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
               const int r = 4 * q + t;
@@ -529,14 +526,10 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
       }
     }
     __syncthreads();  // A: every read of this chunk's tiles, H and cs/dt/w/v is done
-    if (has_next) issue_tiles(L.lane, c1, nvn);
-    if (W == kDtWave && has_next) chunk_dt_wave(raw_next, nvn, bias, Ah, sm.cs, sm.dt, sm.w, sm.v, sm.misc);
-    if (kFull) write_state_lds(L.lane);  // H_c for the next chunk's state->output product
-    __builtin_amdgcn_s_waitcnt(0);       // this wave's direct loads of the next chunk have landed
-    __syncthreads();                     // B: ... and every wave's
-    // y rows i < nv: this lane holds p = 32q + 8 r4 + 4 hh + 0..3 of token c0 + ci
-    if (kFull && ci < nv) {
-      bf16_t *yrow = yg + (int64_t)c0 * p.y_st + (uint32_t)ci * yst;
+    if (kFull) {
+      // y rows through this wave's own rows of the x tile (free until its loads
+      // of the next chunk), so each store writes 8 whole 128-byte rows.  The
+      // lane holds p = 32q + 8 r4 + 4 hh + 0..3 of chunk row ci.
 #pragma unroll
       for (int q = 0; q < 2; ++q)
 #pragma unroll
@@ -544,9 +537,23 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
           u32x2 v;
           v[0] = pack2_bf16(yo[q][4 * r4], yo[q][4 * r4 + 1]);
           v[1] = pack2_bf16(yo[q][4 * r4 + 2], yo[q][4 * r4 + 3]);
-          *reinterpret_cast<u32x2 *>(yrow + 32 * q + 8 * r4 + 4 * L.hh) = v;
+          lds_st<u32x2>(sm.X + off128(ci, 32 * q + 8 * r4 + 4 * L.hh), v);
         }
+      const int rr = 32 * W + (L.lane >> 3);  // + 8k: rows this lane stores
+      bf16_t *ybase = yg + (int64_t)c0 * p.y_st + 8 * (L.lane & 7);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const u32x4 v = lds_ld<u32x4>(sm.X + off128(rr + 8 * k, 8 * (L.lane & 7)));
+        if (rr + 8 * k < nv) *reinterpret_cast<u32x4 *>(ybase + (uint32_t)(rr + 8 * k) * yst) = v;
+      }
     }
+    if (W == kDtWave && has_next) chunk_dt_wave(raw_next, nvn, bias, Ah, sm.cs, sm.dt, sm.w, sm.v, sm.misc);
+    if (kFull) write_state_lds(L.lane);  // H_c for the next chunk's state->output product
+    // the direct loads go last: any LDS access behind them in this wave would
+    // first wait for them to land
+    if (has_next) issue_tiles(L.lane, c1, nvn);
+    __builtin_amdgcn_s_waitcnt(0);       // this wave's direct loads of the next chunk have landed
+    __syncthreads();                     // B: ... and every wave's
   }
 
   // outputs of the segment
@@ -570,7 +577,9 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
 
 template <bool kFull>
 __global__ __launch_bounds__(kThr, 2) void chunk_scan_bf16_kernel(ScanParams p, ScanPlan plan, char *ws) {
-  __shared__ __attribute__((aligned(16))) Smem sm;
+  __shared__ __attribute__((aligned(16))) Smem smem;
+  const Lds sm{(lds_u8 *)smem.B, (lds_u8 *)smem.X, (lds_u8 *)smem.H, (lds_f32 *)smem.cs,
+               (lds_f32 *)smem.dt, (lds_f32 *)smem.w, (lds_f32 *)smem.v, (lds_f32 *)smem.misc};
   int item, h, g;
   if (!map_workgroup(p, plan, item, h, g)) return;
   Item it;
