@@ -27,7 +27,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 PROFILES = os.path.join(ROOT, "profiles")
-SCAN_SOURCES = ["chunk_scan.hip", "common.h", "kernels.h"]
+SCAN_SOURCES = ["chunk_scan.hip", "chunk_scan_bf16.hip", "scan_items.h", "common.h", "kernels.h"]
 CONV_SOURCES = ["conv1d_silu.hip", "common.h", "kernels.h"]
 DECODE_SOURCES = ["decode_step.hip", "common.h", "kernels.h"]
 
@@ -90,37 +90,24 @@ def decode_algorithmic_bytes(dw):
             + CD * dw.conv_width * 4 + 3 * H * 4)
 
 
-def cpu_baseline(w, d, max_heads):
+def cpu_baseline(w, d, rows):
     """The fp64 oracle (as it stands) on a bounded sample of the same workload:
-    batch row 0, all tokens, the first `max_heads` heads with their groups'
-    conv channels.  Scaled to whole-layer tokens/s by the head fraction."""
-    import numpy as np
+    the first `rows` batch rows, all tokens and heads, conv then scan with final
+    states.  Reported as tokens/s of that sample."""
     import oracle
     H, G, P, N = w.nheads, w.ngroups, w.headdim, w.dstate
-    heads = list(range(max_heads))
-    hpg = H // G
-    groups = sorted({h // hpg for h in heads})
-    xch = np.arange(0, max_heads * P)
-    bch = np.concatenate([H * P + np.arange(g * N, (g + 1) * N) for g in groups])
-    cch = np.concatenate([H * P + G * N + np.arange(g * N, (g + 1) * N) for g in groups])
-    ch = np.concatenate([xch, bch, cch])
-    xbc = np.ascontiguousarray(d["xBC"][:1][..., ch])
-    cw = d["conv_w"][ch]
-    t0 = time.perf_counter()
-    v = oracle.conv1d_silu(xbc, cw)
     L = w.seqlen
-    x = v[..., :len(xch)].reshape(1, L, max_heads, P)
-    B = v[..., len(xch):len(xch) + len(bch)].reshape(1, L, len(groups), N)
-    C = v[..., len(xch) + len(bch):].reshape(1, L, len(groups), N)
-    oracle.ssd_scan(x, d["dt"][:1][:, :, heads], d["dt_bias"][heads], d["A"][heads], B, C,
-                    d["D"][heads], want_final_state=True)
+    t0 = time.perf_counter()
+    v = oracle.conv1d_silu(d["xBC"][:rows], d["conv_w"])
+    x = v[..., :H * P].reshape(rows, L, H, P)
+    B = v[..., H * P:H * P + G * N].reshape(rows, L, G, N)
+    C = v[..., H * P + G * N:].reshape(rows, L, G, N)
+    oracle.ssd_scan(x, d["dt"][:rows], d["dt_bias"], d["A"], B, C, d["D"], want_final_state=True)
     el = time.perf_counter() - t0
-    tokens_equiv = L * (max_heads / H)
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
-    return {"value": tokens_equiv / el, "unit": "tokens/s/layer", "cores": min(threads, max_heads),
-            "kind": "oracle",
-            "sample": f"batch row 0 of 4, {L} tokens, {max_heads} of {H} heads (+ their conv "
-                      f"channels), fp64 sequential recurrence, {el:.1f} s; scaled by heads",
+    return {"value": rows * L / el, "unit": "tokens/s/layer", "cores": threads, "kind": "oracle",
+            "sample": f"batch rows 0..{rows - 1} of {w.batch}, all {L} tokens and {H} heads: fp64 conv "
+                      f"then fp64 sequential recurrence with final states, {el:.1f} s wall",
             "seconds": el}
 
 
@@ -133,7 +120,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (profiler runs)")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
-    ap.add_argument("--cpu-heads", type=int, default=32)
+    ap.add_argument("--cpu-rows", type=int, default=4, help="batch rows in the oracle sample (4 = the whole step)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter calibration)")
     args = ap.parse_args()
@@ -288,7 +275,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, d, args.cpu_heads)
+        cpu = cpu_baseline(w, d, args.cpu_rows)
 
     line = {
         "metric": "SSD scan tokens/s/layer @Nemotron-H-8B shape; decode-step HBM GB/s",
