@@ -459,6 +459,9 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
       bf16x8 fr[2][NF > 0 ? NF : 1];
       f32x4 wr[2][2];
       load_frags(0, fr[0], wr[0]);
+      // the k-loop's MFMA stream goes first when the other workgroup's wave on
+      // this SIMD also has work to issue
+      __builtin_amdgcn_s_setprio(2);
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         if (s < 7) load_frags(s + 1, fr[(s + 1) & 1], wr[(s + 1) & 1]);
@@ -467,6 +470,7 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     // the C fragments of this chunk are dead: fetch the next chunk's now
     if (kFull) load_c(L.lane, cn, nvn);
 
