@@ -189,7 +189,8 @@ int ssd_chunk_scan_fwd(const ssd_scan_args *args, void *workspace,
  *   y (batch, nheads, headdim), dtype of xBC, batch stride y_stride_batch.
  *
  * Supported: headdim 64, dstate 128, conv_width 4, dtype F32 or BF16;
- * ssm_state 16-byte aligned.
+ * ssm_state 16-byte aligned; nheads / ngroups at most 254 (one workgroup
+ * holds a group's conv outputs and y in LDS), SSD_ERR_UNSUPPORTED beyond.
  * ---------------------------------------------------------------------- */
 typedef struct ssd_decode_args {
   uint32_t struct_size;          /* sizeof(ssd_decode_args) */

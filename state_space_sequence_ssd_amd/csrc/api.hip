@@ -189,7 +189,7 @@ int ssd_decode_step(const ssd_decode_args *a, void *stream) {
   if (a->conv_state && !a->conv_weight)
     return fail(SSD_ERR_INVALID_ARG, "ssd_decode_step: conv_state needs conv_weight");
   const int hpg = a->nheads / a->ngroups;
-  if ((int64_t)hpg * a->headdim + 2 * a->dstate + 2 * hpg > 32768)
+  if (2 * (int64_t)hpg * a->headdim + 2 * a->dstate + 2 * hpg > 32768)
     return fail(SSD_ERR_UNSUPPORTED, "ssd_decode_step: nheads / ngroups = %d too large for one workgroup", hpg);
   if (!aligned16(a->ssm_state) || (a->conv_weight && !aligned16(a->conv_weight)))
     return fail(SSD_ERR_MISALIGNED, "ssd_decode_step: ssm_state and conv_weight must be 16-byte aligned");

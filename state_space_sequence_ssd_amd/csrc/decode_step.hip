@@ -22,11 +22,11 @@ namespace ssd {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 1024;  // 2 float4 of each head's state per thread
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void decode_step_kernel(DecodeParams p) {
-  extern __shared__ float smem[];  // [hpg*P x | N B | N C] post-conv values, then dt, a
+  extern __shared__ float smem[];  // [hpg*P x | N B | N C] post-conv values, dt, a, then y
   const int b = blockIdx.x / p.G;
   const int g = blockIdx.x % p.G;
   const int hpg = p.H / p.G;
@@ -37,6 +37,16 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(DecodeParams p) {
   float *sv = smem;
   float *s_dt = smem + nloc;
   float *s_a = s_dt + hpg;
+  float *s_y = s_a + hpg;
+
+  // the first head's state streams in while the conv window is computed
+  constexpr int kIters = kHeadDim * kDState / 4 / kThreads;
+  auto state_of = [&](int hl) {
+    return reinterpret_cast<f32x4 *>(p.ssm_state + ((int64_t)b * p.H + g * hpg + hl) * kHeadDim * kDState);
+  };
+  f32x4 s[kIters];
+#pragma unroll
+  for (int i = 0; i < kIters; ++i) s[i] = __builtin_nontemporal_load(state_of(0) + i * kThreads + threadIdx.x);
 
   const T *xbc = reinterpret_cast<const T *>(p.xBC) + (int64_t)b * p.xBC_sb;
   T *cst = p.conv_state ? reinterpret_cast<T *>(p.conv_state) + (int64_t)b * (kConvWidth - 1) * CH
@@ -86,13 +96,13 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(DecodeParams p) {
 
   for (int hl = 0; hl < hpg; ++hl) {
     const int h = g * hpg + hl;
-    f32x4 *S = reinterpret_cast<f32x4 *>(p.ssm_state + ((int64_t)b * p.H + h) * kHeadDim * kDState);
+    f32x4 *S = state_of(hl);
+    if (hl > 0) {
+#pragma unroll
+      for (int i = 0; i < kIters; ++i) s[i] = __builtin_nontemporal_load(S + i * kThreads + threadIdx.x);
+    }
     const float dt = s_dt[hl], a = s_a[hl];
     const float dskip = p.D ? p.D[h] : 0.f;
-    constexpr int kIters = kHeadDim * kDState / 4 / kThreads;  // 8
-    f32x4 s[kIters];
-#pragma unroll
-    for (int i = 0; i < kIters; ++i) s[i] = __builtin_nontemporal_load(S + i * kThreads + threadIdx.x);
 #pragma unroll
     for (int i = 0; i < kIters; ++i) {
       const int f = i * kThreads + threadIdx.x;
@@ -111,16 +121,20 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(DecodeParams p) {
       part += __shfl_xor(part, 4, 32);
       part += __shfl_xor(part, 2, 32);
       part += __shfl_xor(part, 1, 32);
-      if (lane32 == 0) yb[h * kHeadDim + prow] = from_f32<T>(part + dskip * xp);
+      if (lane32 == 0) s_y[hl * kHeadDim + prow] = part + dskip * xp;
     }
   }
+  // the group's heads are contiguous in y: one coalesced write of hpg * P values
+  __syncthreads();
+  T *yg = yb + (int64_t)g * hpg * kHeadDim;
+  for (int e = threadIdx.x; e < hpg * kHeadDim; e += kThreads) yg[e] = from_f32<T>(s_y[e]);
 }
 
 }  // namespace
 
 hipError_t launch_decode_step(const DecodeParams &p, hipStream_t stream) {
   const int hpg = p.H / p.G;
-  const size_t lds = sizeof(float) * (hpg * kHeadDim + 2 * kDState + 2 * hpg);
+  const size_t lds = sizeof(float) * (2 * hpg * kHeadDim + 2 * kDState + 2 * hpg);
   dim3 grid(p.batch * p.G), block(kThreads);
   const void *fn = p.bf16 ? reinterpret_cast<const void *>(decode_step_kernel<bf16_t>)
                          : reinterpret_cast<const void *>(decode_step_kernel<float>);
