@@ -9,12 +9,15 @@
 // non-temporal load and one store per four state values, nothing else of
 // size.
 //
-// One workgroup owns one (batch row, group): it runs the conv window of
-// the group's channels (its heads' x channels plus the group's B and C
-// channels), shifts that part of the conv state -- every channel belongs to
-// exactly one workgroup, so the in-place update has no race -- and then
-// updates the states of the group's heads one after another.  A state row
-// (128 floats) is 32 lanes x float4, so y[p] is a 32-lane butterfly sum.
+// One workgroup of 16 waves owns one (batch row, group): it runs the conv
+// window of the group's channels (its heads' x channels plus the group's B
+// and C channels) and shifts that part of the conv state -- every channel
+// belongs to exactly one workgroup, so the in-place update has no race.
+// Then each wave takes one head and streams its 32 KiB of state in four
+// pieces of 8 KiB; every load instruction covers two whole state rows, so
+// the workgroup walks all of its heads' states at once.  A state row (128
+// floats) is 32 lanes x float4, so y[p] is a 32-lane butterfly sum; y is
+// staged in LDS and written once per group.
 #include "common.h"
 #include "kernels.h"
 
@@ -22,7 +25,7 @@ namespace ssd {
 
 namespace {
 
-constexpr int kThreads = 1024;  // 2 float4 of each head's state per thread
+constexpr int kThreads = 1024;  // 16 waves: one head each (group of 16 heads)
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void decode_step_kernel(DecodeParams p) {
@@ -39,14 +42,9 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(DecodeParams p) {
   float *s_a = s_dt + hpg;
   float *s_y = s_a + hpg;
 
-  // the first head's state streams in while the conv window is computed
-  constexpr int kIters = kHeadDim * kDState / 4 / kThreads;
   auto state_of = [&](int hl) {
     return reinterpret_cast<f32x4 *>(p.ssm_state + ((int64_t)b * p.H + g * hpg + hl) * kHeadDim * kDState);
   };
-  f32x4 s[kIters];
-#pragma unroll
-  for (int i = 0; i < kIters; ++i) s[i] = __builtin_nontemporal_load(state_of(0) + i * kThreads + threadIdx.x);
 
   const T *xbc = reinterpret_cast<const T *>(p.xBC) + (int64_t)b * p.xBC_sb;
   T *cst = p.conv_state ? reinterpret_cast<T *>(p.conv_state) + (int64_t)b * (kConvWidth - 1) * CH
@@ -94,34 +92,38 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(DecodeParams p) {
   const float4 Cv = *reinterpret_cast<const float4 *>(sC + 4 * lane32);
   T *yb = reinterpret_cast<T *>(p.y) + (int64_t)b * p.y_sb;
 
-  for (int hl = 0; hl < hpg; ++hl) {
+  // one wave per head: it streams the head's 32 KiB of state in four pieces
+  // of 8 KiB (each load instruction covers two whole state rows)
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int hl = wave; hl < hpg; hl += kThreads / 64) {
     const int h = g * hpg + hl;
     f32x4 *S = state_of(hl);
-    if (hl > 0) {
-#pragma unroll
-      for (int i = 0; i < kIters; ++i) s[i] = __builtin_nontemporal_load(S + i * kThreads + threadIdx.x);
-    }
     const float dt = s_dt[hl], a = s_a[hl];
     const float dskip = p.D ? p.D[h] : 0.f;
+#pragma unroll 1
+    for (int c = 0; c < 4; ++c) {
+      f32x4 v[8];
 #pragma unroll
-    for (int i = 0; i < kIters; ++i) {
-      const int f = i * kThreads + threadIdx.x;
-      const int prow = f >> 5;  // 32 float4 per state row
-      const float xp = sv[hl * kHeadDim + prow];
-      const float dx = dt * xp;
-      f32x4 n;
-      n[0] = fmaf(a, s[i][0], dx * Bv.x);
-      n[1] = fmaf(a, s[i][1], dx * Bv.y);
-      n[2] = fmaf(a, s[i][2], dx * Bv.z);
-      n[3] = fmaf(a, s[i][3], dx * Bv.w);
-      __builtin_nontemporal_store(n, S + f);
-      float part = n[0] * Cv.x + n[1] * Cv.y + n[2] * Cv.z + n[3] * Cv.w;
-      part += __shfl_xor(part, 16, 32);
-      part += __shfl_xor(part, 8, 32);
-      part += __shfl_xor(part, 4, 32);
-      part += __shfl_xor(part, 2, 32);
-      part += __shfl_xor(part, 1, 32);
-      if (lane32 == 0) s_y[hl * kHeadDim + prow] = part + dskip * xp;
+      for (int i = 0; i < 8; ++i) v[i] = __builtin_nontemporal_load(S + (c * 8 + i) * 64 + lane);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int prow = (c * 8 + i) * 2 + (lane >> 5);
+        const float xp = sv[hl * kHeadDim + prow];
+        const float dx = dt * xp;
+        f32x4 n;
+        n[0] = fmaf(a, v[i][0], dx * Bv.x);
+        n[1] = fmaf(a, v[i][1], dx * Bv.y);
+        n[2] = fmaf(a, v[i][2], dx * Bv.z);
+        n[3] = fmaf(a, v[i][3], dx * Bv.w);
+        __builtin_nontemporal_store(n, S + (c * 8 + i) * 64 + lane);
+        float part = n[0] * Cv.x + n[1] * Cv.y + n[2] * Cv.z + n[3] * Cv.w;
+        part += __shfl_xor(part, 16, 32);
+        part += __shfl_xor(part, 8, 32);
+        part += __shfl_xor(part, 4, 32);
+        part += __shfl_xor(part, 2, 32);
+        part += __shfl_xor(part, 1, 32);
+        if (lane32 == 0) s_y[hl * kHeadDim + prow] = part + dskip * xp;
+      }
     }
   }
   // the group's heads are contiguous in y: one coalesced write of hpg * P values
