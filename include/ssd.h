@@ -93,6 +93,7 @@ typedef enum ssd_dtype {
  *
  * Supported: width 4; dtype F32 or BF16; channels a multiple of 8;
  * x / out 16-byte aligned with token and batch strides multiples of 8.
+ * out must not overlap x (no in-place conv).
  * ---------------------------------------------------------------------- */
 typedef struct ssd_conv_args {
   uint32_t struct_size;          /* sizeof(ssd_conv_args) */

@@ -41,9 +41,11 @@ __device__ __forceinline__ float softplus_f32(float z) {
   return z > 20.f ? z : log1pf(__expf(z));
 }
 
-// SiLU(u) = u * sigmoid(u).
+// SiLU(u) = u * sigmoid(u), with the hardware reciprocal (about 1 ulp) in place
+// of an IEEE division sequence: the result is rounded to the I/O dtype anyway.
+// Very negative u gives exp(-u) = inf, rcp(inf) = 0 and the limit -0.
 __device__ __forceinline__ float silu_f32(float u) {
-  return u / (1.f + __expf(-u));
+  return u * __builtin_amdgcn_rcpf(1.f + __expf(-u));
 }
 
 template <typename T> __device__ __forceinline__ float to_f32(T v);

@@ -23,7 +23,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kVec = 8;    // channels per thread
-constexpr int kTile = 32;  // tokens per thread
+constexpr int kTile = 64;  // tokens per thread (the 3-row halo re-read is 3/64 of the input)
+constexpr int kAhead = 4;  // token rows loaded ahead of their use
 
 template <typename T> struct Vec8;
 template <> struct Vec8<bf16_t> {
@@ -36,7 +37,7 @@ template <> struct Vec8<bf16_t> {
     u32x4 w;
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] = pack2_bf16(v[2 * i], v[2 * i + 1]);
-    *reinterpret_cast<u32x4 *>(p) = w;
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(p));  // streamed out, not re-read here
   }
 };
 template <> struct Vec8<float> {
@@ -73,8 +74,8 @@ __global__ __launch_bounds__(kThreads) void conv1d_silu_kernel(ConvParams p) {
   const int t0 = tile * kTile;
   const int t1 = min(p.L, t0 + kTile);
 
-  const T *x = reinterpret_cast<const T *>(p.x) + (int64_t)b * p.x_sb + c0;
-  T *out = reinterpret_cast<T *>(p.out) + (int64_t)b * p.o_sb + c0;
+  const T *__restrict__ x = reinterpret_cast<const T *>(p.x) + (int64_t)b * p.x_sb + c0;
+  T *__restrict__ out = reinterpret_cast<T *>(p.out) + (int64_t)b * p.o_sb + c0;
   const T *sin = reinterpret_cast<const T *>(p.state_in);
 
   float w[kVec][kConvWidth];
@@ -113,11 +114,11 @@ __global__ __launch_bounds__(kThreads) void conv1d_silu_kernel(ConvParams p) {
     }
   }
 
-  for (int t = t0; t < t1; ++t) {
+  auto step = [&](int t, const float(&v)[kVec]) {
     if (p.seq_idx) {
-      const int s = min(max(p.seq_idx[t], 0), rows - 1);
-      if (s != cur) {  // first token of a new sequence: its window is its conv state
-        cur = s;
+      const int sq = min(max(p.seq_idx[t], 0), rows - 1);
+      if (sq != cur) {  // first token of a new sequence: its window is its conv state
+        cur = sq;
 #pragma unroll
         for (int r = 0; r < 3; ++r) {
           if (sin) Vec8<T>::load(sin + ((int64_t)cur * (kConvWidth - 1) + r) * p.CH + c0, win[r]);
@@ -125,8 +126,6 @@ __global__ __launch_bounds__(kThreads) void conv1d_silu_kernel(ConvParams p) {
         }
       }
     }
-    float v[kVec];
-    Vec8<T>::load(x + (int64_t)t * p.x_st, v);
     float o[kVec];
 #pragma unroll
     for (int i = 0; i < kVec; ++i) {
@@ -140,6 +139,20 @@ __global__ __launch_bounds__(kThreads) void conv1d_silu_kernel(ConvParams p) {
     Vec8<T>::store(out + (int64_t)t * p.o_st, o);
 #pragma unroll
     for (int i = 0; i < kVec; ++i) { win[0][i] = win[1][i]; win[1][i] = win[2][i]; win[2][i] = v[i]; }
+  };
+  // kAhead rows in flight per thread; the tail of a tile one row at a time
+  int t = t0;
+  for (; t + kAhead <= t1; t += kAhead) {
+    float v[kAhead][kVec];
+#pragma unroll
+    for (int k = 0; k < kAhead; ++k) Vec8<T>::load(x + (int64_t)(t + k) * p.x_st, v[k]);
+#pragma unroll
+    for (int k = 0; k < kAhead; ++k) step(t + k, v[k]);
+  }
+  for (; t < t1; ++t) {
+    float v[kVec];
+    Vec8<T>::load(x + (int64_t)t * p.x_st, v);
+    step(t, v);
   }
 }
 
