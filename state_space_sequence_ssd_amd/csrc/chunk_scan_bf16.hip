@@ -224,6 +224,11 @@ __device__ __forceinline__ int opaque_lane() {
   asm volatile("" : "+v"(l));
   return l;
 }
+// A value the compiler cannot see through: x XOR (an opaque zero).
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
 
 // Where one lane sits in the MFMA layouts, and the per-lane LDS byte offsets
 // of its operands at k-step 0.  The swizzles only look at the low 4 (B tile) /
@@ -394,10 +399,25 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
   // cs/dt/w/v), barrier A, the next chunk's loads and dt and this chunk's state
   // into the same buffers, barrier B, then the y stores.  The other workgroup
   // on the CU runs while this one waits.
+  // operand offsets once per segment (a few registers); the rest of the lane
+  // geometry is re-derived in every chunk from an opaque lane id
+  LaneGeo<NCB> LG;
+  LG.template init<Cf>(threadIdx.x & 63);
   f32x16 yo[2];
   for (int c0 = it.tok0; c0 < it.tok1; c0 += kChunk) {
-    LaneGeo<NCB> L;
-    L.template init<Cf>(opaque_lane());
+    struct {
+      int lane, l32, hh;
+    } L;
+    L.lane = opaque_lane();
+    L.l32 = L.lane & 31;
+    L.hh = L.lane >> 5;
+    // row-major operand bases, made opaque per chunk so that their eight
+    // XOR-stepped addresses are formed in the k-loop, not hoisted
+    uint32_t oBr[NCB > 0 ? NCB : 1], oH[2];
+#pragma unroll
+    for (int jb = 0; jb < NCB; ++jb) oBr[jb] = opaque(LG.oBr[jb]);
+    oH[0] = opaque(LG.oH[0]);
+    oH[1] = opaque(LG.oH[1]);
     const int ci = 32 * W + L.l32;  // this lane's chunk row i (full pass)
     const int nv = min(kChunk, it.tok1 - c0);
     const int c1 = c0 + kChunk;
@@ -428,14 +448,14 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
       }
 #pragma unroll
       for (int q = 0; q < 2; ++q)
-        if (Cf::uses_spb(q)) f[k++] = trd(sm.X, L.oXt[q][0] + 2048 * s, L.oXt[q][1] + 2048 * s);
+        if (Cf::uses_spb(q)) f[k++] = trd(sm.X, LG.oXt[q][0] + 2048 * s, LG.oXt[q][1] + 2048 * s);
 #pragma unroll
-      for (int u = 0; u < NNB; ++u) f[k++] = trd(sm.B, L.oBt[u][0] + 4096 * s, L.oBt[u][1] + 4096 * s);
+      for (int u = 0; u < NNB; ++u) f[k++] = trd(sm.B, LG.oBt[u][0] + 4096 * s, LG.oBt[u][1] + 4096 * s);
       if (kFull) {
 #pragma unroll
-        for (int jb = 0; jb < NCB; ++jb) f[k++] = lds_ld<bf16x8>(sm.B + (L.oBr[jb] ^ (32 * s)));
+        for (int jb = 0; jb < NCB; ++jb) f[k++] = lds_ld<bf16x8>(sm.B + (oBr[jb] ^ (32 * s)));
 #pragma unroll
-        for (int q = 0; q < 2; ++q) f[k++] = lds_ld<bf16x8>(sm.H + (L.oH[q] ^ (32 * s)));
+        for (int q = 0; q < 2; ++q) f[k++] = lds_ld<bf16x8>(sm.H + (oH[q] ^ (32 * s)));
       }
     };
     auto mfma_step = [&](int s, const bf16x8 *f, const f32x4 *wv) {
@@ -512,9 +532,9 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
             for (int t = 0; t < 4; ++t) {
               const int r = 4 * q + t;
               const int d = ci - (jq + t);
-              const float gv = G[jb][r];
-              const float mv = gv * __expf(fminf(cs_i - cj[t], 0.f)) * dj[t];
-              Mb[r >> 3][r & 7] = (__bf16)(d > 0 ? mv : (d == 0 ? fmaf(gv, dj[t], Dh) : 0.f));
+              // exp(-inf) = 0 above the diagonal; D joins on it (exp(0) = 1)
+              const float e = __expf(d >= 0 ? cs_i - cj[t] : -INFINITY);
+              Mb[r >> 3][r & 7] = (__bf16)fmaf(G[jb][r] * e, dj[t], d == 0 ? Dh : 0.f);
             }
           }
         }
@@ -524,7 +544,7 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
         for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
           for (int q = 0; q < 2; ++q) {
-            const uint32_t o = L.oYd[q] + 128 * (32 * jb + 16 * s2);
+            const uint32_t o = LG.oYd[q] + 128 * (32 * jb + 16 * s2);
             yo[q] = mfma32(trd(sm.X, o, o + 1024), Mb[s2], yo[q]);
           }
       }
