@@ -334,16 +334,18 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
   };
   // C rows i of this wave's i-block: this lane's 8 k-steps of the MFMA operand
   u32x4 cf[8];
+  // (uniform 64-bit base + per-lane 32-bit byte offset: scalar-base addressing)
   auto load_c = [&](int ln, int c0, int nv) {
     const int ci = 32 * W + (ln & 31);
-    const bf16_t *crow = Cg + (int64_t)c0 * p.C_st + (uint32_t)min(ci, nv - 1) * cst + 8 * (ln >> 5);
+    const char *cc = reinterpret_cast<const char *>(Cg + (int64_t)c0 * p.C_st);
+    const uint32_t o = (uint32_t)min(ci, nv - 1) * cst * 2 + 16 * (ln >> 5);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) cf[s] = *reinterpret_cast<const u32x4 *>(crow + 16 * s);
+    for (int s = 0; s < 8; ++s) cf[s] = *reinterpret_cast<const u32x4 *>(cc + o + 32 * s);
   };
   auto load_dt_raw = [&](int ln, int c0, int nv) -> uint32_t {
-    const bf16_t *dc = dtg + (int64_t)c0 * p.dt_st;
-    const uint32_t lo = dc[(uint32_t)min(2 * ln, nv - 1) * dst];
-    const uint32_t hi = dc[(uint32_t)min(2 * ln + 1, nv - 1) * dst];
+    const char *dc = reinterpret_cast<const char *>(dtg + (int64_t)c0 * p.dt_st);
+    const uint32_t lo = *reinterpret_cast<const bf16_t *>(dc + (uint32_t)min(2 * ln, nv - 1) * dst * 2);
+    const uint32_t hi = *reinterpret_cast<const bf16_t *>(dc + (uint32_t)min(2 * ln + 1, nv - 1) * dst * 2);
     return lo | (hi << 16);
   };
 
@@ -564,11 +566,12 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
           lds_st<u32x2>(sm.X + off128(ci, 32 * q + 8 * r4 + 4 * L.hh), v);
         }
       const int rr = 32 * W + (L.lane >> 3);  // + 8k: rows this lane stores
-      bf16_t *ybase = yg + (int64_t)c0 * p.y_st + 8 * (L.lane & 7);
+      char *yc = reinterpret_cast<char *>(yg + (int64_t)c0 * p.y_st);
+      const uint32_t yo0 = (uint32_t)rr * yst * 2 + 16 * (L.lane & 7), ystep = 8 * yst * 2;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const u32x4 v = lds_ld<u32x4>(sm.X + off128(rr + 8 * k, 8 * (L.lane & 7)));
-        if (rr + 8 * k < nv) *reinterpret_cast<u32x4 *>(ybase + (uint32_t)(rr + 8 * k) * yst) = v;
+        if (rr + 8 * k < nv) *reinterpret_cast<u32x4 *>(yc + yo0 + k * ystep) = v;
       }
     }
     if (W == kDtWave && has_next) chunk_dt_wave(raw_next, nvn, bias, Ah, sm.cs, sm.dt, sm.w, sm.v, sm.misc);
