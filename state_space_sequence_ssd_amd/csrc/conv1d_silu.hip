@@ -23,8 +23,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kVec = 8;    // channels per thread
-constexpr int kTile = 64;  // tokens per thread (the 3-row halo re-read is 3/64 of the input)
-constexpr int kAhead = 4;  // token rows loaded ahead of their use
+constexpr int kTile = 32;  // tokens per thread (the 3-row halo re-read is 3/32 of the input)
+constexpr int kAhead = 8;  // token rows loaded ahead of their use
 
 template <typename T> struct Vec8;
 template <> struct Vec8<bf16_t> {
