@@ -70,21 +70,24 @@ __device__ __forceinline__ int off128(int row, int col) {
   return row * 128 + ((((col >> 3) ^ swz8(row))) << 4) + ((col & 7) << 1);
 }
 
+// Per-token arrays of one chunk (cs, dt, w, v) and exp(cs_last), cs_last.
+constexpr int kSmallBytes = 4 * kChunk * 4 + 16;
 struct Smem {
   uint8_t B[kChunk * 256];    // B[j][n], token-major
   uint8_t X[kChunk * 128];    // x[j][p], token-major
   uint8_t H[kHeadDim * 256];  // running state H[p][n] in bf16
-  float cs[kChunk];
-  float dt[kChunk];
-  float w[kChunk];
-  float v[kChunk];
-  float misc[4];              // exp(cs_last), cs_last
+  // y[i][p] staging between barriers A and B, 128-byte rows like the x tile.
+  // Its last kSmallBytes are the per-token arrays: they lie in rows that only
+  // the dt wave stages, and it rewrites them after reading its y rows back.
+  uint8_t Y[kChunk * 128];
 };
+constexpr int kSmallOff = kChunk * 128 - kSmallBytes;
 // two workgroups per CU: each fits in half of the 160 KiB LDS
 static_assert(sizeof(Smem) <= 80 * 1024, "LDS budget of one of two workgroups per CU");
+static_assert(kSmallOff % 16 == 0, "per-token arrays 16-byte aligned");
 
 struct Lds {
-  lds_u8 *B, *X, *H;
+  lds_u8 *B, *X, *H, *Y;
   lds_f32 *cs, *dt, *w, *v, *misc;
 };
 
@@ -95,6 +98,8 @@ constexpr int kNS[4] = {4, 3, 1, 0};
 constexpr int kSnb[4][4] = {{0, 1, 2, 3}, {0, 1, 2, 0}, {3, 0, 0, 0}, {0, 0, 0, 0}};
 constexpr int kSpb[4][4] = {{0, 0, 0, 0}, {1, 1, 1, 0}, {1, 0, 0, 0}, {0, 0, 0, 0}};
 constexpr int kDtWave = 3;  // the wave that computes the next chunk's dt / cumsum (no state tiles)
+// the per-token arrays overlay staging rows of the dt wave only
+static_assert(kSmallOff >= 32 * kDtWave * 128 && 32 * (kDtWave + 1) == kChunk, "arrays in the dt wave's y rows");
 
 template <bool kFull, int W> struct Cfg {
   static constexpr int NCB = kFull ? W + 1 : 0;
@@ -189,9 +194,24 @@ __device__ __forceinline__ float softplus_fast(float z) {
 }
 
 // dt, cs, w = exp(cs_last - cs) dt and v = exp(cs_r - cs) dt (r = end of the
-// token's 32-block) of one chunk, by one wave (tokens 2 lane, 2 lane + 1).
-__device__ __forceinline__ void chunk_dt_wave(uint32_t raw, int nv, float bias, float A, lds_f32 *cs,
-                                              lds_f32 *dt, lds_f32 *w, lds_f32 *v, lds_f32 *misc) {
+// token's 32-block) of one chunk, by one wave (tokens 2 lane, 2 lane + 1),
+// held in registers until store() puts them in LDS.
+struct ChunkDt {
+  f32x2 cs, dt, w, v;
+  float dec, total;
+  __device__ __forceinline__ void store(lds_f32 *cs_, lds_f32 *dt_, lds_f32 *w_, lds_f32 *v_, lds_f32 *misc) const {
+    const int j0 = 2 * (threadIdx.x & 63);
+    *reinterpret_cast<SSD_LDS f32x2 *>(cs_ + j0) = cs;
+    *reinterpret_cast<SSD_LDS f32x2 *>(dt_ + j0) = dt;
+    *reinterpret_cast<SSD_LDS f32x2 *>(w_ + j0) = w;
+    *reinterpret_cast<SSD_LDS f32x2 *>(v_ + j0) = v;
+    if ((threadIdx.x & 63) == 0) {
+      misc[0] = dec;
+      misc[1] = total;
+    }
+  }
+};
+__device__ __forceinline__ ChunkDt chunk_dt_wave(uint32_t raw, int nv, float bias, float A) {
   const int lane = threadIdx.x & 63;
   const int j0 = 2 * lane;
   const float d0 = j0 < nv ? softplus_fast(lo_bf16(raw) + bias) : 0.f;
@@ -206,14 +226,14 @@ __device__ __forceinline__ void chunk_dt_wave(uint32_t raw, int nv, float bias, 
   const float e2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), 47));
   const int blk = lane >> 4;
   const float cr = blk == 0 ? e0 : blk == 1 ? e1 : blk == 2 ? e2 : total;
-  *reinterpret_cast<SSD_LDS f32x2 *>(cs + j0) = f32x2{cs0, cs1};
-  *reinterpret_cast<SSD_LDS f32x2 *>(dt + j0) = f32x2{d0, d1};
-  *reinterpret_cast<SSD_LDS f32x2 *>(w + j0) = f32x2{__expf(total - cs0) * d0, __expf(total - cs1) * d1};
-  *reinterpret_cast<SSD_LDS f32x2 *>(v + j0) = f32x2{__expf(cr - cs0) * d0, __expf(cr - cs1) * d1};
-  if (lane == 0) {
-    misc[0] = __expf(total);
-    misc[1] = total;
-  }
+  ChunkDt r;
+  r.cs = f32x2{cs0, cs1};
+  r.dt = f32x2{d0, d1};
+  r.w = f32x2{__expf(total - cs0) * d0, __expf(total - cs1) * d1};
+  r.v = f32x2{__expf(cr - cs0) * d0, __expf(cr - cs1) * d1};
+  r.dec = __expf(total);
+  r.total = total;
+  return r;
 }
 
 // Lane id through an empty asm: values derived from it are recomputed in
@@ -390,7 +410,7 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
     const int nv0 = min(kChunk, ntok);
     if (kFull) load_c(ln, it.tok0, nv0);
     if (W == kDtWave)
-      chunk_dt_wave(load_dt_raw(ln, it.tok0, nv0), nv0, bias, Ah, sm.cs, sm.dt, sm.w, sm.v, sm.misc);
+      chunk_dt_wave(load_dt_raw(ln, it.tok0, nv0), nv0, bias, Ah).store(sm.cs, sm.dt, sm.w, sm.v, sm.misc);
     if (kFull) write_state_lds(ln);
     issue_tiles(ln, it.tok0, nv0);  // last, for the same reason as in the loop
     __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
@@ -552,10 +572,18 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
       }
     }
     __syncthreads();  // A: every read of this chunk's tiles, H and cs/dt/w/v is done
+    // the next chunk's direct loads go first, so that they land while this
+    // wave writes H and stages y: LDS writes do not wait for them, the first
+    // LDS read behind them (the y read-back) does
+    // raw_next (loaded at the top of the chunk) is waited for here: a wait for
+    // it behind the direct loads would be a wait for all of them
+    if (W == kDtWave) asm volatile("" ::"v"(raw_next));
+    if (has_next) issue_tiles(L.lane, c1, nvn);
+    __builtin_amdgcn_sched_barrier(0);  // keep them first
     if (kFull) {
-      // y rows through this wave's own rows of the x tile (free until its loads
-      // of the next chunk), so each store writes 8 whole 128-byte rows.  The
-      // lane holds p = 32q + 8 r4 + 4 hh + 0..3 of chunk row ci.
+      write_state_lds(L.lane);  // H_c for the next chunk's state->output product
+      // y rows through the staging tile, so each store writes 8 whole
+      // 128-byte rows.  The lane holds p = 32q + 8 r4 + 4 hh + 0..3 of chunk row ci.
 #pragma unroll
       for (int q = 0; q < 2; ++q)
 #pragma unroll
@@ -563,22 +591,23 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
           u32x2 v;
           v[0] = pack2_bf16(yo[q][4 * r4], yo[q][4 * r4 + 1]);
           v[1] = pack2_bf16(yo[q][4 * r4 + 2], yo[q][4 * r4 + 3]);
-          lds_st<u32x2>(sm.X + off128(ci, 32 * q + 8 * r4 + 4 * L.hh), v);
+          lds_st<u32x2>(sm.Y + off128(ci, 32 * q + 8 * r4 + 4 * L.hh), v);
         }
+    }
+    ChunkDt nd;
+    if (W == kDtWave && has_next) nd = chunk_dt_wave(raw_next, nvn, bias, Ah);
+    if (kFull) {
       const int rr = 32 * W + (L.lane >> 3);  // + 8k: rows this lane stores
       char *yc = reinterpret_cast<char *>(yg + (int64_t)c0 * p.y_st);
       const uint32_t yo0 = (uint32_t)rr * yst * 2 + 16 * (L.lane & 7), ystep = 8 * yst * 2;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const u32x4 v = lds_ld<u32x4>(sm.X + off128(rr + 8 * k, 8 * (L.lane & 7)));
+        const u32x4 v = lds_ld<u32x4>(sm.Y + off128(rr + 8 * k, 8 * (L.lane & 7)));
         if (rr + 8 * k < nv) *reinterpret_cast<u32x4 *>(yc + yo0 + k * ystep) = v;
       }
     }
-    if (W == kDtWave && has_next) chunk_dt_wave(raw_next, nvn, bias, Ah, sm.cs, sm.dt, sm.w, sm.v, sm.misc);
-    if (kFull) write_state_lds(L.lane);  // H_c for the next chunk's state->output product
-    // the direct loads go last: any LDS access behind them in this wave would
-    // first wait for them to land
-    if (has_next) issue_tiles(L.lane, c1, nvn);
+    // after this wave's y read-back: the arrays overlay its staging rows
+    if (W == kDtWave && has_next) nd.store(sm.cs, sm.dt, sm.w, sm.v, sm.misc);
     __builtin_amdgcn_s_waitcnt(0);       // this wave's direct loads of the next chunk have landed
     __syncthreads();                     // B: ... and every wave's
   }
@@ -605,8 +634,9 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
 template <bool kFull>
 __global__ __launch_bounds__(kThr, 2) void chunk_scan_bf16_kernel(ScanParams p, ScanPlan plan, char *ws) {
   __shared__ __attribute__((aligned(16))) Smem smem;
-  const Lds sm{(lds_u8 *)smem.B, (lds_u8 *)smem.X, (lds_u8 *)smem.H, (lds_f32 *)smem.cs,
-               (lds_f32 *)smem.dt, (lds_f32 *)smem.w, (lds_f32 *)smem.v, (lds_f32 *)smem.misc};
+  lds_f32 *small = (lds_f32 *)((lds_u8 *)smem.Y + kSmallOff);
+  const Lds sm{(lds_u8 *)smem.B, (lds_u8 *)smem.X, (lds_u8 *)smem.H, (lds_u8 *)smem.Y,
+               small, small + kChunk, small + 2 * kChunk, small + 3 * kChunk, small + 4 * kChunk};
   int item, h, g;
   if (!map_workgroup(p, plan, item, h, g)) return;
   Item it;
