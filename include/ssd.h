@@ -83,7 +83,12 @@ typedef enum ssd_dtype {
  * Sequences: without seq_idx every batch row is one sequence (rows = batch).
  * With seq_idx (batch must be 1) token t belongs to sequence seq_idx[t];
  * seq_idx must be non-decreasing with values in [0, num_seqs) (rows =
- * num_seqs).  Sequences with no token are allowed.
+ * num_seqs).  Sequences with no token are allowed.  This is a precondition:
+ * by default it is not checked (a value out of range is read out of range).
+ * With SSD_DEBUG=1 in the environment, ssd_conv1d_silu and
+ * ssd_chunk_scan_fwd first check seq_idx on the device, wait for the
+ * answer (a synchronising call) and return SSD_ERR_INVALID_ARG, naming the
+ * first bad token, before any kernel reads by it.
  *
  * conv_state_in / conv_state_out: (rows, width-1, channels), contiguous,
  * same dtype as x.  Row r of a sequence's state is the input width-1-r

@@ -13,7 +13,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libssd.so")
-SOURCES = ["api.hip", "conv1d_silu.hip", "decode_step.hip", "chunk_scan.hip", "chunk_scan_bf16.hip"]
+SOURCES = ["api.hip", "conv1d_silu.hip", "decode_step.hip", "chunk_scan.hip", "chunk_scan_bf16.hip",
+           "debug_checks.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

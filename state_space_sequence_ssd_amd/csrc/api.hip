@@ -2,10 +2,13 @@
 // error reporting and dispatch to the gfx950 kernels.  Every check here is
 // host arithmetic on the argument struct and runs before any HIP call.
 #include <algorithm>
+#include <climits>
 #include <cstdarg>
+#include <cstdlib>
 #include <cstdio>
 #include <cstring>
 
+#include "debug_checks.h"
 #include "kernels.h"
 #include "ssd.h"
 
@@ -35,6 +38,24 @@ int dtype_size(int dt) { return dt == SSD_DTYPE_BF16 ? 2 : 4; }
 bool vec_ok(const void *p, int64_t s0, int64_t s1, int esize) {
   const int64_t per = 16 / esize;
   return aligned16(p) && s0 % per == 0 && s1 % per == 0;
+}
+
+// SSD_DEBUG=1: device checks of seq_idx before the kernels that index by it
+// (a synchronising call; off by default, when nothing is checked on the device).
+bool debug_checks() {
+  const char *e = std::getenv("SSD_DEBUG");
+  return e && e[0] == '1' && e[1] == 0;
+}
+
+int debug_check_seq_idx(const char *fn, const int32_t *seq, int L, int num_seqs, void *stream) {
+  if (!seq || L <= 0 || !debug_checks()) return SSD_OK;
+  int bad = INT_MAX;
+  const hipError_t e = ssd::check_seq_idx(seq, L, num_seqs, reinterpret_cast<hipStream_t>(stream), &bad);
+  if (e != hipSuccess) return fail(SSD_ERR_HIP, "%s: seq_idx check: %s", fn, hipGetErrorString(e));
+  if (bad != INT_MAX)
+    return fail(SSD_ERR_INVALID_ARG, "%s: seq_idx[%d] is outside [0, %d) or below its predecessor (SSD_DEBUG check)",
+                fn, bad, num_seqs);
+  return SSD_OK;
 }
 
 // ---------------------------------------------------------------------------
@@ -143,6 +164,8 @@ int ssd_conv1d_silu(const ssd_conv_args *a, void *stream) {
   p.w = a->weight; p.bias = a->bias;
   p.seq_idx = a->seq_idx; p.num_seqs = a->num_seqs;
   p.state_in = a->conv_state_in; p.state_out = a->conv_state_out;
+  const int drc = debug_check_seq_idx("ssd_conv1d_silu", a->seq_idx, a->seqlen, a->num_seqs, stream);
+  if (drc != SSD_OK) return drc;
   const hipError_t e = ssd::launch_conv1d_silu(p, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SSD_ERR_HIP, "ssd_conv1d_silu: %s", hipGetErrorString(e));
   return ok();
@@ -164,6 +187,8 @@ int ssd_chunk_scan_fwd(const ssd_scan_args *a, void *workspace, size_t ws_bytes,
                 ws_bytes);
   if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u))
     return fail(SSD_ERR_MISALIGNED, "ssd_chunk_scan_fwd: workspace must be 256-byte aligned");
+  const int drc = debug_check_seq_idx("ssd_chunk_scan_fwd", a->seq_idx, a->seqlen, a->num_seqs, stream);
+  if (drc != SSD_OK) return drc;
   const hipError_t e = ssd::launch_chunk_scan(p, plan, workspace, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SSD_ERR_HIP, "ssd_chunk_scan_fwd: %s", hipGetErrorString(e));
   return ok();

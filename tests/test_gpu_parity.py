@@ -122,6 +122,35 @@ def test_conv_batch_mode_strided_input():
 # ---------------------------------------------------------------------------
 # decode step
 # ---------------------------------------------------------------------------
+def test_debug_seq_idx_checks(monkeypatch):
+    """SSD_DEBUG=1: a valid seq_idx runs unchanged; a decreasing or out-of-range
+    one is refused (INVALID_ARG naming the first bad token) before any kernel
+    reads by it."""
+    w = W("bf16_packed_conv_h8_g2", 1, 0, 8, 2, conv=True, lens=[5, 130, 1, 64])
+    d = inputs.make_scan_inputs(w, seed=4)
+    y0, f0 = gpu_layer(d, w)
+    monkeypatch.setenv("SSD_DEBUG", "1")
+    y1, f1 = gpu_layer(d, w)
+    assert torch.equal(y0, y1) and torch.equal(f0, f1)
+    H, G, L = w.nheads, w.ngroups, w.seqlen
+    xbc = to_dev(d["xBC"], BF)
+    x, B, C = split_xbc(xbc, H, G)
+    good = d["seq_idx"]
+    for name, seq, first in [("decreasing", np.where(np.arange(L) == 100, 0, good), 100),
+                             ("too large", np.where(np.arange(L) >= 150, 4, good), 150),
+                             ("negative", np.where(np.arange(L) == 0, -1, good), 0)]:
+        print(f"case {name}: first bad token {first}", flush=True)
+        sq = to_dev(seq.astype(np.int32))
+        with pytest.raises(ssd.SsdError) as ei:
+            ssd.ssd_conv1d_silu(xbc, to_dev(d["conv_w"]), seq_idx=sq, num_seqs=4)
+        assert ei.value.code == 1 and f"seq_idx[{first}]" in str(ei.value)
+        with pytest.raises(ssd.SsdError) as ei:
+            ssd.ssd_chunk_scan_fwd(x, to_dev(d["dt"], BF), to_dev(d["A"]), B, C, seq_idx=sq, num_seqs=4,
+                                   final_state=torch.empty((4, H, 64, 128), device=DEV))
+        assert ei.value.code == 1 and f"seq_idx[{first}]" in str(ei.value)
+    torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("bf16,conv", [(True, True), (True, False), (False, True), (False, False)])
 def test_decode_small(bf16, conv):
     w = inputs.DecodeWorkload("dec", 3, 16, 4, 1, bf16=bf16)
