@@ -36,6 +36,9 @@ SMALL = [
     (W("bf16_packed_h8_g2_init", 1, 0, 8, 2, init=0.3, lens=[1, 3, 200, 129, 128, 64, 300, 2]), 0),
     (W("bf16_packed_seg1_h8_g2_init", 1, 0, 8, 2, init=0.3, lens=[1, 3, 200, 129, 128, 64, 300, 2]), 1),
     (W("bf16_packed_conv_h16_g8", 1, 0, 16, 8, conv=True, lens=[77, 5, 260]), 0),
+    # sequences with no token (first, middle, last): their final state is their initial one
+    (W("bf16_packed_empty_h8_g2_init", 1, 0, 8, 2, init=0.3, lens=[0, 5, 0, 130, 1, 0]), 0),
+    (W("bf16_packed_empty_conv_seg1_h8_g2", 1, 0, 8, 2, conv=True, lens=[0, 200, 0, 3]), 1),
     (inputs.tiny_fp32(), 0),
     (W("fp32_conv_b2_l200_h8_g2_init", 2, 200, 8, 2, bf16=False, conv=True, init=0.3), 0),
     (W("fp32_seg1_b1_l300_h4_g1_init", 1, 300, 4, 1, bf16=False, init=0.3), 1),
