@@ -37,6 +37,8 @@
 //     accumulators, bf16 in LDS as the operand of the state->output product.
 //   * C goes global -> registers (each wave its own 32 rows) right after the
 //     k-loop that last reads the current ones.
+#include <type_traits>
+
 #include "scan_items.h"
 
 namespace ssd {
@@ -70,7 +72,8 @@ __device__ __forceinline__ int off128(int row, int col) {
   return row * 128 + ((((col >> 3) ^ swz8(row))) << 4) + ((col & 7) << 1);
 }
 
-// Per-token arrays of one chunk (cs, dt, w, v) and exp(cs_last), cs_last.
+// Per-token arrays of one chunk (cs, dt, w, v), then exp(cs_last), cs_last and
+// the counter of waves done with the chunk's B tile.
 constexpr int kSmallBytes = 4 * kChunk * 4 + 16;
 struct Smem {
   uint8_t B[kChunk * 256];    // B[j][n], token-major
@@ -208,6 +211,7 @@ struct ChunkDt {
     if ((threadIdx.x & 63) == 0) {
       misc[0] = dec;
       misc[1] = total;
+      misc[2] = 0.f;  // the B-load counter of the chunk (all bits zero)
     }
   }
 };
@@ -234,6 +238,17 @@ __device__ __forceinline__ ChunkDt chunk_dt_wave(uint32_t raw, int nv, float bia
   r.dec = __expf(total);
   r.total = total;
   return r;
+}
+
+// Workgroup barrier for LDS traffic only: this wave's LDS accesses are
+// complete, its global loads (and direct loads to LDS) may still be in
+// flight.  The empty asm keeps the compiler from moving memory accesses
+// across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt not waited for
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // Lane id through an empty asm: values derived from it are recomputed in
@@ -310,23 +325,38 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
   const float Ah = p.A[h];
   const float Dh = p.D ? p.D[h] : 0.f;
 
-  // x / B tiles of one chunk -> LDS by direct loads: wave w fills token rows
-  // [32w, 32w + 32) of both.  Rows past the segment end repeat its last row
-  // (finite values whose every use is cancelled: dt = 0 there).
-  auto issue_tiles = [&](int ln, int c0, int nv) {
+  // B rows [r0, r0 + 4 N) / this wave's x rows of one chunk -> LDS by direct
+  // loads, 4 B rows (8 x rows) per instruction.  Rows past the segment end
+  // repeat its last row (finite values whose every use is cancelled: dt = 0
+  // there).  A whole chunk takes one per-lane 32-bit byte offset per tile,
+  // the row step in the (uniform) base address.
+  auto issue_b = [&](int ln, int c0, int nv, int r0, auto n_instr) {
+    constexpr int N = decltype(n_instr)::value;
     if (nv == kChunk) {
-      // whole chunk: one per-lane 32-bit byte offset per tile, the row step in
-      // the (uniform) base address
       const char *bc = reinterpret_cast<const char *>(Bg + (int64_t)c0 * p.B_st);
-      const char *xc = reinterpret_cast<const char *>(xg + (int64_t)c0 * p.x_st);
-      const uint32_t ob = (32 * W + (ln >> 4)) * bst * 2;
+      const uint32_t ob = (r0 + (ln >> 4)) * bst * 2;
       uint32_t cb[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) cb[i] = ob + 16 * ((ln & 15) ^ swz16((ln >> 4) + 4 * i));
+      for (int i = 0; i < 4; ++i) cb[i] = ob + 16 * ((ln & 15) ^ swz16(r0 + (ln >> 4) + 4 * i));
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < N; ++i)
         __builtin_amdgcn_global_load_lds(bc + (size_t)(8 * i) * bst + cb[i & 3],
-                                         (lds_void *)(sm.B + (32 * W + 4 * i) * 256), 16, 0, 0);
+                                         (lds_void *)(sm.B + (r0 + 4 * i) * 256), 16, 0, 0);
+      return;
+    }
+    const int last = nv - 1;
+    const bf16_t *bc = Bg + (int64_t)c0 * p.B_st;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int r = r0 + 4 * i + (ln >> 4);
+      const int blk = (ln & 15) ^ swz16(r);
+      __builtin_amdgcn_global_load_lds(bc + (uint32_t)min(r, last) * bst + 8 * blk,
+                                       (lds_void *)(sm.B + (r0 + 4 * i) * 256), 16, 0, 0);
+    }
+  };
+  auto issue_x = [&](int ln, int c0, int nv) {
+    if (nv == kChunk) {
+      const char *xc = reinterpret_cast<const char *>(xg + (int64_t)c0 * p.x_st);
       const uint32_t ox = (32 * W + (ln >> 3)) * xst * 2 + 16 * ((ln & 7) ^ swz8(ln >> 3));
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -335,15 +365,7 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
       return;
     }
     const int last = nv - 1;
-    const bf16_t *bc = Bg + (int64_t)c0 * p.B_st;
     const bf16_t *xc = xg + (int64_t)c0 * p.x_st;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = 32 * W + 4 * i + (ln >> 4);
-      const int blk = (ln & 15) ^ swz16(r);
-      __builtin_amdgcn_global_load_lds(bc + (uint32_t)min(r, last) * bst + 8 * blk,
-                                       (lds_void *)(sm.B + (32 * W + 4 * i) * 256), 16, 0, 0);
-    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 32 * W + 8 * i + (ln >> 3);
@@ -351,6 +373,10 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
       __builtin_amdgcn_global_load_lds(xc + (uint32_t)min(r, last) * xst + 8 * blk,
                                        (lds_void *)(sm.X + (32 * W + 8 * i) * 128), 16, 0, 0);
     }
+  };
+  auto issue_tiles = [&](int ln, int c0, int nv) {
+    issue_b(ln, c0, nv, 32 * W, std::integral_constant<int, 8>{});
+    issue_x(ln, c0, nv);
   };
   // C rows i of this wave's i-block: this lane's 8 k-steps of the MFMA operand
   u32x4 cf[8];
@@ -513,8 +539,24 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
       }
     }
     __builtin_amdgcn_s_setprio(0);
+    // raw_next (loaded at the top of the chunk) is waited for here, before any
+    // later load: a wait for it behind those would be a wait for all of them
+    if (W == kDtWave) asm volatile("" ::"v"(raw_next));
     // the C fragments of this chunk are dead: fetch the next chunk's now
     if (kFull) load_c(L.lane, cn, nvn);
+    // B is only read in the k-loop.  The last wave to finish it loads the
+    // whole next B tile at the end of its intra-chunk phase (after its last
+    // LDS read: a read behind a direct load waits for it), ahead of barrier
+    // A, so that only the x tile is left to load after the barrier.  (The
+    // counter is zeroed with the per-token arrays of every chunk.)
+    bool b_loader = false;
+    if (has_next) {
+      uint32_t done = 0;
+      if (L.lane == 0)
+        done = __hip_atomic_fetch_add(reinterpret_cast<SSD_LDS uint32_t *>(sm.misc + 2), 1u, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_WORKGROUP);
+      b_loader = __builtin_amdgcn_readfirstlane(done) == 3;
+    }
 
     if (kFull) {
       // y = exp(cs_i) (C H_prev^T) + M x: scale the state->output part, then the
@@ -571,14 +613,14 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
           }
       }
     }
-    __syncthreads();  // A: every read of this chunk's tiles, H and cs/dt/w/v is done
+    if (b_loader) issue_b(L.lane, c1, nvn, 0, std::integral_constant<int, 32>{});
+    // A: every read of this chunk's tiles, H and cs/dt/w/v is done.  LDS only:
+    // the next B tile may still be landing (nothing reads it before barrier B).
+    lds_barrier();
     // the next chunk's direct loads go first, so that they land while this
     // wave writes H and stages y: LDS writes do not wait for them, the first
     // LDS read behind them (the y read-back) does
-    // raw_next (loaded at the top of the chunk) is waited for here: a wait for
-    // it behind the direct loads would be a wait for all of them
-    if (W == kDtWave) asm volatile("" ::"v"(raw_next));
-    if (has_next) issue_tiles(L.lane, c1, nvn);
+    if (has_next) issue_x(L.lane, c1, nvn);
     __builtin_amdgcn_sched_barrier(0);  // keep them first
     if (kFull) {
       write_state_lds(L.lane);  // H_c for the next chunk's state->output product
