@@ -60,11 +60,15 @@ def read_traffic(kernel_tag, files):
 
 
 def scan_algorithmic_bytes(w, with_final=True):
-    """Each input / output tensor of the scan moved once (chunk states excluded)."""
+    """Each input / output tensor of the scan moved once (chunk states excluded):
+    x, y, B, C, dt per token in the I/O dtype, seq_idx (int32) when packed, the
+    fp32 initial states when given and the final states, the per-head params."""
     T = w.batch * w.seqlen
     H, G, P, N = w.nheads, w.ngroups, w.headdim, w.dstate
-    per_tok = 2 * (H * P) * 2 + 2 * (G * N) * 2 + H * 2      # x, y, B, C, dt (bf16)
-    states = w.num_seqs * H * P * N * 4 if with_final else 0
+    es = 2 if w.bf16 else 4
+    per_tok = (2 * (H * P) + 2 * (G * N) + H) * es + (4 if w.packed_lengths is not None else 0)
+    state = w.num_seqs * H * P * N * 4
+    states = (state if with_final else 0) + (state if w.init_std > 0 else 0)
     return T * per_tok + states + 3 * H * 4
 
 
@@ -76,7 +80,9 @@ def scan_flops(w):
 
 
 def conv_algorithmic_bytes(w):
-    return w.batch * w.seqlen * w.conv_dim * 2 * 2 + w.conv_dim * 4 * 4
+    es = 2 if w.bf16 else 4
+    return (w.batch * w.seqlen * w.conv_dim * 2 * es + w.conv_dim * 4 * 4
+            + (w.batch * w.seqlen * 4 if w.packed_lengths is not None else 0))
 
 
 def decode_algorithmic_bytes(dw):
@@ -88,6 +94,78 @@ def decode_algorithmic_bytes(dw):
             + 2 * b * (dw.conv_width - 1) * CD * 2   # conv state read + write
             + b * H * P * 2 + b * H * 2      # y, dt
             + CD * dw.conv_width * 4 + 3 * H * 4)
+
+
+def time_config(w, seed, steps, warmup):
+    """conv (if the workload has one) + scan of one synthetic config, event-timed
+    per kernel on the launch stream; rates against the HBM roofline."""
+    import numpy as np
+    import torch
+    from state_space_sequence_ssd_amd import inputs, ssd
+    dev = torch.device("cuda:0")
+    dtp = torch.bfloat16 if w.bf16 else torch.float32
+    d = inputs.make_scan_inputs(w, seed=seed)
+    H, G, P, N = w.nheads, w.ngroups, w.headdim, w.dstate
+    Bt, L = w.batch, w.seqlen
+    seq = torch.from_numpy(d["seq_idx"]).to(dev) if "seq_idx" in d else None
+    nseq = w.num_seqs if seq is not None else None
+    if w.conv:
+        xbc = torch.from_numpy(d["xBC"]).to(dev, dtp)
+        conv_w = torch.from_numpy(d["conv_w"]).to(dev)
+        conv_out = torch.empty_like(xbc)
+        x = conv_out[..., :H * P].view(Bt, L, H, P)
+        Bm = conv_out[..., H * P:H * P + G * N].view(Bt, L, G, N)
+        Cm = conv_out[..., H * P + G * N:].view(Bt, L, G, N)
+    else:
+        x = torch.from_numpy(d["x"]).to(dev, dtp)
+        Bm = torch.from_numpy(d["B"]).to(dev, dtp)
+        Cm = torch.from_numpy(d["C"]).to(dev, dtp)
+    dt = torch.from_numpy(d["dt"]).to(dev, dtp)
+    A, D = torch.from_numpy(d["A"]).to(dev), torch.from_numpy(d["D"]).to(dev)
+    dt_bias = torch.from_numpy(d["dt_bias"]).to(dev)
+    init = torch.from_numpy(d["initial_state"]).to(dev) if "initial_state" in d else None
+    y = torch.empty((Bt, L, H, P), dtype=dtp, device=dev)
+    fs = torch.empty((w.num_seqs, H, P, N), dtype=torch.float32, device=dev)
+    wsb = ssd.ssd_chunk_scan_workspace_size(x, dt, A, Bm, Cm, seq_idx=seq, num_seqs=nseq)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        if w.conv:
+            ssd.ssd_conv1d_silu(xbc, conv_w, seq_idx=seq, num_seqs=nseq, out=conv_out)
+        if ev is not None:
+            ev[1].record(stream)
+        ssd.ssd_chunk_scan_fwd(x, dt, A, Bm, Cm, dt_bias=dt_bias, D=D, seq_idx=seq, num_seqs=nseq,
+                               initial_state=init, final_state=fs, y=y, workspace=ws)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    scan_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    sb = scan_algorithmic_bytes(w)
+    out = {"tokens": Bt * L, "io_dtype": "bf16" if w.bf16 else "f32",
+           "scan_avg_ms": round(scan_ms, 5), "scan_algorithmic_bytes": sb,
+           "scan_gbs": round(sb / (scan_ms * 1e-3) / 1e9, 1),
+           "scan_hbm_frac": round(sb / (scan_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "scan_tokens_per_s": round(Bt * L / (scan_ms * 1e-3), 1)}
+    step_ms = scan_ms
+    if w.conv:
+        conv_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        cb = conv_algorithmic_bytes(w)
+        out.update({"conv_avg_ms": round(conv_ms, 5), "conv_algorithmic_bytes": cb,
+                    "conv_gbs": round(cb / (conv_ms * 1e-3) / 1e9, 1),
+                    "conv_hbm_frac": round(cb / (conv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+        step_ms += conv_ms
+    out["layer_tokens_per_s"] = round(Bt * L / (step_ms * 1e-3), 1)
+    return out
 
 
 def cpu_baseline(w, d, rows):
@@ -120,6 +198,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (profiler runs)")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other synthetic configs (profiler runs: same kernel names)")
     ap.add_argument("--cpu-rows", type=int, default=4, help="batch rows in the oracle sample (4 = the whole step)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter calibration)")
@@ -273,6 +353,14 @@ def main():
         del layers
         torch.cuda.empty_cache()
 
+    # ---------------- the other synthetic configs (parity workloads) ----------------
+    configs = None
+    if not args.no_configs:
+        configs = {}
+        for cw, seed in [(inputs.tiny_fp32(), 0), (inputs.nemotron3_nano(), 2), (inputs.packed_3b(), 3)]:
+            configs[cw.name] = time_config(cw, seed, steps=10, warmup=2)
+            torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, d, args.cpu_rows)
@@ -299,6 +387,7 @@ def main():
         "cpu_baseline": None if cpu is None else {k: v for k, v in cpu.items() if k != "seconds"},
         "kernels": kernels,
         "decode": decode,
+        "configs": configs,
     }
     print(json.dumps(line))
 

@@ -1,4 +1,6 @@
-// Chunked SSD prefill of the Mamba-2 selective scan on gfx950.
+// Chunked SSD prefill of the Mamba-2 selective scan on gfx950: the work
+// plan, the fp32 path and the launch sequence (the bf16 MFMA kernel is in
+// chunk_scan_bf16.hip).
 //
 // The layer's per-head recurrence S_t = exp(dt_t A) S_{t-1} + dt_t x_t B_t^T,
 // y_t = S_t C_t + D x_t has a scalar-times-identity transition ("Mamba-3: an
@@ -6,46 +8,33 @@
 // which makes the map over a block of tokens a masked matrix product -- the
 // state space duality with (linear) attention ("AI Engineering EP6",
 // sec. 8 and sec. 10).  Blocks are chunk_size = 128 tokens ("Nemotron-H style
-// Hybrid Mamba-Transformer 3B feasibility study", sec. 1.4).  For a chunk
-// with inclusive in-chunk cumulative log-decay cs_i = sum_{k<=i} dt_k A:
+// Hybrid Mamba-Transformer 3B feasibility study", sec. 1.4).  For a block
+// with inclusive in-block cumulative log-decay cs_i = sum_{k<=i} dt_k A:
 //
-//   CB    = C B^T                                           (Q x Q, K = N)
-//   M_ji  = CB_ij exp(cs_i - cs_j) dt_j  for j <= i, else 0  (+ D on j == i)
-//   y     = exp(cs_i) C_i H_prev^T  +  sum_j M_ji x_j       (K = N, K = Q)
+//   CB    = C B^T                                           (K = N)
+//   M_ij  = CB_ij exp(cs_i - cs_j) dt_j  for j <= i, else 0  (+ D on j == i)
+//   y     = exp(cs_i) C_i H_prev^T  +  sum_j M_ij x_j
 //   H     = exp(cs_last) H_prev + sum_j exp(cs_last - cs_j) dt_j x_j B_j^T
 //
 // Every exponent is a difference cs_i - cs_j with j <= i, so it is <= 0:
-// no exp(+large) ever forms.
+// no exp(+large) ever forms.  The result does not depend on the block
+// length, which the fp32 path uses (64-token sub-blocks).
 //
-// Design (one workgroup = one segment of one sequence x one head, 4 waves):
-//   * the running state H (64 x 128 fp32) never leaves the chip: it lives in
-//     MFMA accumulator registers (wave w owns state rows n in [32w, 32w+32))
-//     and, rounded to bf16, in LDS as the operand of the state->output
-//     product.  Chunk states are never written to HBM, so the kernel moves
-//     each input byte once and each output byte once.
-//   * all four products run on v_mfma_f32_32x32x16_bf16 (bf16 operands, fp32
-//     accumulation).  Wave w owns output rows i in [32w, 32w+32) of the
-//     chunk; it computes the causal CB tiles j-block <= w, turns them into
-//     the decay-masked M in registers, and feeds them straight back as the
-//     MFMA operand of the intra-chunk product (the accumulator layout holds
-//     4+4 rows per lane, used as a permuted K order that the other operand,
-//     read from LDS, follows).
-//   * B is staged twice in LDS (token-major for C B^T, transposed for the
-//     chunk-state product), x once (transposed); C goes global -> registers,
-//     each wave loading only its own 32 rows.  The next chunk's loads are
-//     issued before the current chunk's math.
+// Work: one workgroup = one segment of one sequence x one head; it walks
+// the segment's chunks in order and keeps the state on chip, so chunk
+// states never go to HBM.
 //   * packed sequences: a chunk grid is anchored at each sequence start, so
-//     no chunk ever spans two sequences; the sequence table comes from
-//     seq_idx on the device.
-//   * long sequences with too few (sequence, head) pairs to fill 256 CUs are
-//     cut into segments; a state-only pre-pass gives each segment's local
-//     end state and total decay, a small combine kernel chains them into
-//     entry states, and the full pass then runs all segments in parallel
-//     (segments are the Blelloch-style split of the scan over chunks that
-//     the "Nemotron-Mamba3 architecture" article, sec. 2.2, mentions, one
-//     level deep).
+//     no chunk spans two sequences; plan_kernel builds the sequence table
+//     and work list from seq_idx on the device.
+//   * long sequences with too few (sequence, head) pairs to fill the chip
+//     are cut into segments: a state-only pre-pass gives each segment's
+//     local end state and total log-decay, combine_kernel chains them into
+//     entry states (affine maps h -> a h + S), and the full pass then runs
+//     all segments in parallel -- the split of the scan over chunks that the
+//     "Nemotron-Mamba3 architecture" article, sec. 2.2, mentions, one level
+//     deep.
 //   * workgroup -> work mapping is XCD-aware: consecutive work (the heads of
-//     one group on one segment, which read the same B and C) is sent to the
+//     one group on one segment, which read the same B and C) goes to the
 //     same XCD, so B/C come from HBM once and from that XCD's L2 after.
 #include "common.h"
 #include "kernels.h"
@@ -57,53 +46,65 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// dt, in-chunk cumulative log-decay cs, and the chunk-state weights
-// w_j = exp(cs_last - cs_j) dt_j for one chunk; run by one wave (2 tokens per
-// lane).  Tokens past the end of the sequence get dt = 0, which leaves cs
-// flat and removes them from every product.  Also v_j = exp(cs_r - cs_j) dt_j
-// with r the last token of j's 32-token block (the row factor of the
-// off-diagonal decay tiles).
-__device__ __forceinline__ void chunk_dt(float raw0, float raw1, int j0, int n_valid, float bias,
-                                         float A, float *s_cs, float *s_dt, float *s_w,
-                                         float *s_misc, float *s_v = nullptr) {
+// ---------------------------------------------------------------------------
+// fp32 path: register-tiled FMA kernel (all-fp32 arithmetic, for fp32 inputs)
+// ---------------------------------------------------------------------------
+// The chunk form is exact for any block length, so this path walks each
+// 128-token chunk of the work list as two sub-chunks of kSub = 64 tokens: x,
+// B and C of a sub-chunk, its decay-masked matrix M and a copy of the state
+// then all fit in LDS, and every product is a 4x4 (state: 4x8) register tile
+// per thread over LDS operands.  The fp32 state itself stays in registers.
+constexpr int kSub = 64;
+constexpr int kPadX = kHeadDim + 4;  // LDS row strides (floats): rows stay 16-byte aligned
+constexpr int kPadN = kDState + 4;
+constexpr int kPadM = kSub + 4;
+
+// dt = softplus(dt_raw + bias), inclusive in-sub-chunk cumulative log-decay
+// cs, w = exp(cs_last - cs) dt, and exp(cs_last), cs_last; one token per lane
+// of one wave.  Tokens past the end get dt = 0: cs stays flat and they drop
+// out of every product.
+__device__ __forceinline__ void subchunk_dt(float raw, bool valid, float bias, float A, float *s_cs,
+                                            float *s_dt, float *s_w, float *s_misc) {
   const int lane = threadIdx.x & 63;
-  const float d0 = j0 < n_valid ? softplus_f32(raw0 + bias) : 0.f;
-  const float d1 = j0 + 1 < n_valid ? softplus_f32(raw1 + bias) : 0.f;
-  const float a0 = d0 * A, a1 = d1 * A;
-  float incl = a0 + a1;
+  const float d = valid ? softplus_f32(raw + bias) : 0.f;
+  float incl = d * A;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const float t = __shfl_up(incl, off, 64);
     if (lane >= off) incl += t;
   }
   const float total = __shfl(incl, 63, 64);
-  const float cs1 = incl, cs0 = incl - a1;
-  *reinterpret_cast<float2 *>(s_cs + j0) = make_float2(cs0, cs1);
-  *reinterpret_cast<float2 *>(s_dt + j0) = make_float2(d0, d1);
-  *reinterpret_cast<float2 *>(s_w + j0) =
-      make_float2(__expf(total - cs0) * d0, __expf(total - cs1) * d1);
-  if (s_v) {
-    const float cr = __shfl(incl, lane | 15, 64);  // cs at the end of this 32-token block
-    *reinterpret_cast<float2 *>(s_v + j0) = make_float2(__expf(cr - cs0) * d0, __expf(cr - cs1) * d1);
-  }
+  s_cs[lane] = incl;
+  s_dt[lane] = d;
+  s_w[lane] = expf(total - incl) * d;
   if (lane == 0) {
-    s_misc[0] = __expf(total);
+    s_misc[0] = expf(total);
     s_misc[1] = total;
   }
 }
 
-// ---------------------------------------------------------------------------
-// fp32 path: plain FMA chunk kernel (all-fp32 arithmetic, for fp32 inputs)
-// ---------------------------------------------------------------------------
+__device__ __forceinline__ float4 lds4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+
+// acc[r][c] += a[r] . b[c] over 4 consecutive K values
+__device__ __forceinline__ void fma4x4(float (&acc)[4][4], const float4 (&a)[4], const float4 (&b)[4]) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      acc[r][c] = fmaf(a[r].w, b[c].w, fmaf(a[r].z, b[c].z, fmaf(a[r].y, b[c].y, fmaf(a[r].x, b[c].x, acc[r][c]))));
+}
+
 template <bool kFull>
 __global__ __launch_bounds__(kThreads, 1) void chunk_scan_f32_kernel(ScanParams p, ScanPlan plan,
                                                                      char *ws) {
-  __shared__ __attribute__((aligned(16))) float sX[kChunk * kHeadDim];  // [j][p]
-  __shared__ __attribute__((aligned(16))) float sB[kChunk * kDState];   // [j][n]
-  __shared__ __attribute__((aligned(16))) float sH[kHeadDim * kDState]; // [p][n], the running state
-  __shared__ __attribute__((aligned(16))) float s_cs[kChunk];
-  __shared__ __attribute__((aligned(16))) float s_dt[kChunk];
-  __shared__ __attribute__((aligned(16))) float s_w[kChunk];
+  __shared__ __attribute__((aligned(16))) float sX[kSub * kPadX];      // x[j][p]
+  __shared__ __attribute__((aligned(16))) float sB[kSub * kPadN];      // B[j][n]
+  __shared__ __attribute__((aligned(16))) float sC[kSub * kPadN];      // C[i][n]
+  __shared__ __attribute__((aligned(16))) float sH[kHeadDim * kPadN];  // H[p][n] entering the sub-chunk
+  __shared__ __attribute__((aligned(16))) float sM[kSub * kPadM];      // M[i][j]
+  __shared__ __attribute__((aligned(16))) float s_cs[kSub];
+  __shared__ __attribute__((aligned(16))) float s_dt[kSub];
+  __shared__ __attribute__((aligned(16))) float s_w[kSub];
   __shared__ float s_misc[2];
 
   int item, h, g;
@@ -119,135 +120,163 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_f32_kernel(ScanParams 
   const float *Bg = reinterpret_cast<const float *>(p.B) + it.boff * p.B_sb + g * kDState;
   const float *Cg = reinterpret_cast<const float *>(p.C) + it.boff * p.C_sb + g * kDState;
   const float *dtg = reinterpret_cast<const float *>(p.dt) + it.boff * p.dt_sb + h;
+  float *yg = reinterpret_cast<float *>(p.y) + it.boff * p.y_sb + h * kHeadDim;
   const float bias = p.dt_bias ? p.dt_bias[h] : 0.f;
   const float Ah = p.A[h];
   const float Dh = p.D ? p.D[h] : 0.f;
 
-  // state entries updated by this thread: p = tid / 4, n in [32 (tid % 4), +32)
-  const int sp = tid >> 2, sn0 = 32 * (tid & 3);
+  // output tiles: rows i in [4 ti, +4), columns (j of M, or p of y) in [4 tj, +4)
+  const int ti = tid >> 4, tj = tid & 15;
+  // state tile: p in [4 ti, +4), n in [8 tj, +8), in registers
+  float hs[4][8];
   {
     const float *entry = nullptr;
     if (kFull) {
       if (it.first) entry = p.init ? p.init + ((int64_t)it.row * p.H + h) * kPN : nullptr;
       else entry = ws_f32(plan, ws, plan.ws_entry_off) + ((int64_t)item * p.H + h) * kPN;
     }
-    for (int k = 0; k < 32; ++k) sH[sp * kDState + sn0 + k] = entry ? entry[sp * kDState + sn0 + k] : 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) hs[r][c] = entry ? entry[(4 * ti + r) * kDState + 8 * tj + c] : 0.f;
+    if (kFull) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        *reinterpret_cast<float4 *>(sH + (4 * ti + r) * kPadN + 8 * tj) = make_float4(hs[r][0], hs[r][1], hs[r][2], hs[r][3]);
+        *reinterpret_cast<float4 *>(sH + (4 * ti + r) * kPadN + 8 * tj + 4) = make_float4(hs[r][4], hs[r][5], hs[r][6], hs[r][7]);
+      }
+    }
   }
 
   float logdecay = 0.f;
-  for (int c0 = it.tok0; c0 < it.tok1; c0 += kChunk) {
-    const int nv = min(kChunk, it.tok1 - c0);
-    // stage x, B and dt of this chunk
-    for (int f = tid; f < kChunk * kHeadDim / 4; f += kThreads) {
-      const int j = f / (kHeadDim / 4), c4 = f % (kHeadDim / 4);
-      reinterpret_cast<float4 *>(sX)[f] =
-          j < nv ? *reinterpret_cast<const float4 *>(xg + (int64_t)(c0 + j) * p.x_st + 4 * c4)
-                 : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c0 = it.tok0; c0 < it.tok1; c0 += kSub) {
+    const int nv = min(kSub, it.tok1 - c0);
+    // stage x, B (and C) of this sub-chunk, rows past the end zero
+#pragma unroll
+    for (int k = 0; k < kSub * kHeadDim / 4 / kThreads; ++k) {
+      const int f = tid + k * kThreads, j = f >> 4, c4 = f & 15;
+      *reinterpret_cast<float4 *>(sX + j * kPadX + 4 * c4) =
+          j < nv ? *reinterpret_cast<const float4 *>(xg + (int64_t)(c0 + j) * p.x_st + 4 * c4) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    for (int f = tid; f < kChunk * kDState / 4; f += kThreads) {
-      const int j = f / (kDState / 4), c4 = f % (kDState / 4);
-      reinterpret_cast<float4 *>(sB)[f] =
-          j < nv ? *reinterpret_cast<const float4 *>(Bg + (int64_t)(c0 + j) * p.B_st + 4 * c4)
-                 : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int k = 0; k < kSub * kDState / 4 / kThreads; ++k) {
+      const int f = tid + k * kThreads, j = f >> 5, c4 = f & 31;
+      *reinterpret_cast<float4 *>(sB + j * kPadN + 4 * c4) =
+          j < nv ? *reinterpret_cast<const float4 *>(Bg + (int64_t)(c0 + j) * p.B_st + 4 * c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+      if (kFull)
+        *reinterpret_cast<float4 *>(sC + j * kPadN + 4 * c4) =
+            j < nv ? *reinterpret_cast<const float4 *>(Cg + (int64_t)(c0 + j) * p.C_st + 4 * c4) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     if (wv == 0) {
-      const int j = 2 * lane;
-      const float r0 = j < nv ? dtg[(int64_t)(c0 + j) * p.dt_st] : 0.f;
-      const float r1 = j + 1 < nv ? dtg[(int64_t)(c0 + j + 1) * p.dt_st] : 0.f;
-      chunk_dt(r0, r1, j, nv, bias, Ah, s_cs, s_dt, s_w, s_misc);
+      const float raw = lane < nv ? dtg[(int64_t)(c0 + lane) * p.dt_st] : 0.f;
+      subchunk_dt(raw, lane < nv, bias, Ah, s_cs, s_dt, s_w, s_misc);
     }
     __syncthreads();
 
+    float yo[4][4];
     if (kFull) {
-      // outputs: thread -> row i = tid / 2, p in [32 (tid % 2), +32)
-      const int i = tid >> 1, p0 = 32 * (tid & 1);
-      if (i < nv) {
-        const float *cr = Cg + (int64_t)(c0 + i) * p.C_st;
-        const float cs_i = s_cs[i];
-        // state -> output: yo[k] = sum_n C[i][n] H[p0 + k][n]
-        float yo[32];
+      // M[i][j] = (C_i . B_j) exp(cs_i - cs_j) dt_j for j < i, (C_i . B_i) dt_i + D on
+      // the diagonal, 0 above it; tiles entirely above the diagonal are never read
+      if (tj <= ti) {
+        float cb[4][4] = {};
+        for (int n = 0; n < kDState; n += 4) {
+          float4 a[4], b[4];
 #pragma unroll
-        for (int k = 0; k < 32; ++k) yo[k] = 0.f;
-        for (int n4 = 0; n4 < kDState / 4; ++n4) {
-          const float4 cv = reinterpret_cast<const float4 *>(cr)[n4];
+          for (int r = 0; r < 4; ++r) a[r] = lds4(sC + (4 * ti + r) * kPadN + n);
 #pragma unroll
-          for (int k = 0; k < 32; ++k) {
-            const float4 hv = *reinterpret_cast<const float4 *>(sH + (p0 + k) * kDState + 4 * n4);
-            yo[k] = fmaf(cv.x, hv.x, fmaf(cv.y, hv.y, fmaf(cv.z, hv.z, fmaf(cv.w, hv.w, yo[k]))));
-          }
+          for (int c = 0; c < 4; ++c) b[c] = lds4(sB + (4 * tj + c) * kPadN + n);
+          fma4x4(cb, a, b);
         }
-        // intra-chunk: yd[k] = sum_{j<=i} (C_i . B_j) exp(cs_i - cs_j) dt_j x[j][p0 + k]
-        float crow[kDState];
 #pragma unroll
-        for (int n4 = 0; n4 < kDState / 4; ++n4) {
-          const float4 v = reinterpret_cast<const float4 *>(cr)[n4];
-          crow[4 * n4] = v.x; crow[4 * n4 + 1] = v.y; crow[4 * n4 + 2] = v.z; crow[4 * n4 + 3] = v.w;
-        }
-        float yd[32];
+        for (int r = 0; r < 4; ++r) {
+          const int i = 4 * ti + r;
+          const float cs_i = s_cs[i];
+          float m[4];
 #pragma unroll
-        for (int k = 0; k < 32; ++k) yd[k] = 0.f;
-        for (int j = 0; j <= i; ++j) {
-          const float4 *br = reinterpret_cast<const float4 *>(sB + j * kDState);
-          float cb = 0.f;
-#pragma unroll
-          for (int n4 = 0; n4 < kDState / 4; ++n4) {
-            const float4 bv = br[n4];
-            cb = fmaf(crow[4 * n4], bv.x, cb);
-            cb = fmaf(crow[4 * n4 + 1], bv.y, cb);
-            cb = fmaf(crow[4 * n4 + 2], bv.z, cb);
-            cb = fmaf(crow[4 * n4 + 3], bv.w, cb);
+          for (int c = 0; c < 4; ++c) {
+            const int j = 4 * tj + c;
+            m[c] = j < i ? cb[r][c] * expf(cs_i - s_cs[j]) * s_dt[j] : j == i ? fmaf(cb[r][c], s_dt[j], Dh) : 0.f;
           }
-          const float m = cb * expf(cs_i - s_cs[j]) * s_dt[j];
-          const float4 *xr = reinterpret_cast<const float4 *>(sX + j * kHeadDim + p0);
-#pragma unroll
-          for (int k4 = 0; k4 < 8; ++k4) {
-            const float4 xv = xr[k4];
-            yd[4 * k4] = fmaf(m, xv.x, yd[4 * k4]);
-            yd[4 * k4 + 1] = fmaf(m, xv.y, yd[4 * k4 + 1]);
-            yd[4 * k4 + 2] = fmaf(m, xv.z, yd[4 * k4 + 2]);
-            yd[4 * k4 + 3] = fmaf(m, xv.w, yd[4 * k4 + 3]);
-          }
-        }
-        const float ecs = expf(cs_i);
-        float *yrow = reinterpret_cast<float *>(p.y) + it.boff * p.y_sb + (int64_t)(c0 + i) * p.y_st +
-                      h * kHeadDim + p0;
-        const float *xi = sX + i * kHeadDim + p0;
-#pragma unroll
-        for (int k4 = 0; k4 < 8; ++k4) {
-          float4 o;
-          o.x = fmaf(ecs, yo[4 * k4 + 0], yd[4 * k4 + 0]) + Dh * xi[4 * k4 + 0];
-          o.y = fmaf(ecs, yo[4 * k4 + 1], yd[4 * k4 + 1]) + Dh * xi[4 * k4 + 1];
-          o.z = fmaf(ecs, yo[4 * k4 + 2], yd[4 * k4 + 2]) + Dh * xi[4 * k4 + 2];
-          o.w = fmaf(ecs, yo[4 * k4 + 3], yd[4 * k4 + 3]) + Dh * xi[4 * k4 + 3];
-          reinterpret_cast<float4 *>(yrow)[k4] = o;
+          *reinterpret_cast<float4 *>(sM + i * kPadM + 4 * tj) = make_float4(m[0], m[1], m[2], m[3]);
         }
       }
-      __syncthreads();  // the state is read above and rewritten below
+      // state -> output: yo[i][p] = C_i . H_prev[p]
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) yo[r][c] = 0.f;
+      for (int n = 0; n < kDState; n += 4) {
+        float4 a[4], b[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) a[r] = lds4(sC + (4 * ti + r) * kPadN + n);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) b[c] = lds4(sH + (4 * tj + c) * kPadN + n);
+        fma4x4(yo, a, b);
+      }
     }
-    // state update of this thread's 32 entries: H = exp(cs_last) H + sum_j w_j x_j B_j^T
+    __syncthreads();  // M complete; every read of the entering state done
+
+    if (kFull) {
+      // y[i][p] = exp(cs_i) yo[i][p] + sum_{j <= i} M[i][j] x[j][p]
+      float yd[4][4] = {};
+      for (int j0 = 0; j0 <= 4 * ti; j0 += 4) {
+        float4 m[4], xv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) m[r] = lds4(sM + (4 * ti + r) * kPadM + j0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) xv[q] = lds4(sX + (j0 + q) * kPadX + 4 * tj);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float mr[4] = {m[r].x, m[r].y, m[r].z, m[r].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            yd[r][0] = fmaf(mr[q], xv[q].x, yd[r][0]);
+            yd[r][1] = fmaf(mr[q], xv[q].y, yd[r][1]);
+            yd[r][2] = fmaf(mr[q], xv[q].z, yd[r][2]);
+            yd[r][3] = fmaf(mr[q], xv[q].w, yd[r][3]);
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 4 * ti + r;
+        if (i < nv) {
+          const float ecs = expf(s_cs[i]);
+          *reinterpret_cast<float4 *>(yg + (int64_t)(c0 + i) * p.y_st + 4 * tj) =
+              make_float4(fmaf(ecs, yo[r][0], yd[r][0]), fmaf(ecs, yo[r][1], yd[r][1]),
+                          fmaf(ecs, yo[r][2], yd[r][2]), fmaf(ecs, yo[r][3], yd[r][3]));
+        }
+      }
+    }
+    // state: H = exp(cs_last) H + sum_j w_j x_j B_j^T on this thread's tile
     {
+      float acc[4][8] = {};
+      for (int j = 0; j < nv; ++j) {
+        const float wj = s_w[j];
+        const float4 xv = lds4(sX + j * kPadX + 4 * ti);
+        const float4 b0 = lds4(sB + j * kPadN + 8 * tj), b1 = lds4(sB + j * kPadN + 8 * tj + 4);
+        const float xw[4] = {xv.x * wj, xv.y * wj, xv.z * wj, xv.w * wj};
+        const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int c = 0; c < 8; ++c) acc[r][c] = fmaf(xw[r], bb[c], acc[r][c]);
+      }
       const float dec = s_misc[0];
       logdecay += s_misc[1];
-      float acc[32];
 #pragma unroll
-      for (int k = 0; k < 32; ++k) acc[k] = 0.f;
-      for (int j = 0; j < nv; ++j) {
-        const float xw = sX[j * kHeadDim + sp] * s_w[j];
-        const float4 *br = reinterpret_cast<const float4 *>(sB + j * kDState + sn0);
+      for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int k4 = 0; k4 < 8; ++k4) {
-          const float4 bv = br[k4];
-          acc[4 * k4] = fmaf(xw, bv.x, acc[4 * k4]);
-          acc[4 * k4 + 1] = fmaf(xw, bv.y, acc[4 * k4 + 1]);
-          acc[4 * k4 + 2] = fmaf(xw, bv.z, acc[4 * k4 + 2]);
-          acc[4 * k4 + 3] = fmaf(xw, bv.w, acc[4 * k4 + 3]);
-        }
-      }
-      float *hrow = sH + sp * kDState + sn0;
-#pragma unroll
-      for (int k = 0; k < 32; ++k) hrow[k] = fmaf(dec, hrow[k], acc[k]);
+        for (int c = 0; c < 8; ++c) hs[r][c] = fmaf(dec, hs[r][c], acc[r][c]);
     }
-    __syncthreads();
+    __syncthreads();  // every read of this sub-chunk's LDS operands done
+    if (kFull) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        *reinterpret_cast<float4 *>(sH + (4 * ti + r) * kPadN + 8 * tj) = make_float4(hs[r][0], hs[r][1], hs[r][2], hs[r][3]);
+        *reinterpret_cast<float4 *>(sH + (4 * ti + r) * kPadN + 8 * tj + 4) = make_float4(hs[r][4], hs[r][5], hs[r][6], hs[r][7]);
+      }
+    }
   }
 
   float *dst = nullptr;
@@ -258,8 +287,11 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_f32_kernel(ScanParams 
     if (tid == 0) ws_f32(plan, ws, plan.ws_decay_off)[(int64_t)item * p.H + h] = logdecay;
   }
   if (dst) {
-    __syncthreads();
-    for (int k = 0; k < 32; ++k) dst[sp * kDState + sn0 + k] = sH[sp * kDState + sn0 + k];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      *reinterpret_cast<float4 *>(dst + (4 * ti + r) * kDState + 8 * tj) = make_float4(hs[r][0], hs[r][1], hs[r][2], hs[r][3]);
+      *reinterpret_cast<float4 *>(dst + (4 * ti + r) * kDState + 8 * tj + 4) = make_float4(hs[r][4], hs[r][5], hs[r][6], hs[r][7]);
+    }
   }
 }
 
@@ -350,20 +382,38 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(ScanParams p, ScanPla
                               : nullptr;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) e[i] = init ? init[i * kThreads + threadIdx.x] : make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int k = 1; k < nseg; ++k) {
+  // segment k - 1's local state and decay are loaded one step ahead, before
+  // segment k's entry state is stored: the stores may not be reordered with
+  // later loads of the same workspace, so in-order code would wait for every
+  // load in turn
+  const int last = min(nseg, plan.items - off);  // entries 1 .. last-1 are written
+  auto load = [&](int k, float4 (&l)[kPer], float &d) {
     const int prev = off + k - 1;
-    if (off + k >= plan.items) break;
-    const float d = __expf(ldec[(int64_t)prev * p.H + h]);
+    d = __expf(ldec[(int64_t)prev * p.H + h]);
     const float4 *lp = reinterpret_cast<const float4 *>(local + ((int64_t)prev * p.H + h) * kPN);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) l[i] = lp[i * kThreads + threadIdx.x];
+  };
+  float4 l[kPer];
+  float d = 0.f;
+  if (1 < last) load(1, l, d);
+  for (int k = 1; k < last; ++k) {
+    float4 ln[kPer];
+    float dn = 0.f;
+    if (k + 1 < last) load(k + 1, ln, dn);
     float4 *ep = reinterpret_cast<float4 *>(entry + ((int64_t)(off + k) * p.H + h) * kPN);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const float4 l = lp[i * kThreads + threadIdx.x];
-      e[i].x = fmaf(d, e[i].x, l.x);
-      e[i].y = fmaf(d, e[i].y, l.y);
-      e[i].z = fmaf(d, e[i].z, l.z);
-      e[i].w = fmaf(d, e[i].w, l.w);
+      e[i].x = fmaf(d, e[i].x, l[i].x);
+      e[i].y = fmaf(d, e[i].y, l[i].y);
+      e[i].z = fmaf(d, e[i].z, l[i].z);
+      e[i].w = fmaf(d, e[i].w, l[i].w);
       ep[i * kThreads + threadIdx.x] = e[i];
+    }
+    if (k + 1 < last) {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) l[i] = ln[i];
+      d = dn;
     }
   }
 }
