@@ -57,6 +57,25 @@ def test_layer_small(w, seg):
     assert ey <= TOL[w.bf16] and ef <= TOL[w.bf16]
 
 
+def test_strong_decay():
+    """Heads whose 32-token blocks decay by more than e^64 next to heads with
+    mild decay, and a head with A = -1e4 that drives every off-diagonal term
+    to zero: the mask tiles' exponents span the whole fp32 range."""
+    w = W("bf16_strong_decay_b2_l300_h8_g2_init", 2, 300, 8, 2, init=0.3)
+    d = inputs.make_scan_inputs(w, seed=21)
+    d["A"] = (d["A"] * np.array([1, 40, 1, 80, 5, 200, 1, 1], np.float32)).astype(np.float32)
+    d["A"][6] = np.float32(-1e4)
+    dt = np.logaddexp(0.0, d["dt"].astype(np.float64) + d["dt_bias"][None, None, :])
+    blocks = np.add.reduceat(-(dt[:, :288] * d["A"]), np.arange(0, 288, 32), axis=1)
+    print(f"max 32-block log-decay per head: {blocks.max(axis=(0, 1)).round(1)}", flush=True)
+    assert (blocks.max(axis=(0, 1)) > 64).sum() >= 3 and (blocks.max(axis=(0, 1)) < 64).sum() >= 3
+    y, fs = gpu_layer(d, w)
+    ry, rf = oracle_layer(d, w)
+    ey, ef = rel(to_np(y), ry), rel(to_np(fs), rf)
+    print(f"  y rel err {ey:.3e}  final-state rel err {ef:.3e}")
+    assert ey <= TOL[True] and ef <= TOL[True]
+
+
 def test_empty_sequence_keeps_initial_state():
     w = W("bf16_l0", 2, 0, 8, 2, init=0.3)
     d = inputs.make_scan_inputs(w, seed=3)
