@@ -24,10 +24,11 @@
 // v_mfma_f32_32x32x16_bf16.
 //
 // Memory path, MI355X-specific:
-//   * x and B arrive by global->LDS direct loads (global_load_lds_dwordx4),
-//     double-buffered one chunk ahead, into token-major tiles whose 16-byte
-//     blocks are XOR-swizzled per row; no VGPR staging and no transposing
-//     copies.
+//   * x and B arrive by global->LDS direct loads (global_load_lds_dwordx4)
+//     into token-major tiles whose 16-byte blocks are XOR-swizzled per row;
+//     no VGPR staging and no transposing copies.  Each tile is reloaded as
+//     soon as its last reader is done: B (read only in the k-loop) by the
+//     last wave out of the k-loop, x after barrier A.
 //   * operands whose contraction runs over tokens (B^T and x^T) are read
 //     straight from those token-major tiles with the LDS transpose read
 //     ds_read_b64_tr_b16: in each 16-lane group, lane s points at row
@@ -37,6 +38,8 @@
 //     accumulators, bf16 in LDS as the operand of the state->output product.
 //   * C goes global -> registers (each wave its own 32 rows) right after the
 //     k-loop that last reads the current ones.
+//   * y is staged through an LDS tile of its own, so every store writes whole
+//     128-byte rows while the next x tile is landing.
 #include <type_traits>
 
 #include "scan_items.h"
@@ -443,10 +446,11 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
     __syncthreads();
   }
 
-  // Per chunk: k-loop and intra-chunk product (every read of the tiles, H and
-  // cs/dt/w/v), barrier A, the next chunk's loads and dt and this chunk's state
-  // into the same buffers, barrier B, then the y stores.  The other workgroup
-  // on the CU runs while this one waits.
+  // Per chunk: k-loop (the last wave out of it loads the next B tile at the
+  // end of its intra-chunk phase), intra-chunk product, barrier A (LDS only),
+  // then the next x tile's loads, this chunk's state into H, y through the
+  // staging tile, the next chunk's dt, and barrier B once every direct load
+  // has landed.  The other workgroup on the CU runs while this one waits.
   // operand offsets once per segment (a few registers); the rest of the lane
   // geometry is re-derived in every chunk from an opaque lane id
   LaneGeo<NCB> LG;
