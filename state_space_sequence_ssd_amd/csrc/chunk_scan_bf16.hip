@@ -575,6 +575,18 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
       // then y^T[p][i] += sum_j x[j][p] M[j][i]
 #pragma unroll
       for (int jb = 0; jb < NCB; ++jb) {
+        // x^T (row p, k = j) in the accumulator's permuted K order: slots 0..3
+        // are rows 16s + 4hh + 0..3, slots 4..7 rows 16s + 8 + 4hh + 0..3.
+        // Read first, so that building this tile's mask hides the LDS latency.
+        bf16x8 xf[2][2];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const uint32_t o = LG.oYd[q] + 128 * (32 * jb + 16 * s2);
+            xf[s2][q] = trd(sm.X, o, o + 1024);
+          }
+        __builtin_amdgcn_sched_barrier(0);
         bf16x8 Mb[2];
         if (jb < W) {
           // all j < i: exp(cs_i - cs_j) = exp(cs_i - cs_r) exp(cs_r - cs_j) with r
@@ -606,15 +618,10 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
             }
           }
         }
-        // x^T (row p, k = j) in the accumulator's permuted K order: slots 0..3
-        // are rows 16s + 4hh + 0..3, slots 4..7 rows 16s + 8 + 4hh + 0..3
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const uint32_t o = LG.oYd[q] + 128 * (32 * jb + 16 * s2);
-            yo[q] = mfma32(trd(sm.X, o, o + 1024), Mb[s2], yo[q]);
-          }
+          for (int q = 0; q < 2; ++q) yo[q] = mfma32(xf[s2][q], Mb[s2], yo[q]);
       }
     }
     if (b_loader) issue_b(L.lane, c1, nvn, 0, std::integral_constant<int, 32>{});
