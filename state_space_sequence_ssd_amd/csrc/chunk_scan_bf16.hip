@@ -586,15 +586,31 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
             const uint32_t o = LG.oYd[q] + 128 * (32 * jb + 16 * s2);
             xf[s2][q] = trd(sm.X, o, o + 1024);
           }
+        // ... and so are the per-token factors of the mask: v_j and cs at the
+        // block end off the diagonal, cs_j and dt_j on it
+        f32x4 fa[4], fb[4];
+        float cs_r = 0.f;
+        if (jb < W) {
+          cs_r = sm.cs[32 * jb + 31];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) fa[q] = lds_ld<f32x4>((const lds_u8 *)&sm.v[32 * jb + 8 * q + 4 * L.hh]);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int jq = 32 * jb + 8 * q + 4 * L.hh;
+            fa[q] = lds_ld<f32x4>((const lds_u8 *)&sm.cs[jq]);
+            fb[q] = lds_ld<f32x4>((const lds_u8 *)&sm.dt[jq]);
+          }
+        }
         __builtin_amdgcn_sched_barrier(0);
         bf16x8 Mb[2];
         if (jb < W) {
           // all j < i: exp(cs_i - cs_j) = exp(cs_i - cs_r) exp(cs_r - cs_j) with r
           // the last row of block jb; both exponents are <= 0
-          const float u = __expf(cs_i - sm.cs[32 * jb + 31]);
+          const float u = __expf(cs_i - cs_r);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const f32x4 vj = lds_ld<f32x4>((const lds_u8 *)&sm.v[32 * jb + 8 * q + 4 * L.hh]);
+            const f32x4 vj = fa[q];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
               const int r = 4 * q + t;
@@ -606,8 +622,7 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int jq = 32 * jb + 8 * q + 4 * L.hh;
-            const f32x4 cj = lds_ld<f32x4>((const lds_u8 *)&sm.cs[jq]);
-            const f32x4 dj = lds_ld<f32x4>((const lds_u8 *)&sm.dt[jq]);
+            const f32x4 cj = fa[q], dj = fb[q];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
               const int r = 4 * q + t;
