@@ -481,6 +481,7 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
 
     const float dec = sm.misc[0];
     logdecay += sm.misc[1];
+    const float cs_i = kFull ? sm.cs[ci] : 0.f;  // read now, used after the k-loop
 #pragma unroll
     for (int t = 0; t < NS; ++t)
 #pragma unroll
@@ -553,19 +554,15 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
     // LDS read: a read behind a direct load waits for it), ahead of barrier
     // A, so that only the x tile is left to load after the barrier.  (The
     // counter is zeroed with the per-token arrays of every chunk.)
-    bool b_loader = false;
-    if (has_next) {
-      uint32_t done = 0;
-      if (L.lane == 0)
-        done = __hip_atomic_fetch_add(reinterpret_cast<SSD_LDS uint32_t *>(sm.misc + 2), 1u, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_WORKGROUP);
-      b_loader = __builtin_amdgcn_readfirstlane(done) == 3;
-    }
+    // (the count is only looked at after the intra-chunk phase)
+    uint32_t done = 0;
+    if (has_next && L.lane == 0)
+      done = __hip_atomic_fetch_add(reinterpret_cast<SSD_LDS uint32_t *>(sm.misc + 2), 1u, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_WORKGROUP);
 
     if (kFull) {
       // y = exp(cs_i) (C H_prev^T) + M x: scale the state->output part, then the
       // intra-chunk product accumulates on top of it
-      const float cs_i = sm.cs[ci];
       const float ecs = __expf(cs_i);
 #pragma unroll
       for (int q = 0; q < 2; ++q)
@@ -639,7 +636,8 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
           for (int q = 0; q < 2; ++q) yo[q] = mfma32(xf[s2][q], Mb[s2], yo[q]);
       }
     }
-    if (b_loader) issue_b(L.lane, c1, nvn, 0, std::integral_constant<int, 32>{});
+    if (has_next && __builtin_amdgcn_readfirstlane(done) == 3)
+      issue_b(L.lane, c1, nvn, 0, std::integral_constant<int, 32>{});
     // A: every read of this chunk's tiles, H and cs/dt/w/v is done.  LDS only:
     // the next B tile may still be landing (nothing reads it before barrier B).
     lds_barrier();
