@@ -391,11 +391,11 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
 #pragma unroll
     for (int s = 0; s < 8; ++s) cf[s] = *reinterpret_cast<const u32x4 *>(cc + o + 32 * s);
   };
-  auto load_dt_raw = [&](int ln, int c0, int nv) -> uint32_t {
+  // raw dt of tokens 2 lane, 2 lane + 1 (two bf16, packed by the caller)
+  auto load_dt_raw = [&](int ln, int c0, int nv, uint32_t &lo, uint32_t &hi) {
     const char *dc = reinterpret_cast<const char *>(dtg + (int64_t)c0 * p.dt_st);
-    const uint32_t lo = *reinterpret_cast<const bf16_t *>(dc + (uint32_t)min(2 * ln, nv - 1) * dst * 2);
-    const uint32_t hi = *reinterpret_cast<const bf16_t *>(dc + (uint32_t)min(2 * ln + 1, nv - 1) * dst * 2);
-    return lo | (hi << 16);
+    lo = *reinterpret_cast<const bf16_t *>(dc + (uint32_t)min(2 * ln, nv - 1) * dst * 2);
+    hi = *reinterpret_cast<const bf16_t *>(dc + (uint32_t)min(2 * ln + 1, nv - 1) * dst * 2);
   };
 
   // state tiles H^T (rows n = 32 nb + 8q + 4hh + 0..3, col p = 32 pb + l32)
@@ -438,8 +438,11 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
     const int ln = threadIdx.x & 63;
     const int nv0 = min(kChunk, ntok);
     if (kFull) load_c(ln, it.tok0, nv0);
-    if (W == kDtWave)
-      chunk_dt_wave(load_dt_raw(ln, it.tok0, nv0), nv0, bias, Ah).store(sm.cs, sm.dt, sm.w, sm.v, sm.misc);
+    if (W == kDtWave) {
+      uint32_t lo, hi;
+      load_dt_raw(ln, it.tok0, nv0, lo, hi);
+      chunk_dt_wave(lo | (hi << 16), nv0, bias, Ah).store(sm.cs, sm.dt, sm.w, sm.v, sm.misc);
+    }
     if (kFull) write_state_lds(ln);
     issue_tiles(ln, it.tok0, nv0);  // last, for the same reason as in the loop
     __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
@@ -476,8 +479,10 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
     const bool has_next = c1 < it.tok1;
     const int cn = has_next ? c1 : c0;
     const int nvn = has_next ? min(kChunk, it.tok1 - c1) : nv;
-    uint32_t raw_next = 0;
-    if (W == kDtWave) raw_next = load_dt_raw(L.lane, cn, nvn);
+    // the next chunk's raw dt: loaded now, packed (and so waited for) only
+    // after the k-loop
+    uint32_t raw_lo = 0, raw_hi = 0;
+    if (W == kDtWave) load_dt_raw(L.lane, cn, nvn, raw_lo, raw_hi);
 
     const float dec = sm.misc[0];
     logdecay += sm.misc[1];
@@ -546,7 +551,11 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
     __builtin_amdgcn_s_setprio(0);
     // raw_next (loaded at the top of the chunk) is waited for here, before any
     // later load: a wait for it behind those would be a wait for all of them
-    if (W == kDtWave) asm volatile("" ::"v"(raw_next));
+    uint32_t raw_next = 0;
+    if (W == kDtWave) {
+      asm volatile("" : "+v"(raw_lo), "+v"(raw_hi));
+      raw_next = raw_lo | (raw_hi << 16);
+    }
     // the C fragments of this chunk are dead: fetch the next chunk's now
     if (kFull) load_c(L.lane, cn, nvn);
     // B is only read in the k-loop.  The last wave to finish it loads the
