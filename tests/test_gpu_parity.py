@@ -76,6 +76,38 @@ def test_strong_decay():
     assert ey <= TOL[True] and ef <= TOL[True]
 
 
+def test_in_proj_layout_strided_views():
+    """x, B, C and dt as views into one in-projection output per token
+    (z | x | B | C | dt | pad), batch rows padded by 3 tokens, and y written
+    into a view of a wider buffer: every token and batch stride differs from
+    its row width.  Bytes outside y's view stay untouched."""
+    w = W("bf16_inproj_views_b2_l300_h8_g2_init", 2, 300, 8, 2, init=0.3)
+    d = inputs.make_scan_inputs(w, seed=17)
+    H, G, P, N, Bt, L = w.nheads, w.ngroups, 64, 128, w.batch, w.seqlen
+    HP, GN = H * P, G * N
+    width = 2 * HP + 2 * GN + H + 8
+    buf = torch.zeros((Bt, L + 3, width), dtype=BF, device=DEV)
+    buf[:, :L, HP:2 * HP] = to_dev(d["x"], BF).reshape(Bt, L, HP)
+    buf[:, :L, 2 * HP:2 * HP + GN] = to_dev(d["B"], BF).reshape(Bt, L, GN)
+    buf[:, :L, 2 * HP + GN:2 * HP + 2 * GN] = to_dev(d["C"], BF).reshape(Bt, L, GN)
+    buf[:, :L, 2 * HP + 2 * GN:2 * HP + 2 * GN + H] = to_dev(d["dt"], BF)
+    x = buf[:, :L, HP:2 * HP].unflatten(2, (H, P))
+    Bv = buf[:, :L, 2 * HP:2 * HP + GN].unflatten(2, (G, N))
+    Cv = buf[:, :L, 2 * HP + GN:2 * HP + 2 * GN].unflatten(2, (G, N))
+    dtv = buf[:, :L, 2 * HP + 2 * GN:2 * HP + 2 * GN + H]
+    ybuf = torch.full((Bt, L, HP + 64), 7.0, dtype=BF, device=DEV)
+    y = ybuf[..., 32:32 + HP].unflatten(2, (H, P))
+    fs = torch.empty((Bt, H, P, N), device=DEV)
+    ssd.ssd_chunk_scan_fwd(x, dtv, to_dev(d["A"]), Bv, Cv, dt_bias=to_dev(d["dt_bias"]), D=to_dev(d["D"]),
+                           initial_state=to_dev(d["initial_state"]), final_state=fs, y=y)
+    torch.cuda.synchronize()
+    ry, rf = oracle_layer(d, w)
+    ey, ef = rel(to_np(y), ry), rel(to_np(fs), rf)
+    print(f"  y rel err {ey:.3e}  final-state rel err {ef:.3e}")
+    assert ey <= TOL[True] and ef <= TOL[True]
+    assert torch.all(ybuf[..., :32] == 7.0) and torch.all(ybuf[..., 32 + HP:] == 7.0)
+
+
 def test_empty_sequence_keeps_initial_state():
     w = W("bf16_l0", 2, 0, 8, 2, init=0.3)
     d = inputs.make_scan_inputs(w, seed=3)
