@@ -226,6 +226,30 @@ def test_decode_small(bf16, conv):
         assert np.array_equal(to_np(cs), rc)
 
 
+def test_decode_strided_rows():
+    """Decode with the token (x|B|C) and dt as views into one wider row per
+    batch entry, and y written into a wider buffer (batch strides > widths)."""
+    w = inputs.DecodeWorkload("dec_views", 5, 16, 4, 1)
+    d = inputs.make_decode_small_inputs(w, seed=23, layer=0)
+    st = inputs.decode_state_host(w, 23, 0)
+    CD, H = w.conv_dim, w.nheads
+    row = torch.zeros((w.batch, 40 + CD + H + 24), dtype=BF, device=DEV)
+    row[:, 40:40 + CD] = to_dev(d["xBC"], BF)
+    row[:, 40 + CD:40 + CD + H] = to_dev(d["dt"], BF)
+    state, cs = to_dev(st), to_dev(d["conv_state"], BF)
+    ybuf = torch.full((w.batch, H * 64 + 32), 3.0, dtype=BF, device=DEV)
+    y = ybuf[:, 16:16 + H * 64].unflatten(1, (H, 64))
+    ssd.ssd_decode_step(row[:, 40:40 + CD], row[:, 40 + CD:40 + CD + H], to_dev(d["A"]), state, H, w.ngroups,
+                        dt_bias=to_dev(d["dt_bias"]), D=to_dev(d["D"]), conv_state=cs,
+                        conv_weight=to_dev(d["conv_w"]), y=y)
+    torch.cuda.synchronize()
+    ry, rs, rc = oracle.decode_step(d["xBC"], d["dt"], d["dt_bias"], d["A"], d["D"], st, H, 64, 128,
+                                    w.ngroups, conv_w=d["conv_w"], conv_state=d["conv_state"])
+    assert rel(to_np(y), ry) <= TOL[True] and rel(to_np(state), rs) <= TOL[True]
+    assert np.array_equal(to_np(cs), rc)
+    assert torch.all(ybuf[:, :16] == 3.0) and torch.all(ybuf[:, 16 + H * 64:] == 3.0)
+
+
 def test_prefill_then_decode_chain():
     """GPU prefill of L tokens (conv state + final state out) then GPU decode of
     token L == oracle prefill of L+1 tokens."""
