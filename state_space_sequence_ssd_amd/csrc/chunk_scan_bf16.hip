@@ -36,8 +36,9 @@
 //     k0..k0+3 of column c0 + i -- four K values of its MFMA column.
 //   * the running state stays on chip: fp32 in the owning waves' MFMA
 //     accumulators, bf16 in LDS as the operand of the state->output product.
-//   * C goes global -> registers (each wave its own 32 rows) right after the
-//     k-loop that last reads the current ones.
+//   * C goes global -> registers (each wave its own 32 rows), one fragment of
+//     the next chunk per k-step, right after the step that used the current
+//     one.
 //   * y is staged through an LDS tile of its own, so every store writes whole
 //     128-byte rows while the next x tile is landing.
 #include <type_traits>
@@ -533,6 +534,12 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
         for (int q = 0; q < 2; ++q) yo[q] = mfma32(f[k++], cb, yo[q]);
       }
     };
+    // The next chunk's C fragments are loaded one per k-step, into the one the
+    // step has just used.  A fragment load touches 32 cache lines (one per
+    // row); eight of them from each wave in one burst after the k-loop would
+    // hold up the direct loads queued behind them.
+    const char *ccn = reinterpret_cast<const char *>(Cg + (int64_t)cn * p.C_st);
+    const uint32_t ocn = (uint32_t)min(ci, nvn - 1) * cst * 2 + 16 * L.hh;
     {
       bf16x8 fr[2][NF > 0 ? NF : 1];
       f32x4 wr[2][2];
@@ -545,6 +552,7 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
         if (s < 7) load_frags(s + 1, fr[(s + 1) & 1], wr[(s + 1) & 1]);
         __builtin_amdgcn_sched_barrier(0);
         mfma_step(s, fr[s & 1], wr[s & 1]);
+        if (kFull) cf[s] = *reinterpret_cast<const u32x4 *>(ccn + ocn + 32 * s);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -556,8 +564,6 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
       asm volatile("" : "+v"(raw_lo), "+v"(raw_hi));
       raw_next = raw_lo | (raw_hi << 16);
     }
-    // the C fragments of this chunk are dead: fetch the next chunk's now
-    if (kFull) load_c(L.lane, cn, nvn);
     // B is only read in the k-loop.  The last wave to finish it loads the
     // whole next B tile at the end of its intra-chunk phase (after its last
     // LDS read: a read behind a direct load waits for it), ahead of barrier
