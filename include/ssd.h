@@ -138,12 +138,15 @@ int ssd_conv1d_silu(const ssd_conv_args *args, void *stream);
  * Precision: bf16 x/B/C/dt/y with fp32 state and accumulation (MFMA bf16
  * operands); fp32 inputs run an all-fp32 path.
  *
- * Supported: headdim 64, dstate 128, chunk_size 128, dtype F32 or BF16.
+ * Supported: headdim 64, dstate 128, chunk_size 64, 128 or 256, dtype F32
+ * or BF16.  chunk_size is the model's chunk length; the block (chunked) form
+ * of the recurrence gives the same result for any chunk length, up to
+ * rounding, so the kernels always work in 128-token tiles.
  * x, B, C, y 16-byte aligned with strides multiples of 8 elements; token
  * strides below 2^22 elements (SSD_ERR_INVALID_ARG otherwise).
  *
  * seg_chunks: 0 = automatic.  Otherwise each sequence is cut into segments
- * of seg_chunks chunks that run in parallel; the state entering each
+ * of seg_chunks 128-token tiles that run in parallel; the state entering each
  * segment is found by a short pre-pass (same result, more parallelism for
  * few long sequences).
  *

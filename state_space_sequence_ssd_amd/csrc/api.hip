@@ -72,9 +72,13 @@ int check_scan(const ssd_scan_args *a, ssd::ScanParams &p) {
   if (a->nheads % a->ngroups != 0)
     return fail(SSD_ERR_INVALID_ARG, "ssd_chunk_scan_fwd: nheads %d not a multiple of ngroups %d", a->nheads,
                 a->ngroups);
-  if (a->headdim != ssd::kHeadDim || a->dstate != ssd::kDState || a->chunk_size != ssd::kChunk)
-    return fail(SSD_ERR_UNSUPPORTED, "ssd_chunk_scan_fwd: built for headdim 64, dstate 128, chunk 128 (got %d, %d, %d)",
-                a->headdim, a->dstate, a->chunk_size);
+  // the model's chunk length does not change the result (the chunked form is
+  // exact for any block length); the kernels always work in 128-token tiles
+  if (a->headdim != ssd::kHeadDim || a->dstate != ssd::kDState ||
+      (a->chunk_size != 64 && a->chunk_size != 128 && a->chunk_size != 256))
+    return fail(SSD_ERR_UNSUPPORTED,
+                "ssd_chunk_scan_fwd: built for headdim 64, dstate 128, chunk 64/128/256 (got %d, %d, %d)", a->headdim,
+                a->dstate, a->chunk_size);
   if (a->seg_chunks < 0) return fail(SSD_ERR_INVALID_ARG, "ssd_chunk_scan_fwd: seg_chunks < 0");
   if (!a->A) return fail(SSD_ERR_INVALID_ARG, "ssd_chunk_scan_fwd: A is NULL");
   if (a->seqlen > 0 && (!a->x || !a->B || !a->C || !a->dt || !a->y))

@@ -40,7 +40,7 @@ def split_xbc(v, H, G, P=64, N=128):
             v[..., H * P + G * N:].reshape(b, L, G, N))
 
 
-def gpu_layer(d, w, seg_chunks=0, final=True):
+def gpu_layer(d, w, seg_chunks=0, final=True, chunk_size=128):
     """conv (if the workload has it) + chunk scan on the GPU.  Returns (y, final_state)."""
     H, G = w.nheads, w.ngroups
     dt_t = BF if w.bf16 else torch.float32
@@ -58,7 +58,8 @@ def gpu_layer(d, w, seg_chunks=0, final=True):
     y = ssd.ssd_chunk_scan_fwd(x, to_dev(d["dt"], dt_t), to_dev(d["A"]), B, C,
                                dt_bias=to_dev(d["dt_bias"]), D=to_dev(d["D"]), seq_idx=seq_idx,
                                num_seqs=rows if seq_idx is not None else None,
-                               initial_state=init, final_state=fs, seg_chunks=seg_chunks)
+                               initial_state=init, final_state=fs, seg_chunks=seg_chunks,
+                               chunk_size=chunk_size)
     torch.cuda.synchronize()
     return y, fs
 

@@ -78,7 +78,7 @@ def scan_rc(a, ws=None, ws_bytes=1 << 40):
 
 @pytest.mark.parametrize("field,value,code", [
     ("struct_size", 8, 1), ("dtype", 7, 2), ("batch", 0, 1), ("nheads", 0, 1), ("ngroups", 3, 1),
-    ("headdim", 32, 2), ("dstate", 64, 2), ("chunk_size", 64, 2), ("seg_chunks", -1, 1),
+    ("headdim", 32, 2), ("dstate", 64, 2), ("chunk_size", 32, 2), ("chunk_size", 100, 2), ("seg_chunks", -1, 1),
     ("A", None, 1), ("x", None, 1), ("y", None, 1), ("dt", None, 1),
     ("x", FAKE + 2, 4), ("B_stride_token", 2048 + 2, 4), ("x_stride_token", 1024, 1),
     ("C_stride_token", 1 << 22, 1), ("dt_stride_token", 1 << 22, 1),
@@ -87,6 +87,13 @@ def test_scan_argument_errors(field, value, code):
     a = scan_args(**{field: value})
     assert scan_rc(a) == code
     assert ssd.load_library().ssd_last_error().decode()
+
+
+@pytest.mark.parametrize("q", [64, 128, 256])
+def test_scan_accepts_model_chunk_sizes(q):
+    """The model's chunk length is 64, 128 or 256; the result does not depend on it."""
+    lib = ssd.load_library()
+    assert lib.ssd_chunk_scan_workspace_size(ctypes.byref(scan_args(chunk_size=q))) == 0
 
 
 def test_scan_seq_idx_rules():

@@ -57,6 +57,23 @@ def test_layer_small(w, seg):
     assert ey <= TOL[w.bf16] and ef <= TOL[w.bf16]
 
 
+@pytest.mark.parametrize("q", [64, 256])
+def test_model_chunk_sizes(q):
+    """chunk_size 64 or 256 (the model's chunk length) gives the oracle's
+    result: the chunked form is exact for any block length, and the kernels
+    always tile by 128, so the output equals the chunk-128 run bit for bit."""
+    w = W("bf16_conv_b2_l300_h16_g4_init", 2, 300, 16, 4, conv=True, init=0.3)
+    print(f"case {w.name} chunk_size={q}", flush=True)
+    d = inputs.make_scan_inputs(w, seed=11)
+    y, fs = gpu_layer(d, w, chunk_size=q)
+    y128, fs128 = gpu_layer(d, w)
+    ry, rf = oracle_layer(d, w)
+    ey, ef = rel(to_np(y), ry), rel(to_np(fs), rf)
+    print(f"  y rel err {ey:.3e}  final-state rel err {ef:.3e}")
+    assert ey <= TOL[True] and ef <= TOL[True]
+    assert torch.equal(y, y128) and torch.equal(fs, fs128)
+
+
 def test_strong_decay():
     """Heads whose 32-token blocks decay by more than e^64 next to heads with
     mild decay, and a head with A = -1e4 that drives every off-diagonal term
