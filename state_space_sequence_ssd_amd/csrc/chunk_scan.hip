@@ -360,9 +360,18 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t *seq_i
 // ---------------------------------------------------------------------------
 // segment combine: entry state of segment k = decay_{k-1} entry_{k-1} + local_{k-1}
 // ---------------------------------------------------------------------------
+// The map is elementwise over the state, so each (row, head) is split over
+// kCombSplit workgroups with one float4 of the state per thread, and the local
+// states of kCombBatch segments are all in flight before their chain runs:
+// the kernel then costs a few memory round trips instead of one per segment.
+constexpr int kCombSplit = 8;
+constexpr int kCombBatch = 8;
+static_assert(kPN / 4 == kCombSplit * kThreads, "one float4 of the state per thread");
+
 __global__ __launch_bounds__(kThreads) void combine_kernel(ScanParams p, ScanPlan plan, char *ws) {
-  const int row = blockIdx.x / p.H;
-  const int h = blockIdx.x % p.H;
+  const int part = blockIdx.x % kCombSplit;
+  const int row = blockIdx.x / kCombSplit / p.H;
+  const int h = blockIdx.x / kCombSplit % p.H;
   int nseg, off;
   if (plan.packed) {
     const PlanView v = plan_view(plan, ws);
@@ -373,47 +382,33 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(ScanParams p, ScanPla
     off = row * plan.nseg;
   }
   if (nseg <= 1) return;
-  const float *local = ws_f32(plan, ws, plan.ws_local_off);
-  const float *ldec = ws_f32(plan, ws, plan.ws_decay_off);
-  float *entry = ws_f32(plan, ws, plan.ws_entry_off);
-  constexpr int kPer = kPN / 4 / kThreads;  // float4 per thread (8)
-  float4 e[kPer];
-  const float4 *init = p.init ? reinterpret_cast<const float4 *>(p.init + ((int64_t)row * p.H + h) * kPN)
-                              : nullptr;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) e[i] = init ? init[i * kThreads + threadIdx.x] : make_float4(0.f, 0.f, 0.f, 0.f);
-  // segment k - 1's local state and decay are loaded one step ahead, before
-  // segment k's entry state is stored: the stores may not be reordered with
-  // later loads of the same workspace, so in-order code would wait for every
-  // load in turn
+  const float *__restrict__ local = ws_f32(plan, ws, plan.ws_local_off);
+  const float *__restrict__ ldec = ws_f32(plan, ws, plan.ws_decay_off);
+  float *__restrict__ entry = ws_f32(plan, ws, plan.ws_entry_off);
+  const int idx = part * kThreads + threadIdx.x;  // float4 of the head's state
+  float4 e = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (p.init) e = reinterpret_cast<const float4 *>(p.init + ((int64_t)row * p.H + h) * kPN)[idx];
   const int last = min(nseg, plan.items - off);  // entries 1 .. last-1 are written
-  auto load = [&](int k, float4 (&l)[kPer], float &d) {
-    const int prev = off + k - 1;
-    d = __expf(ldec[(int64_t)prev * p.H + h]);
-    const float4 *lp = reinterpret_cast<const float4 *>(local + ((int64_t)prev * p.H + h) * kPN);
+  for (int k0 = 1; k0 < last; k0 += kCombBatch) {
+    float4 l[kCombBatch];
+    float d[kCombBatch];
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) l[i] = lp[i * kThreads + threadIdx.x];
-  };
-  float4 l[kPer];
-  float d = 0.f;
-  if (1 < last) load(1, l, d);
-  for (int k = 1; k < last; ++k) {
-    float4 ln[kPer];
-    float dn = 0.f;
-    if (k + 1 < last) load(k + 1, ln, dn);
-    float4 *ep = reinterpret_cast<float4 *>(entry + ((int64_t)(off + k) * p.H + h) * kPN);
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      e[i].x = fmaf(d, e[i].x, l[i].x);
-      e[i].y = fmaf(d, e[i].y, l[i].y);
-      e[i].z = fmaf(d, e[i].z, l[i].z);
-      e[i].w = fmaf(d, e[i].w, l[i].w);
-      ep[i * kThreads + threadIdx.x] = e[i];
+    for (int j = 0; j < kCombBatch; ++j) {
+      const int prev = off + k0 + j - 1;
+      if (k0 + j < last) {
+        d[j] = __expf(ldec[(int64_t)prev * p.H + h]);
+        l[j] = reinterpret_cast<const float4 *>(local + ((int64_t)prev * p.H + h) * kPN)[idx];
+      }
     }
-    if (k + 1 < last) {
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) l[i] = ln[i];
-      d = dn;
+    for (int j = 0; j < kCombBatch; ++j) {
+      if (k0 + j < last) {
+        e.x = fmaf(d[j], e.x, l[j].x);
+        e.y = fmaf(d[j], e.y, l[j].y);
+        e.z = fmaf(d[j], e.z, l[j].z);
+        e.w = fmaf(d[j], e.w, l[j].w);
+        reinterpret_cast<float4 *>(entry + ((int64_t)(off + k0 + j) * p.H + h) * kPN)[idx] = e;
+      }
     }
   }
 }
@@ -485,7 +480,7 @@ hipError_t launch_chunk_scan(const ScanParams &p, const ScanPlan &plan, void *wo
       e = hipGetLastError();
     }
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(combine_kernel, dim3(plan.rows * p.H), dim3(kThreads), 0, stream, p, plan, ws);
+    hipLaunchKernelGGL(combine_kernel, dim3(plan.rows * p.H * kCombSplit), dim3(kThreads), 0, stream, p, plan, ws);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
