@@ -206,7 +206,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1",
+        print("bench.py: one GPU only (there is no multi-GPU path); use --gpus 1",
               file=sys.stderr)
         sys.exit(2)
 

@@ -76,3 +76,15 @@ def test_scan_flops_nemotron_h_8b():
     per_chunk = 2 * (Q * (Q + 1) // 2) * (G * N + H * P) + Q * 2 * (2 * H * P * N)
     assert bench.scan_flops(w) == T // Q * per_chunk
     assert abs(bench.scan_flops(w) / 1e9 - 88.2) < 0.05
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """Everything here runs on one GPU: --gpus N > 1 stops before touching a device."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr + r.stdout
