@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_f32_kernel(ScanParams 
   __shared__ float s_misc[2];
 
   int item, h, g;
-  if (!map_workgroup(p, plan, item, h, g)) return;
+  if (!map_workgroup(p, plan, ws, item, h, g)) return;
   Item it;
   if (!get_item(p, plan, ws, item, it)) return;
   if (!kFull && it.last) return;
@@ -308,6 +308,7 @@ __device__ __forceinline__ int lower_bound_seq(const int32_t *seq_idx, int L, in
 }
 
 constexpr int kPlanThreads = 1024;
+constexpr int kPlanSortMax = 4096;  // longer work lists are not reordered
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t *seq_idx, int L,
                                                             ScanPlan plan, char *ws) {
@@ -355,6 +356,33 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t *seq_i
     __syncthreads();
   }
   if (threadIdx.x == 0) *n_items = min(carry, plan.items);
+  __syncthreads();
+  // Items ranked longest first (ties in list order), the order in which the
+  // scan kernels start them.  The rank count is quadratic, so very long work
+  // lists keep their list order.
+  int *item_order = n_items + 1;
+  const int n = min(carry, plan.items);
+  __shared__ int nchunks[kPlanSortMax];
+  const bool sort = n <= kPlanSortMax;
+  if (sort) {
+    for (int i = threadIdx.x; i < n; i += kPlanThreads) {
+      const int s = item_seq[i], t0 = seq_start[s] + item_k[i] * plan.seg_len;
+      nchunks[i] = (min(seq_end[s], t0 + plan.seg_len) - t0 + kChunk - 1) / kChunk;
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += kPlanThreads) {
+    int rank = i;
+    if (sort) {
+      const int ci = nchunks[i];
+      rank = 0;
+      for (int j = 0; j < n; ++j) {
+        const int cj = nchunks[j];
+        rank += cj > ci || (cj == ci && j < i);
+      }
+    }
+    item_order[rank] = i;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -445,7 +473,7 @@ ScanPlan make_scan_plan(const ScanParams &p, int seg_chunks) {
   }
   size_t off = 0;
   plan.ws_plan_off = off;
-  if (plan.packed) off = align256(off + sizeof(int) * (4 * (size_t)plan.rows + 2 * (size_t)plan.items + 1));
+  if (plan.packed) off = align256(off + sizeof(int) * (4 * (size_t)plan.rows + 3 * (size_t)plan.items + 1));
   plan.ws_local_off = plan.ws_entry_off = plan.ws_decay_off = off;
   if (plan.segmented) {
     const size_t st = sizeof(float) * (size_t)plan.items * p.H * kPN;
@@ -468,8 +496,7 @@ hipError_t launch_chunk_scan(const ScanParams &p, const ScanPlan &plan, void *wo
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const long long total = (long long)plan.items * p.H;
-  const unsigned nblk = (unsigned)((total + kNumXCD - 1) / kNumXCD * kNumXCD);
+  const unsigned nblk = scan_grid_size(p, plan);
   if (nblk == 0) return hipSuccess;
   if (plan.segmented) {
     hipError_t e;

@@ -719,7 +719,7 @@ __global__ __launch_bounds__(kThr, 2) void chunk_scan_bf16_kernel(ScanParams p, 
   const Lds sm{(lds_u8 *)smem.B, (lds_u8 *)smem.X, (lds_u8 *)smem.H, (lds_u8 *)smem.Y,
                small, small + kChunk, small + 2 * kChunk, small + 3 * kChunk, small + 4 * kChunk};
   int item, h, g;
-  if (!map_workgroup(p, plan, item, h, g)) return;
+  if (!map_workgroup(p, plan, ws, item, h, g)) return;
   Item it;
   if (!get_item(p, plan, ws, item, it)) return;
   if (!kFull && it.last) return;  // the pre-pass only needs segments that have a successor

@@ -17,7 +17,7 @@ struct Item {
 };
 
 struct PlanView {
-  const int *seq_start, *seq_end, *seq_nseg, *seq_off, *item_seq, *item_k, *n_items;
+  const int *seq_start, *seq_end, *seq_nseg, *seq_off, *item_seq, *item_k, *n_items, *item_order;
 };
 
 __device__ __forceinline__ PlanView plan_view(const ScanPlan &plan, const char *ws) {
@@ -30,6 +30,7 @@ __device__ __forceinline__ PlanView plan_view(const ScanPlan &plan, const char *
   v.item_seq = b + 4 * plan.rows;
   v.item_k = v.item_seq + plan.items;
   v.n_items = v.item_k + plan.items;
+  v.item_order = v.n_items + 1;
   return v;
 }
 
@@ -59,21 +60,50 @@ __device__ __forceinline__ bool get_item(const ScanParams &p, const ScanPlan &pl
   return true;
 }
 
-// blockIdx -> (item, head): XCD x gets a contiguous range of the work list,
-// ordered item-major, then group, then head.
-__device__ __forceinline__ bool map_workgroup(const ScanParams &p, const ScanPlan &plan, int &item,
-                                              int &h, int &g) {
+// blockIdx -> (item, head).  Workgroups go to the XCDs round-robin by
+// blockIdx, and each XCD starts its workgroups in blockIdx order.
+//  * Batch mode (items of equal length): XCD x gets a contiguous range of the
+//    work list, ordered item-major, then group, then head.
+//  * Packed mode (items of any length): the (item, group) units, longest item
+//    first, are dealt round-robin over the XCDs, and each XCD runs its units'
+//    heads one unit after the other.  The long items start first and every
+//    XCD gets a share of each length, so the last workgroups to finish are
+//    short ones; a unit's heads (which read the same B and C) stay on one XCD.
+__device__ __forceinline__ bool map_workgroup(const ScanParams &p, const ScanPlan &plan, const char *ws,
+                                              int &item, int &h, int &g) {
+  const int hpg = p.H / p.G;
+  if (plan.packed) {
+    const int pos = blockIdx.x / kNumXCD;
+    const int k = (pos / hpg) * kNumXCD + blockIdx.x % kNumXCD;  // unit rank
+    const int rank = k / p.G;
+    const PlanView v = plan_view(plan, ws);
+    if (rank >= *v.n_items) return false;
+    item = v.item_order[rank];
+    g = k % p.G;
+    h = g * hpg + pos % hpg;
+    return true;
+  }
   const int total = plan.items * p.H;
   const int per_xcd = gridDim.x / kNumXCD;
   const int w = (blockIdx.x % kNumXCD) * per_xcd + blockIdx.x / kNumXCD;
   if (w >= total) return false;
-  const int hpg = p.H / p.G;
   const int hl = w % hpg;
   const int t = w / hpg;
   g = t % p.G;
   item = t / p.G;
   h = g * hpg + hl;
   return true;
+}
+
+// Workgroups a scan launch needs for this plan (a multiple of the XCD count).
+inline unsigned scan_grid_size(const ScanParams &p, const ScanPlan &plan) {
+  const long long x = kNumXCD;
+  if (plan.packed) {
+    const long long units = (long long)plan.items * p.G;
+    return (unsigned)((units + x - 1) / x * x * (p.H / p.G));
+  }
+  const long long total = (long long)plan.items * p.H;
+  return (unsigned)((total + x - 1) / x * x);
 }
 
 __device__ __forceinline__ float *ws_f32(const ScanPlan &plan, char *ws, size_t off) {
