@@ -74,6 +74,22 @@ def test_model_chunk_sizes(q):
     assert torch.equal(y, y128) and torch.equal(fs, fs128)
 
 
+def test_packed_many_short_sequences():
+    """5,000 sequences of 0-3 tokens: more work items than the plan ranks by
+    length (they keep list order), empty sequences among them, and chunks
+    holding several sequences."""
+    rng = np.random.default_rng(17)
+    lens = rng.integers(0, 4, 5000)
+    w = W("bf16_packed_5000seqs_h2_g1_init", 1, 0, 2, 1, init=0.3, lens=lens)
+    print(f"case {w.name} tokens={int(lens.sum())}", flush=True)
+    d = inputs.make_scan_inputs(w, seed=19)
+    y, fs = gpu_layer(d, w)
+    ry, rf = oracle_layer(d, w)
+    ey, ef = rel(to_np(y), ry), rel(to_np(fs), rf)
+    print(f"  y rel err {ey:.3e}  final-state rel err {ef:.3e}")
+    assert ey <= TOL[True] and ef <= TOL[True]
+
+
 def test_strong_decay():
     """Heads whose 32-token blocks decay by more than e^64 next to heads with
     mild decay, and a head with A = -1e4 that drives every off-diagonal term
