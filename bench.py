@@ -189,6 +189,23 @@ def cpu_baseline(w, d, rows):
             "seconds": el}
 
 
+def cpu_baseline_single_core(w, d):
+    """The same oracle on one host thread over one batch row, so that the
+    per-core rate sits beside the all-core one.  The oracle's recurrences are
+    an OpenMP loop; its thread count is set through the OpenMP runtime the
+    oracle library is linked against, and restored afterwards."""
+    import ctypes
+    gomp = ctypes.CDLL("libgomp.so.1")
+    n = gomp.omp_get_max_threads()
+    gomp.omp_set_num_threads(1)
+    try:
+        r = cpu_baseline(w, d, 1)
+    finally:
+        gomp.omp_set_num_threads(n)
+    r["cores"] = 1
+    return r
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -361,9 +378,10 @@ def main():
             configs[cw.name] = time_config(cw, seed, steps=10, warmup=2)
             torch.cuda.empty_cache()
 
-    cpu = None
+    cpu = cpu1 = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, d, args.cpu_rows)
+        cpu1 = cpu_baseline_single_core(w, d)
 
     line = {
         "metric": "SSD scan tokens/s/layer @Nemotron-H-8B shape; decode-step HBM GB/s",
@@ -385,6 +403,7 @@ def main():
         "wall_s_timed": round(wall, 4),
         "roofline": roofline,
         "cpu_baseline": None if cpu is None else {k: v for k, v in cpu.items() if k != "seconds"},
+        "cpu_baseline_single_core": None if cpu1 is None else {k: v for k, v in cpu1.items() if k != "seconds"},
         "kernels": kernels,
         "decode": decode,
         "configs": configs,

@@ -88,3 +88,17 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in r.stderr + r.stdout
+
+
+def test_cpu_baseline_single_core_restores_threads():
+    """The one-thread oracle timing reports cores = 1 and leaves the OpenMP
+    thread count as it found it."""
+    import ctypes
+    w = inputs.ScanWorkload("tiny_conv", 1, 256, 8, 2, bf16=True, conv=True, final_state=True)
+    d = inputs.make_scan_inputs(w, seed=3)
+    gomp = ctypes.CDLL("libgomp.so.1")
+    before = gomp.omp_get_max_threads()
+    r = bench.cpu_baseline_single_core(w, d)
+    assert gomp.omp_get_max_threads() == before
+    assert r["cores"] == 1 and r["kind"] == "oracle" and r["value"] > 0
+    assert "batch rows 0..0 of 1" in r["sample"]
