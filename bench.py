@@ -150,6 +150,12 @@ def time_config(w, seed, steps, warmup):
         step(evs[i])
     torch.cuda.synchronize()
     scan_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    # launch-inclusive: host wall clock over back-to-back calls of the whole step
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    host_ms = (time.perf_counter() - t0) * 1e3 / steps
     sb = scan_algorithmic_bytes(w)
     out = {"tokens": Bt * L, "io_dtype": "bf16" if w.bf16 else "f32",
            "scan_avg_ms": round(scan_ms, 5), "scan_algorithmic_bytes": sb,
@@ -165,6 +171,7 @@ def time_config(w, seed, steps, warmup):
                     "conv_hbm_frac": round(cb / (conv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
         step_ms += conv_ms
     out["layer_tokens_per_s"] = round(Bt * L / (step_ms * 1e-3), 1)
+    out["step_launch_inclusive_ms"] = round(host_ms, 5)
     return out
 
 
