@@ -298,6 +298,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_f32_kernel(ScanParams 
 // ---------------------------------------------------------------------------
 // packed-sequence planner: sequence bounds from seq_idx and the work list
 // ---------------------------------------------------------------------------
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanSortMax = 4096;  // longer work lists are not reordered
+
 __device__ __forceinline__ int lower_bound_seq(const int32_t *seq_idx, int L, int s) {
   int lo = 0, hi = L;
   while (lo < hi) {
@@ -307,8 +310,18 @@ __device__ __forceinline__ int lower_bound_seq(const int32_t *seq_idx, int L, in
   return lo;
 }
 
-constexpr int kPlanThreads = 1024;
-constexpr int kPlanSortMax = 4096;  // longer work lists are not reordered
+// Where every sequence id starts: one binary search per id in [0, rows], all
+// in parallel; the end of id s is the start of id s + 1, so each boundary is
+// searched for once.
+__device__ __forceinline__ void sequence_bounds(const int32_t *seq_idx, int L, int rows, int *seq_start,
+                                                int *seq_end) {
+  for (int s = threadIdx.x; s <= rows; s += kPlanThreads) {
+    const int st = lower_bound_seq(seq_idx, L, s);
+    if (s < rows) seq_start[s] = st;
+    if (s >= 1) seq_end[s - 1] = st;
+  }
+  __syncthreads();
+}
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t *seq_idx, int L,
                                                             ScanPlan plan, char *ws) {
@@ -321,13 +334,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t *seq_i
   __shared__ int scan[kPlanThreads];
   __shared__ int carry;
   if (threadIdx.x == 0) carry = 0;
-  __syncthreads();
+  sequence_bounds(seq_idx, L, plan.rows, seq_start, seq_end);
   for (int base = 0; base < plan.rows; base += kPlanThreads) {
     const int s = base + threadIdx.x;
     int nseg = 0, st = 0, en = 0;
     if (s < plan.rows) {
-      st = lower_bound_seq(seq_idx, L, s);
-      en = max(st, lower_bound_seq(seq_idx, L, s + 1));
+      st = seq_start[s];
+      en = max(st, seq_end[s]);
       nseg = max(1, (en - st + plan.seg_len - 1) / plan.seg_len);
     }
     scan[threadIdx.x] = nseg;
