@@ -156,14 +156,20 @@ __global__ __launch_bounds__(kThreads) void conv1d_silu_kernel(ConvParams p) {
   }
 }
 
-// First index in [0, L) with seq_idx[i] >= s (seq_idx non-decreasing).
-__device__ __forceinline__ int lower_bound_seq(const int32_t *seq_idx, int L, int s) {
-  int lo = 0, hi = L;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (seq_idx[mid] < s) lo = mid + 1; else hi = mid;
+// First indices in [0, L] with seq_idx[i] >= s and >= s + 1 (seq_idx
+// non-decreasing): both binary searches advance in the same loop, so their
+// dependent loads overlap.
+__device__ __forceinline__ void sequence_span(const int32_t *seq_idx, int L, int s, int &start, int &end) {
+  int lo0 = 0, hi0 = L, lo1 = 0, hi1 = L;
+  while (lo0 < hi0 || lo1 < hi1) {
+    const int m0 = (lo0 + hi0) >> 1, m1 = (lo1 + hi1) >> 1;
+    const int v0 = lo0 < hi0 ? seq_idx[m0] : 0;
+    const int v1 = lo1 < hi1 ? seq_idx[m1] : 0;
+    if (lo0 < hi0) { if (v0 < s) lo0 = m0 + 1; else hi0 = m0; }
+    if (lo1 < hi1) { if (v1 < s + 1) lo1 = m1 + 1; else hi1 = m1; }
   }
-  return lo;
+  start = lo0;
+  end = max(lo0, lo1);
 }
 
 // conv_state_out[row][r] = v(end - 3 + r) of each sequence.
@@ -178,8 +184,7 @@ __global__ __launch_bounds__(kThreads) void conv_state_out_kernel(ConvParams p, 
   int start = 0, end = p.L;
   const T *x = reinterpret_cast<const T *>(p.x) + c0;
   if (p.seq_idx) {
-    start = lower_bound_seq(p.seq_idx, p.L, s);
-    end = max(start, lower_bound_seq(p.seq_idx, p.L, s + 1));
+    sequence_span(p.seq_idx, p.L, s, start, end);
   } else {
     x += (int64_t)s * p.x_sb;
   }
