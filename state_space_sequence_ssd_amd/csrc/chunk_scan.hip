@@ -301,24 +301,47 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_f32_kernel(ScanParams 
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanSortMax = 4096;  // longer work lists are not reordered
 
-__device__ __forceinline__ int lower_bound_seq(const int32_t *seq_idx, int L, int s) {
+// First index in [0, L] with seq_idx[i] >= s, found by a group of gs lanes
+// (gs a power of two up to 64, the group aligned inside its wave, lane k of
+// it): every round the group probes gs points of [lo, hi) at once and keeps
+// the gap between the last probe below s and the first one not below, so a
+// search takes log_{gs+1} L rounds of one load each.  gs = 1 is a binary
+// search.  The result stays in [0, L] whatever seq_idx holds.
+__device__ __forceinline__ int lower_bound_group(const int32_t *seq_idx, int L, int s, int gs, int k) {
+  const int gbase = (threadIdx.x & 63) & ~(gs - 1);
+  const uint64_t gmask = (gs == 64 ? ~0ull : (1ull << gs) - 1) << gbase;
   int lo = 0, hi = L;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (seq_idx[mid] < s) lo = mid + 1; else hi = mid;
+  while (hi - lo > gs) {
+    const int n = hi - lo;
+    const int pk = lo + (int)((int64_t)(k + 1) * n / (gs + 1));
+    const int c = __popcll(__ballot(seq_idx[pk] < s) & gmask);
+    const int nlo = c > 0 ? lo + (int)((int64_t)c * n / (gs + 1)) + 1 : lo;
+    const int nhi = c < gs ? lo + (int)((int64_t)(c + 1) * n / (gs + 1)) : hi;
+    lo = nlo;
+    hi = nhi;
   }
-  return lo;
+  const bool below = lo + k < hi && seq_idx[lo + k] < s;
+  return lo + __popcll(__ballot(below) & gmask);
 }
 
-// Where every sequence id starts: one binary search per id in [0, rows], all
-// in parallel; the end of id s is the start of id s + 1, so each boundary is
-// searched for once.
+// Where every sequence id starts: one search per id in [0, rows], all of them
+// in parallel, with as many lanes per search as the workgroup has to spare;
+// the end of id s is the start of id s + 1.
 __device__ __forceinline__ void sequence_bounds(const int32_t *seq_idx, int L, int rows, int *seq_start,
                                                 int *seq_end) {
-  for (int s = threadIdx.x; s <= rows; s += kPlanThreads) {
-    const int st = lower_bound_seq(seq_idx, L, s);
-    if (s < rows) seq_start[s] = st;
-    if (s >= 1) seq_end[s - 1] = st;
+  int gs = 64;
+  while (gs > 1 && gs * (rows + 1) > kPlanThreads) gs >>= 1;
+  const int per_pass = kPlanThreads / gs;
+  for (int b0 = 0; b0 <= rows; b0 += per_pass) {
+    const int b = b0 + (int)threadIdx.x / gs;  // the same for the whole group
+    if (b <= rows) {
+      const int k = (int)threadIdx.x & (gs - 1);
+      const int st = lower_bound_group(seq_idx, L, b, gs, k);
+      if (k == 0) {
+        if (b < rows) seq_start[b] = st;
+        if (b >= 1) seq_end[b - 1] = st;
+      }
+    }
   }
   __syncthreads();
 }
