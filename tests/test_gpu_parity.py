@@ -90,6 +90,23 @@ def test_packed_many_short_sequences():
     assert ey <= TOL[True] and ef <= TOL[True]
 
 
+@pytest.mark.parametrize("nseq", [100, 200, 300])
+def test_packed_sequence_counts(nseq):
+    """Packed streams whose sequence count sets how many lanes share each
+    sequence-bound search in the planner (8, 4 and 2 lanes at 100, 200 and
+    300 sequences), with empty sequences among them."""
+    rng = np.random.default_rng(nseq)
+    lens = rng.integers(0, 40, nseq) * (rng.random(nseq) < 0.85)
+    w = W(f"bf16_packed_{nseq}seqs_h2_g1_init", 1, 0, 2, 1, init=0.3, lens=lens)
+    print(f"case {w.name} tokens={int(lens.sum())}", flush=True)
+    d = inputs.make_scan_inputs(w, seed=nseq + 1)
+    y, fs = gpu_layer(d, w)
+    ry, rf = oracle_layer(d, w)
+    ey, ef = rel(to_np(y), ry), rel(to_np(fs), rf)
+    print(f"  y rel err {ey:.3e}  final-state rel err {ef:.3e}")
+    assert ey <= TOL[True] and ef <= TOL[True]
+
+
 def test_strong_decay():
     """Heads whose 32-token blocks decay by more than e^64 next to heads with
     mild decay, and a head with A = -1e4 that drives every off-diagonal term
