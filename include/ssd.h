@@ -141,14 +141,16 @@ int ssd_conv1d_silu(const ssd_conv_args *args, void *stream);
  * Supported: headdim 64, dstate 128, chunk_size 64, 128 or 256, dtype F32
  * or BF16.  chunk_size is the model's chunk length; the block (chunked) form
  * of the recurrence gives the same result for any chunk length, up to
- * rounding, so the kernels always work in 128-token tiles.
+ * rounding, so the kernels always work in their own tiles (128 tokens for
+ * bf16, 64 for fp32).
  * x, B, C, y 16-byte aligned with strides multiples of 8 elements; token
  * strides below 2^22 elements (SSD_ERR_INVALID_ARG otherwise).
  *
- * seg_chunks: 0 = automatic.  Otherwise each sequence is cut into segments
- * of seg_chunks 128-token tiles that run in parallel; the state entering each
- * segment is found by a short pre-pass (same result, more parallelism for
- * few long sequences).
+ * seg_chunks: 0 = automatic (segments of whole kernel tiles, as many as
+ * fill the GPU).  Otherwise each sequence is cut into segments of seg_chunks
+ * 128-token tiles that run in parallel; the state entering each segment is
+ * found by a short pre-pass (same result, more parallelism for few long
+ * sequences).
  *
  * The workspace (device memory, at least ssd_chunk_scan_workspace_size()
  * bytes, 256-byte aligned, contents on entry irrelevant) holds the

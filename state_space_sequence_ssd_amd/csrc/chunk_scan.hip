@@ -486,19 +486,28 @@ ScanPlan make_scan_plan(const ScanParams &p, int seg_chunks) {
   plan.packed = p.seq_idx != nullptr;
   plan.rows = plan.packed ? p.num_seqs : p.batch;
   const int chunks_max = std::max(1, (p.L + kChunk - 1) / kChunk);
+  // Automatic segments are whole tiles of the kernel that runs them: 128
+  // tokens for bf16, the fp32 kernel's 64-token sub-chunks for fp32 (its
+  // result does not depend on where segments start, so short inputs with few
+  // (sequence, head) pairs get twice the workgroups).
+  const int unit = p.bf16 ? kChunk : kSub;
+  int seg_units;
   if (seg_chunks <= 0) {
+    const int units_max = std::max(1, (p.L + unit - 1) / unit);
     // workgroup slots of one wave of launches: the bf16 kernel fits two per CU
     const long long slots = p.bf16 ? 2LL * kNumCU : (long long)kNumCU;
     const long long base = (long long)plan.rows * p.H;
     if (base >= slots) {
-      seg_chunks = chunks_max;
+      seg_units = units_max;
     } else {
       const int factor = (int)((slots + base - 1) / base);
-      seg_chunks = std::max(1, (chunks_max + factor - 1) / factor);
+      seg_units = std::max(1, (units_max + factor - 1) / factor);
     }
+    seg_units = std::min(seg_units, units_max);
+  } else {
+    seg_units = std::min(seg_chunks, chunks_max) * (kChunk / unit);
   }
-  seg_chunks = std::min(seg_chunks, chunks_max);
-  plan.seg_len = seg_chunks * kChunk;
+  plan.seg_len = seg_units * unit;
   plan.segmented = plan.seg_len < p.L;
   if (!plan.packed) {
     plan.nseg = std::max(1, (p.L + plan.seg_len - 1) / plan.seg_len);
