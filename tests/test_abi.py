@@ -177,3 +177,23 @@ def test_library_has_no_cpu_fallback_symbols():
     exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
     assert {e for e in exported if e.startswith("ssd_")} == set(ssd.EXPORTS)
     assert not any("oracle" in e for e in exported)
+
+
+def test_automatic_segments_follow_the_kernel_tile():
+    """Automatic segmentation cuts fp32 inputs at the fp32 kernel's 64-token
+    sub-chunks and bf16 inputs at 128-token tiles; an explicit seg_chunks
+    counts 128-token tiles for both.  The workspace holds a local and an
+    entry state (64 x 128 fp32) per (segment, head) plus the decays, each
+    block 256-byte aligned."""
+    lib = ssd.load_library()
+    state = 64 * 128 * 4
+
+    def need(**kw):
+        return lib.ssd_chunk_scan_workspace_size(
+            ctypes.byref(scan_args(batch=1, seqlen=512, nheads=8, ngroups=1, **kw)))
+
+    def expected(nseg):
+        return 2 * nseg * 8 * state + (-(-nseg * 8 * 4 // 256)) * 256
+    assert need(dtype=ssd.SSD_DTYPE_F32) == expected(8)   # 64-token segments
+    assert need() == expected(4)                          # bf16: 128-token segments
+    assert need(dtype=ssd.SSD_DTYPE_F32, seg_chunks=2) == expected(2)
