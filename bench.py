@@ -12,7 +12,7 @@ layer) is timed in the same run and reported as HBM GB/s.
 Per-kernel times come from HIP events recorded on the stream the kernels
 run on (torch's current stream, which the C ABI launches on).
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 200]
 """
 import argparse
 import hashlib
@@ -217,7 +217,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # The scan is bound by the shader clock, which ramps up over the first
+    # ~100 ms of load: 200 untimed steps (~80 ms) reach the steady state.
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--decode-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (profiler runs)")
