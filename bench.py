@@ -7,12 +7,24 @@ scan (chunk 128) writing y and the final states.  Inputs are synthetic and
 already resident in HBM.  The headline value is layer tokens/s.
 
 The decode step at batch 256 through 29 Mamba-2 layers (1 GiB fp32 state per
-layer) is timed in the same run and reported as HBM GB/s.
+layer) is timed in the same run and reported as HBM GB/s, and so are the
+other synthetic configs (tiny fp32, Nemotron 3 Nano, packed 3B stream).
+
+Order of the run: decode first, then the other configs, then the headline
+step.  The scan is bound by the shader clock, which ramps up over the first
+~100 ms of load; by the time the headline step is timed the GPU has been
+busy for well over that, so its W warm-up steps and K timed steps run at the
+clock a loaded GPU holds.
 
 Per-kernel times come from HIP events recorded on the stream the kernels
 run on (torch's current stream, which the C ABI launches on).
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 200]
+The fp64 oracle (test infrastructure) is timed beside every config on the
+host's cores, on all OpenMP threads and on one, over a bounded sample of
+each workload; its all-core outputs also give each config's parity error.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 20]
+    python bench.py --only nemotron_h_8b     # one part only (profiler runs)
 """
 import argparse
 import hashlib
@@ -96,137 +108,376 @@ def decode_algorithmic_bytes(dw):
             + CD * dw.conv_width * 4 + 3 * H * 4)
 
 
-def time_config(w, seed, steps, warmup):
-    """conv (if the workload has one) + scan of one synthetic config, event-timed
-    per kernel on the launch stream; rates against the HBM roofline."""
-    import numpy as np
-    import torch
-    from state_space_sequence_ssd_amd import inputs, ssd
-    dev = torch.device("cuda:0")
-    dtp = torch.bfloat16 if w.bf16 else torch.float32
-    d = inputs.make_scan_inputs(w, seed=seed)
-    H, G, P, N = w.nheads, w.ngroups, w.headdim, w.dstate
-    Bt, L = w.batch, w.seqlen
-    seq = torch.from_numpy(d["seq_idx"]).to(dev) if "seq_idx" in d else None
-    nseq = w.num_seqs if seq is not None else None
-    if w.conv:
-        xbc = torch.from_numpy(d["xBC"]).to(dev, dtp)
-        conv_w = torch.from_numpy(d["conv_w"]).to(dev)
-        conv_out = torch.empty_like(xbc)
-        x = conv_out[..., :H * P].view(Bt, L, H, P)
-        Bm = conv_out[..., H * P:H * P + G * N].view(Bt, L, G, N)
-        Cm = conv_out[..., H * P + G * N:].view(Bt, L, G, N)
-    else:
-        x = torch.from_numpy(d["x"]).to(dev, dtp)
-        Bm = torch.from_numpy(d["B"]).to(dev, dtp)
-        Cm = torch.from_numpy(d["C"]).to(dev, dtp)
-    dt = torch.from_numpy(d["dt"]).to(dev, dtp)
-    A, D = torch.from_numpy(d["A"]).to(dev), torch.from_numpy(d["D"]).to(dev)
-    dt_bias = torch.from_numpy(d["dt_bias"]).to(dev)
-    init = torch.from_numpy(d["initial_state"]).to(dev) if "initial_state" in d else None
-    y = torch.empty((Bt, L, H, P), dtype=dtp, device=dev)
-    fs = torch.empty((w.num_seqs, H, P, N), dtype=torch.float32, device=dev)
-    wsb = ssd.ssd_chunk_scan_workspace_size(x, dt, A, Bm, Cm, seq_idx=seq, num_seqs=nseq)
-    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
+class ScanRun:
+    """Device tensors of one prefill config and its step (conv if the workload
+    has one, then the scan with final states), launched through the C ABI."""
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    def __init__(self, w, seed):
+        import torch
+        from state_space_sequence_ssd_amd import inputs, ssd
+        self.w, self.ssd = w, ssd
+        dev = torch.device("cuda:0")
+        dtp = torch.bfloat16 if w.bf16 else torch.float32
+        self.d = d = inputs.make_scan_inputs(w, seed=seed)
+        H, G, P, N = w.nheads, w.ngroups, w.headdim, w.dstate
+        Bt, L = w.batch, w.seqlen
+        self.seq = torch.from_numpy(d["seq_idx"]).to(dev) if "seq_idx" in d else None
+        self.nseq = w.num_seqs if self.seq is not None else None
         if w.conv:
-            ssd.ssd_conv1d_silu(xbc, conv_w, seq_idx=seq, num_seqs=nseq, out=conv_out)
-        if ev is not None:
-            ev[1].record(stream)
-        ssd.ssd_chunk_scan_fwd(x, dt, A, Bm, Cm, dt_bias=dt_bias, D=D, seq_idx=seq, num_seqs=nseq,
-                               initial_state=init, final_state=fs, y=y, workspace=ws)
-        if ev is not None:
-            ev[2].record(stream)
+            self.xbc = torch.from_numpy(d["xBC"]).to(dev, dtp)
+            self.conv_w = torch.from_numpy(d["conv_w"]).to(dev)
+            self.conv_out = torch.empty_like(self.xbc)
+            co = self.conv_out
+            self.x = co[..., :H * P].view(Bt, L, H, P)
+            self.B = co[..., H * P:H * P + G * N].view(Bt, L, G, N)
+            self.C = co[..., H * P + G * N:].view(Bt, L, G, N)
+        else:
+            self.x = torch.from_numpy(d["x"]).to(dev, dtp)
+            self.B = torch.from_numpy(d["B"]).to(dev, dtp)
+            self.C = torch.from_numpy(d["C"]).to(dev, dtp)
+        self.dt = torch.from_numpy(d["dt"]).to(dev, dtp)
+        self.A, self.D = torch.from_numpy(d["A"]).to(dev), torch.from_numpy(d["D"]).to(dev)
+        self.dt_bias = torch.from_numpy(d["dt_bias"]).to(dev)
+        self.init = torch.from_numpy(d["initial_state"]).to(dev) if "initial_state" in d else None
+        self.y = torch.empty((Bt, L, H, P), dtype=dtp, device=dev)
+        self.fs = torch.empty((w.num_seqs, H, P, N), dtype=torch.float32, device=dev)
+        wsb = ssd.ssd_chunk_scan_workspace_size(self.x, self.dt, self.A, self.B, self.C, seq_idx=self.seq,
+                                                num_seqs=self.nseq)
+        self.ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+        self.stream = torch.cuda.current_stream()
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    for i in range(steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    scan_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    # launch-inclusive: host wall clock over back-to-back calls of the whole step
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize()
-    host_ms = (time.perf_counter() - t0) * 1e3 / steps
+    def step(self, ev=None):
+        ssd, w = self.ssd, self.w
+        if ev is not None:
+            ev[0].record(self.stream)
+        if w.conv:
+            ssd.ssd_conv1d_silu(self.xbc, self.conv_w, seq_idx=self.seq, num_seqs=self.nseq, out=self.conv_out)
+        if ev is not None:
+            ev[1].record(self.stream)
+        ssd.ssd_chunk_scan_fwd(self.x, self.dt, self.A, self.B, self.C, dt_bias=self.dt_bias, D=self.D,
+                               seq_idx=self.seq, num_seqs=self.nseq, initial_state=self.init,
+                               final_state=self.fs, y=self.y, workspace=self.ws)
+        if ev is not None:
+            ev[2].record(self.stream)
+
+    def timed(self, steps, warmup):
+        """W untimed steps, then K steps bracketed by events per kernel and
+        around the whole region.  Returns (total_ms, conv_ms list, scan_ms list, wall_s)."""
+        import torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        t0.record(self.stream)
+        for i in range(steps):
+            self.step(evs[i])
+        t1.record(self.stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        conv = [e[0].elapsed_time(e[1]) for e in evs]
+        scan = [e[1].elapsed_time(e[2]) for e in evs]
+        return t0.elapsed_time(t1), conv, scan, wall
+
+    def launch_inclusive_ms(self, steps):
+        """Host wall clock per back-to-back call of the whole step."""
+        import torch
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            self.step()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def config_result(run, steps, warmup):
+    """One synthetic config, event-timed per kernel on the launch stream; rates
+    against the HBM roofline."""
+    import numpy as np
+    w = run.w
+    _, conv, scan, _ = run.timed(steps, warmup)
+    scan_ms = float(np.mean(scan))
+    tokens = w.batch * w.seqlen
     sb = scan_algorithmic_bytes(w)
-    out = {"tokens": Bt * L, "io_dtype": "bf16" if w.bf16 else "f32",
+    out = {"tokens": tokens, "io_dtype": "bf16" if w.bf16 else "f32",
            "scan_avg_ms": round(scan_ms, 5), "scan_algorithmic_bytes": sb,
            "scan_gbs": round(sb / (scan_ms * 1e-3) / 1e9, 1),
            "scan_hbm_frac": round(sb / (scan_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-           "scan_tokens_per_s": round(Bt * L / (scan_ms * 1e-3), 1)}
+           "scan_tokens_per_s": round(tokens / (scan_ms * 1e-3), 1)}
     step_ms = scan_ms
     if w.conv:
-        conv_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        conv_ms = float(np.mean(conv))
         cb = conv_algorithmic_bytes(w)
         out.update({"conv_avg_ms": round(conv_ms, 5), "conv_algorithmic_bytes": cb,
                     "conv_gbs": round(cb / (conv_ms * 1e-3) / 1e9, 1),
                     "conv_hbm_frac": round(cb / (conv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
         step_ms += conv_ms
-    out["layer_tokens_per_s"] = round(Bt * L / (step_ms * 1e-3), 1)
-    out["step_launch_inclusive_ms"] = round(host_ms, 5)
+    out["layer_tokens_per_s"] = round(tokens / (step_ms * 1e-3), 1)
+    out["step_launch_inclusive_ms"] = round(run.launch_inclusive_ms(steps), 5)
     return out
 
 
-def cpu_baseline(w, d, rows):
-    """The fp64 oracle (as it stands) on a bounded sample of the same workload:
-    the first `rows` batch rows, all tokens and heads, conv then scan with final
-    states.  Reported as tokens/s of that sample."""
+# ---------------------------------------------------------------------------
+# the fp64 oracle beside the GPU: all OpenMP threads and one, bounded samples
+# ---------------------------------------------------------------------------
+_GOMP = None
+
+
+def omp_threads(n=None):
+    """Get (n None) or set the OpenMP thread count of the oracle's runtime."""
+    global _GOMP
+    import ctypes
+    if _GOMP is None:
+        _GOMP = ctypes.CDLL("libgomp.so.1")
+    if n is None:
+        return _GOMP.omp_get_max_threads()
+    _GOMP.omp_set_num_threads(int(n))
+    return n
+
+
+def host_info():
+    import torch
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    rocm = None
+    try:
+        rocm = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        pass
+    drv = None
+    try:
+        drv = open("/sys/module/amdgpu/version").read().strip()
+    except OSError:
+        pass
+    return {"cpu_model": model, "host_cpus_usable": len(os.sched_getaffinity(0)),
+            "omp_threads": omp_threads(), "rocm": rocm, "amdgpu_driver": drv,
+            "torch": torch.__version__, "torch_hip": getattr(torch.version, "hip", None),
+            "gpu": torch.cuda.get_device_name(0)}
+
+
+def oracle_scan_sample(w, d, rows=None, seqs=None, tokens=None):
+    """The oracle's conv (if any) + scan with final states over a sample of one
+    workload: the first `rows` batch rows, or the first `seqs` packed
+    sequences, or the first `tokens` tokens of a one-row stream.  Returns
+    (y, final_state, seconds, tokens, description)."""
+    import numpy as np
     import oracle
     H, G, P, N = w.nheads, w.ngroups, w.headdim, w.dstate
-    L = w.seqlen
+    seq_idx = d.get("seq_idx")
+    init = d.get("initial_state")
+    if seqs is not None:
+        T = int(np.sum(w.packed_lengths[:seqs]))
+        bsel, tsel = slice(0, 1), slice(0, T)
+        seq_idx, nseq = seq_idx[:T], seqs
+        init = None if init is None else init[:seqs]
+        desc = f"first {seqs} of {w.num_seqs} packed sequences ({T} tokens), all {H} heads"
+    else:
+        r = rows if rows is not None else w.batch
+        T = tokens if tokens is not None else w.seqlen
+        bsel, tsel = slice(0, r), slice(0, T)
+        nseq = None
+        init = None if init is None else init[:r]
+        desc = (f"batch rows 0..{r - 1} of {w.batch}, tokens 0..{T - 1} of {w.seqlen}, all {H} heads")
     t0 = time.perf_counter()
-    v = oracle.conv1d_silu(d["xBC"][:rows], d["conv_w"])
-    x = v[..., :H * P].reshape(rows, L, H, P)
-    B = v[..., H * P:H * P + G * N].reshape(rows, L, G, N)
-    C = v[..., H * P + G * N:].reshape(rows, L, G, N)
-    oracle.ssd_scan(x, d["dt"][:rows], d["dt_bias"], d["A"], B, C, d["D"], want_final_state=True)
+    if w.conv:
+        v = oracle.conv1d_silu(d["xBC"][bsel, tsel], d["conv_w"], seq_idx=seq_idx, num_seqs=nseq)
+        b_ = v.shape[0]
+        x = v[..., :H * P].reshape(b_, -1, H, P)
+        B = v[..., H * P:H * P + G * N].reshape(b_, -1, G, N)
+        C = v[..., H * P + G * N:].reshape(b_, -1, G, N)
+    else:
+        x, B, C = d["x"][bsel, tsel], d["B"][bsel, tsel], d["C"][bsel, tsel]
+    y, fs = oracle.ssd_scan(x, d["dt"][bsel, tsel], d["dt_bias"], d["A"], B, C, d["D"], seq_idx=seq_idx,
+                            num_seqs=nseq, initial_state=init, want_final_state=True)
     el = time.perf_counter() - t0
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
-    return {"value": rows * L / el, "unit": "tokens/s/layer", "cores": threads, "kind": "oracle",
-            "sample": f"batch rows 0..{rows - 1} of {w.batch}, all {L} tokens and {H} heads: fp64 conv "
-                      f"then fp64 sequential recurrence with final states, {el:.1f} s wall",
-            "seconds": el}
+    ntok = (bsel.stop - bsel.start) * (tsel.stop - tsel.start)
+    step = "fp64 conv then fp64 sequential recurrence" if w.conv else "fp64 sequential recurrence"
+    return y, fs, el, ntok, f"{desc}: {step} with final states"
 
 
-def cpu_baseline_single_core(w, d):
-    """The same oracle on one host thread over one batch row, so that the
-    per-core rate sits beside the all-core one.  The oracle's recurrences are
-    an OpenMP loop; its thread count is set through the OpenMP runtime the
-    oracle library is linked against, and restored afterwards."""
-    import ctypes
-    gomp = ctypes.CDLL("libgomp.so.1")
-    n = gomp.omp_get_max_threads()
-    gomp.omp_set_num_threads(1)
+def rel_err(a, ref):
+    import numpy as np
+    den = float(np.max(np.abs(ref))) if ref.size else 0.0
+    err = float(np.max(np.abs(np.asarray(a, np.float64) - ref))) if ref.size else 0.0
+    return err / den if den > 0 else err
+
+
+def oracle_beside(run, all_sample, one_sample, parity=True):
+    """Oracle tokens/s on all threads (all_sample) and on one (one_sample), and
+    the parity error of the GPU outputs against the all-thread outputs, which
+    are the oracle's result on the same inputs (the sample's rows/tokens)."""
+    import numpy as np
+    w, d = run.w, run.d
+    n = omp_threads()
+    y, fs, el, ntok, desc = oracle_scan_sample(w, d, **all_sample)
+    res = {"value": round(ntok / el, 1), "unit": "tokens/s/layer", "cores": n, "kind": "oracle",
+           "sample": f"{desc}, {el:.2f} s wall"}
+    if parity:
+        bs = all_sample
+        if "seqs" in bs:
+            T = y.shape[1]
+            yg = run.y[:, :T]
+            fg = run.fs[:bs["seqs"]]
+        else:
+            r = bs.get("rows") or w.batch
+            T = bs.get("tokens") or w.seqlen
+            yg = run.y[:r, :T]
+            fg = run.fs[:r] if T == w.seqlen else None
+        ey = rel_err(yg.float().cpu().numpy(), y)
+        res["parity"] = {"y_rel_err": float(f"{ey:.3e}"), "bar": 2e-2 if w.bf16 else 1e-4}
+        if fg is not None:
+            res["parity"]["final_state_rel_err"] = float(f"{rel_err(fg.cpu().numpy(), fs):.3e}")
+    del y, fs
+    omp_threads(1)
     try:
-        r = cpu_baseline(w, d, 1)
+        _, _, el1, ntok1, desc1 = oracle_scan_sample(w, d, **one_sample)
     finally:
-        gomp.omp_set_num_threads(n)
-    r["cores"] = 1
-    return r
+        omp_threads(n)
+    one = {"value": round(ntok1 / el1, 1), "unit": "tokens/s/layer", "cores": 1, "kind": "oracle",
+           "sample": f"{desc1}, {el1:.2f} s wall"}
+    return res, one
+
+
+def oracle_decode_beside(dw, rows_all, rows_one):
+    """Oracle decode on a sample of batch rows of one layer (fresh inputs of
+    the same workload), all threads and one: tokens/s and algorithmic GB/s
+    scaled per token."""
+    import oracle
+    from state_space_sequence_ssd_amd import inputs
+    n = omp_threads()
+    out = {}
+    for tag, rows in (("all", rows_all), ("one", rows_one)):
+        w = inputs.DecodeWorkload(dw.name, rows, dw.nheads, dw.ngroups, 1, bf16=dw.bf16)
+        dd = inputs.make_decode_small_inputs(w, seed=4, layer=0)
+        st = inputs.decode_state_host(w, 4, 0)
+        if tag == "one":
+            omp_threads(1)
+        try:
+            t0 = time.perf_counter()
+            oracle.decode_step(dd["xBC"], dd["dt"], dd["dt_bias"], dd["A"], dd["D"], st, dw.nheads,
+                               dw.headdim, dw.dstate, dw.ngroups, conv_w=dd["conv_w"],
+                               conv_state=dd["conv_state"])
+            el = time.perf_counter() - t0
+        finally:
+            omp_threads(n)
+        bytes_per_tok = decode_algorithmic_bytes(dw) / dw.batch
+        out[tag] = {"value": round(rows / el, 1), "unit": "tokens/s/layer",
+                    "gbs": round(rows * bytes_per_tok / el / 1e9, 2),
+                    "cores": n if tag == "all" else 1, "kind": "oracle",
+                    "sample": f"one layer, {rows} of {dw.batch} batch rows (fresh inputs of the same "
+                              f"distributions): fp64 conv window + recurrence step, {el:.2f} s wall"}
+    return out["all"], out["one"]
+
+
+# ---------------------------------------------------------------------------
+def run_decode(args, stream):
+    """Batch-256 decode through 29 layers: HBM GB/s of the whole sweep, one
+    layer's event-timed kernel, and the parity of the first application on
+    16 rows of layer 0 against the oracle."""
+    import numpy as np
+    import torch
+    import oracle
+    from state_space_sequence_ssd_amd import inputs, ssd
+    dev = torch.device("cuda:0")
+    bf = torch.bfloat16
+    dw = inputs.decode_29_layers()
+    layers = []
+    for l in range(dw.layers):
+        dd = inputs.make_decode_small_inputs(dw, seed=4, layer=l)
+        layers.append({
+            "host": dd if l == 0 else None,
+            "xBC": torch.from_numpy(dd["xBC"]).to(dev, bf),
+            "dt": torch.from_numpy(dd["dt"]).to(dev, bf),
+            "conv_state": torch.from_numpy(dd["conv_state"]).to(dev, bf),
+            "conv_w": torch.from_numpy(dd["conv_w"]).to(dev),
+            "A": torch.from_numpy(dd["A"]).to(dev), "D": torch.from_numpy(dd["D"]).to(dev),
+            "dt_bias": torch.from_numpy(dd["dt_bias"]).to(dev),
+            "state": inputs.decode_state_device(dw, 4, l, dev),
+            "y": torch.empty((dw.batch, dw.nheads, dw.headdim), dtype=bf, device=dev)})
+    prow = 16
+    st0 = layers[0]["state"][:prow].cpu().numpy()
+
+    def dstep(ev=None):
+        for li, L_ in enumerate(layers):
+            if ev is not None and li == 0:
+                ev[0].record(stream)
+            ssd.ssd_decode_step(L_["xBC"], L_["dt"], L_["A"], L_["state"], dw.nheads, dw.ngroups,
+                                dt_bias=L_["dt_bias"], D=L_["D"], conv_state=L_["conv_state"],
+                                conv_weight=L_["conv_w"], y=L_["y"])
+            if ev is not None and li == 0:
+                ev[1].record(stream)
+
+    dstep()
+    torch.cuda.synchronize()
+    y_first = layers[0]["y"][:prow].float().cpu().numpy()
+    s_first = layers[0]["state"][:prow].cpu().numpy()
+    for _ in range(2):
+        dstep()
+    torch.cuda.synchronize()
+    devs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.decode_steps)]
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    d0.record(stream)
+    for i in range(args.decode_steps):
+        dstep(devs[i])
+    d1.record(stream)
+    torch.cuda.synchronize()
+    dms = d0.elapsed_time(d1) / args.decode_steps
+    one_layer_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in devs]))
+    dbytes = decode_algorithmic_bytes(dw)
+    gbs = dbytes * dw.layers / (dms * 1e-3) / 1e9
+    h = layers[0]["host"]
+    del layers
+    torch.cuda.empty_cache()
+    ry, rs, _ = oracle.decode_step(h["xBC"][:prow], h["dt"][:prow], h["dt_bias"], h["A"], h["D"], st0,
+                                   dw.nheads, dw.headdim, dw.dstate, dw.ngroups, conv_w=h["conv_w"],
+                                   conv_state=h["conv_state"][:prow])
+    out = {"metric": "decode-step HBM GB/s", "value": round(gbs, 1), "unit": "GB/s",
+           "frac": round(gbs / HBM_PEAK_GBS, 4), "ms_per_29_layers": round(dms, 4),
+           "tokens_per_s": round(dw.batch / (dms * 1e-3), 1),
+           "layer_kernel_avg_ms": round(one_layer_ms, 4),
+           "layer_kernel_gbs": round(dbytes / (one_layer_ms * 1e-3) / 1e9, 1),
+           "algorithmic_bytes_per_layer": dbytes,
+           "traffic": read_traffic("decode_step_b256_h128", DECODE_SOURCES),
+           "workload": dw.name,
+           "parity": {"y_rel_err": float(f"{rel_err(y_first, ry):.3e}"),
+                      "state_rel_err": float(f"{rel_err(s_first, rs):.3e}"), "bar": 2e-2,
+                      "sample": f"layer 0, batch rows 0..{prow - 1}, first application"}}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"], out["cpu_baseline_single_core"] = oracle_decode_beside(dw, 64, 8)
+    return out
+
+
+CONFIG_SAMPLES = {
+    # name: (all-thread sample, one-thread sample)
+    "tiny_fp32_h8_l512": ({}, {}),
+    "nemotron3_nano_b1_l16384": ({}, {"tokens": 2048}),
+    "packed_3b_h40_32seqs": ({}, {"seqs": 2}),
+}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    # The scan is bound by the shader clock, which ramps up over the first
-    # ~100 ms of load: 200 untimed steps (~80 ms) reach the steady state.
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--decode-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true",
-                    help="skip the oracle timing (profiler runs)")
+                    help="skip the oracle timing and parity (profiler runs)")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other synthetic configs (profiler runs: same kernel names)")
-    ap.add_argument("--cpu-rows", type=int, default=4, help="batch rows in the oracle sample (4 = the whole step)")
+    ap.add_argument("--only", choices=["nemotron_h_8b", "decode", "tiny_fp32", "nemotron3_nano", "packed_3b"],
+                    help="run one part only (profiler runs: one workload per kernel name)")
+    ap.add_argument("--cpu-rows", type=int, default=4, help="batch rows in the all-thread oracle sample "
+                    "of the headline workload (4 = the whole step)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter calibration)")
     args = ap.parse_args()
@@ -243,56 +494,41 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     ssd.load_library()
-    bf = torch.bfloat16
-
-    # ---------------- prefill workload (Nemotron-H 8B layer shape) ----------------
-    w = inputs.nemotron_h_8b()
-    d = inputs.make_scan_inputs(w, seed=1)
-    H, G, P, N = w.nheads, w.ngroups, w.headdim, w.dstate
-    xbc = torch.from_numpy(d["xBC"]).to(dev, bf)
-    conv_w = torch.from_numpy(d["conv_w"]).to(dev)
-    dt = torch.from_numpy(d["dt"]).to(dev, bf)
-    A = torch.from_numpy(d["A"]).to(dev)
-    D = torch.from_numpy(d["D"]).to(dev)
-    dt_bias = torch.from_numpy(d["dt_bias"]).to(dev)
-    conv_out = torch.empty_like(xbc)
-    x = conv_out[..., :H * P].view(w.batch, w.seqlen, H, P)
-    Bm = conv_out[..., H * P:H * P + G * N].view(w.batch, w.seqlen, G, N)
-    Cm = conv_out[..., H * P + G * N:].view(w.batch, w.seqlen, G, N)
-    y = torch.empty((w.batch, w.seqlen, H, P), dtype=bf, device=dev)
-    fs = torch.empty((w.batch, H, P, N), dtype=torch.float32, device=dev)
-    ws_bytes = ssd.ssd_chunk_scan_workspace_size(x, dt, A, Bm, Cm)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
+    want = (lambda part: args.only is None or args.only == part)
+    cpu_on = not args.no_cpu_baseline
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        ssd.ssd_conv1d_silu(xbc, conv_w, out=conv_out)
-        if ev is not None:
-            ev[1].record(stream)
-        ssd.ssd_chunk_scan_fwd(x, dt, A, Bm, Cm, dt_bias=dt_bias, D=D, final_state=fs, y=y,
-                               workspace=ws)
-        if ev is not None:
-            ev[2].record(stream)
+    # ---------------- decode: batch 256 through 29 layers ----------------
+    decode = None
+    if want("decode") and not args.no_decode:
+        decode = run_decode(args, stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record(stream)
-    for i in range(args.steps):
-        step(evs[i])
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = t_start.elapsed_time(t_end)
-    conv_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    scan_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    # ---------------- the other synthetic configs (parity workloads) ----------------
+    configs = None
+    if not args.no_configs or args.only in ("tiny_fp32", "nemotron3_nano", "packed_3b"):
+        configs = {}
+        for key, cw, seed in [("tiny_fp32", inputs.tiny_fp32(), 0), ("nemotron3_nano", inputs.nemotron3_nano(), 2),
+                              ("packed_3b", inputs.packed_3b(), 3)]:
+            if not want(key):
+                continue
+            run = ScanRun(cw, seed)
+            configs[cw.name] = config_result(run, args.steps, args.warmup)
+            if cpu_on:
+                a, o = CONFIG_SAMPLES[cw.name]
+                configs[cw.name]["cpu_baseline"], configs[cw.name]["cpu_baseline_single_core"] = \
+                    oracle_beside(run, a, o)
+            del run
+            torch.cuda.empty_cache()
+
+    if not want("nemotron_h_8b"):
+        print(json.dumps({"only": args.only, "decode": decode, "configs": configs}))
+        return
+
+    # ---------------- headline: prefill step at the Nemotron-H 8B layer shape ----------------
+    w = inputs.nemotron_h_8b()
+    run = ScanRun(w, seed=1)
+    H, G, P, N = w.nheads, w.ngroups, w.headdim, w.dstate
+    total_ms, conv_ms, scan_ms, wall = run.timed(args.steps, args.warmup)
     ms_per_step = total_ms / args.steps
     tokens = w.batch * w.seqlen
     value = tokens / (ms_per_step / 1e3)
@@ -326,71 +562,11 @@ def main():
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
-
-    # ---------------- decode: batch 256 through 29 layers ----------------
-    decode = None
-    if not args.no_decode:
-        dw = inputs.decode_29_layers()
-        layers = []
-        for l in range(dw.layers):
-            dd = inputs.make_decode_small_inputs(dw, seed=4, layer=l)
-            layers.append({
-                "xBC": torch.from_numpy(dd["xBC"]).to(dev, bf),
-                "dt": torch.from_numpy(dd["dt"]).to(dev, bf),
-                "conv_state": torch.from_numpy(dd["conv_state"]).to(dev, bf),
-                "conv_w": torch.from_numpy(dd["conv_w"]).to(dev),
-                "A": torch.from_numpy(dd["A"]).to(dev), "D": torch.from_numpy(dd["D"]).to(dev),
-                "dt_bias": torch.from_numpy(dd["dt_bias"]).to(dev),
-                "state": inputs.decode_state_device(dw, 4, l, dev),
-                "y": torch.empty((dw.batch, dw.nheads, dw.headdim), dtype=bf, device=dev)})
-
-        def dstep(ev=None):
-            for li, L_ in enumerate(layers):
-                if ev is not None and li == 0:
-                    ev[0].record(stream)
-                ssd.ssd_decode_step(L_["xBC"], L_["dt"], L_["A"], L_["state"], dw.nheads, dw.ngroups,
-                                    dt_bias=L_["dt_bias"], D=L_["D"], conv_state=L_["conv_state"],
-                                    conv_weight=L_["conv_w"], y=L_["y"])
-                if ev is not None and li == 0:
-                    ev[1].record(stream)
-
-        for _ in range(2):
-            dstep()
-        torch.cuda.synchronize()
-        devs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.decode_steps)]
-        d0 = torch.cuda.Event(enable_timing=True)
-        d1 = torch.cuda.Event(enable_timing=True)
-        d0.record(stream)
-        for i in range(args.decode_steps):
-            dstep(devs[i])
-        d1.record(stream)
-        torch.cuda.synchronize()
-        dms = d0.elapsed_time(d1) / args.decode_steps
-        one_layer_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in devs]))
-        dbytes = decode_algorithmic_bytes(dw)
-        gbs = dbytes * dw.layers / (dms * 1e-3) / 1e9
-        decode = {"metric": "decode-step HBM GB/s", "value": round(gbs, 1), "unit": "GB/s",
-                  "frac": round(gbs / HBM_PEAK_GBS, 4), "ms_per_29_layers": round(dms, 4),
-                  "tokens_per_s": round(dw.batch / (dms * 1e-3), 1),
-                  "layer_kernel_avg_ms": round(one_layer_ms, 4),
-                  "algorithmic_bytes_per_layer": dbytes,
-                  "traffic": read_traffic("decode_step_b256_h128", DECODE_SOURCES),
-                  "workload": dw.name}
-        del layers
-        torch.cuda.empty_cache()
-
-    # ---------------- the other synthetic configs (parity workloads) ----------------
-    configs = None
-    if not args.no_configs:
-        configs = {}
-        for cw, seed in [(inputs.tiny_fp32(), 0), (inputs.nemotron3_nano(), 2), (inputs.packed_3b(), 3)]:
-            configs[cw.name] = time_config(cw, seed, steps=10, warmup=2)
-            torch.cuda.empty_cache()
+        del src, dst
 
     cpu = cpu1 = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, d, args.cpu_rows)
-        cpu1 = cpu_baseline_single_core(w, d)
+    if cpu_on:
+        cpu, cpu1 = oracle_beside(run, {"rows": args.cpu_rows}, {"rows": 1})
 
     line = {
         "metric": "SSD scan tokens/s/layer @Nemotron-H-8B shape; decode-step HBM GB/s",
@@ -411,11 +587,12 @@ def main():
                    "parallelism": "single GPU"},
         "wall_s_timed": round(wall, 4),
         "roofline": roofline,
-        "cpu_baseline": None if cpu is None else {k: v for k, v in cpu.items() if k != "seconds"},
-        "cpu_baseline_single_core": None if cpu1 is None else {k: v for k, v in cpu1.items() if k != "seconds"},
+        "cpu_baseline": cpu,
+        "cpu_baseline_single_core": cpu1,
         "kernels": kernels,
         "decode": decode,
         "configs": configs,
+        "host": host_info(),
     }
     print(json.dumps(line))
 

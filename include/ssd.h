@@ -71,6 +71,11 @@ typedef enum ssd_dtype {
 /* ------------------------------------------------------------------------
  * ssd_conv1d_silu -- depthwise causal conv1d + SiLU.
  *
+ * Passage: the Mamba-2 block's short causal convolution of kernel 4 with SiLU
+ * on the x|B|C channels ("Nemotron-H style Hybrid Mamba-Transformer 3B
+ * feasibility study", sec. 1.4 "Mamba-2 configuration"), applied before the
+ * scan ("Nemotron-Mamba3 architecture" article, sec. 2.2).
+ *
  *   u[t][c]   = bias[c] + sum_{k=0}^{width-1} weight[c][k] * v(t-(width-1)+k, c)
  *   out[t][c] = u[t][c] / (1 + exp(-u[t][c]))
  *
@@ -118,6 +123,14 @@ int ssd_conv1d_silu(const ssd_conv_args *args, void *stream);
 
 /* ------------------------------------------------------------------------
  * ssd_chunk_scan_fwd -- chunked SSD prefill of the selective scan above.
+ *
+ * Passages: the recurrence with a scalar-times-identity transition per head
+ * ("Mamba-3: an inference-first state space model", the paragraph on
+ * Mamba-2's simplified transition); its block (chunked) evaluation as a
+ * masked matrix product, the state space duality ("AI Engineering EP6",
+ * sec. 8 and 10); chunk 128 and n_groups 8 (feasibility study sec. 1.4);
+ * states carried between calls for resumable, chunked prefill ("Bamba-9B"
+ * summary, inference-efficiency section).
  *
  * Tensors (innermost two dims contiguous; strides for batch and token):
  *   x  (batch, seqlen, nheads, headdim)    head stride = headdim
@@ -187,6 +200,11 @@ int ssd_chunk_scan_fwd(const ssd_scan_args *args, void *workspace,
  * ssd_decode_step -- one token of the recurrence for every batch row,
  * updating the states in place.
  *
+ * Passage: decoding applies the same recurrence one token at a time to a
+ * fixed-size state, which makes it memory-bound ("Mamba-3" blog, the
+ * paragraph on why the simplified transition ties decoding to memory
+ * traffic; "Bamba-9B" summary, inference-efficiency section).
+ *
  *   xBC (batch, conv_dim), conv_dim = nheads*headdim + 2*ngroups*dstate,
  *       channel order x (head-major), B (group-major), C (group-major).
  *       Raw (pre-conv) when conv_state != NULL, else already conv+SiLU'd.
@@ -200,8 +218,9 @@ int ssd_chunk_scan_fwd(const ssd_scan_args *args, void *workspace,
  *   y (batch, nheads, headdim), dtype of xBC, batch stride y_stride_batch.
  *
  * Supported: headdim 64, dstate 128, conv_width 4, dtype F32 or BF16;
- * ssm_state 16-byte aligned; nheads / ngroups at most 254 (one workgroup
- * holds a group's conv outputs and y in LDS), SSD_ERR_UNSUPPORTED beyond.
+ * ssm_state 16-byte aligned; nheads / ngroups at most 250 (one workgroup
+ * holds a group's conv outputs and y in 128 KiB of LDS:
+ * 130 * (nheads / ngroups) + 256 floats), SSD_ERR_UNSUPPORTED beyond.
  * ---------------------------------------------------------------------- */
 typedef struct ssd_decode_args {
   uint32_t struct_size;          /* sizeof(ssd_decode_args) */

@@ -109,6 +109,9 @@ int oracle_conv1d_silu(int batch, int L, int CH, int K,
         const double *xs = x + (seq_idx ? 0 : (size_t)s * L * CH);
         double *os = out + (seq_idx ? 0 : (size_t)s * L * CH);
         const double *st = conv_state_in ? conv_state_in + (size_t)s * (K - 1) * CH : NULL;
+        /* channels are independent: OpenMP only splits the channel loop over
+         * threads; each output element is computed exactly as in one thread */
+#pragma omp parallel for schedule(static)
         for (int c = 0; c < CH; ++c) {
             /* v(tau) for tau relative to the sequence start */
             for (int t = start[s]; t < end[s]; ++t) {
@@ -223,8 +226,11 @@ int oracle_decode_step(int batch, int H, int P, int N, int G, int K,
     if (conv_state && (!conv_w || K < 1)) return -1;
     const int CH = H * P + 2 * G * N;
     const int heads_per_group = H / G;
-    double *v = (double *)malloc(sizeof(double) * CH);
+    /* batch rows are independent: OpenMP only splits the row loop over
+     * threads, each row with its own conv-output buffer v */
+#pragma omp parallel for schedule(dynamic, 1)
     for (int b = 0; b < batch; ++b) {
+        double *v = (double *)malloc(sizeof(double) * CH);
         const double *tok = xBC + (size_t)b * CH;
         if (conv_state) {
             double *cs = conv_state + (size_t)b * (K - 1) * CH;
@@ -262,7 +268,7 @@ int oracle_decode_step(int batch, int H, int P, int N, int G, int K,
                 y[((size_t)b * H + h) * P + p] = acc + (D ? D[h] : 0.0) * xv[h * P + p];
             }
         }
+        free(v);
     }
-    free(v);
     return 0;
 }

@@ -117,12 +117,49 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream
 
 
-def _f32(t: Optional[torch.Tensor], name: str):
+def _f32(t: Optional[torch.Tensor], name: str, numel: Optional[int] = None,
+         shape: Optional[tuple] = None):
+    """A contiguous float32 tensor (or None), of `numel` elements / `shape` if given."""
     if t is None:
         return None
     if t.dtype != torch.float32 or not t.is_contiguous():
         raise TypeError(f"{name} must be a contiguous float32 tensor")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} elements (got {t.numel()})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
     return t
+
+
+def _same_dtype(ref: torch.Tensor, **tensors):
+    """Every given tensor has ref's dtype (the one dtype code the ABI carries)."""
+    for name, t in tensors.items():
+        if t is not None and t.dtype != ref.dtype:
+            raise TypeError(f"{name} is {t.dtype}, but the call's tensors are {ref.dtype}")
+
+
+def _shape(t: Optional[torch.Tensor], name: str, shape: tuple):
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+
+
+def _seq_idx(seq_idx: Optional[torch.Tensor], L: int, num_seqs: Optional[int]):
+    if seq_idx is None:
+        return
+    if seq_idx.dtype != torch.int32 or not seq_idx.is_contiguous() or tuple(seq_idx.shape) != (L,):
+        raise TypeError(f"seq_idx must be a contiguous int32 tensor of shape ({L},)")
+    if num_seqs is None or int(num_seqs) < 1:
+        raise ValueError("num_seqs (>= 1) is required with seq_idx")
+
+
+def _on_gpu(ref: torch.Tensor, **tensors):
+    """Every tensor lives on ref's GPU: the library dereferences device pointers
+    only.  Checked last, after every dtype and shape check."""
+    if not ref.is_cuda:
+        raise ValueError("tensors must be on a GPU (the HIP path has no CPU fallback)")
+    for name, t in tensors.items():
+        if t is not None and (not t.is_cuda or t.device != ref.device):
+            raise ValueError(f"{name} must be on {ref.device} (got {t.device})")
 
 
 # ---------------------------------------------------------------------------
@@ -133,9 +170,29 @@ def ssd_conv1d_silu(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.
                     out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Depthwise causal conv1d (width = weight.shape[1]) + SiLU.  x: (batch, L, channels)."""
     lib = load_library()
+    if x.dim() != 3:
+        raise ValueError("x must be (batch, L, channels)")
     batch, L, CH = x.shape
     if x.stride(2) != 1:
         raise ValueError("x must have unit channel stride")
+    _dtype_code(x)
+    if weight.dim() != 2 or weight.shape[0] != CH:
+        raise ValueError(f"weight must be (channels={CH}, width)")
+    K = weight.shape[1]
+    _f32(weight, "weight")
+    _f32(bias, "bias", numel=CH)
+    _seq_idx(seq_idx, L, num_seqs)
+    rows = int(num_seqs) if seq_idx is not None else batch
+    _same_dtype(x, out=out, conv_state_in=conv_state_in, conv_state_out=conv_state_out)
+    _shape(out, "out", (batch, L, CH))
+    for name, t in (("conv_state_in", conv_state_in), ("conv_state_out", conv_state_out)):
+        _shape(t, name, (rows, K - 1, CH))
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if out is not None and out.stride(2) != 1:
+        raise ValueError("out must have unit channel stride")
+    _on_gpu(x, out=out, weight=weight, bias=bias, seq_idx=seq_idx, conv_state_in=conv_state_in,
+            conv_state_out=conv_state_out)
     if out is None:
         out = torch.empty((batch, L, CH), dtype=x.dtype, device=x.device)
     a = SsdConvArgs()
@@ -156,8 +213,25 @@ def ssd_conv1d_silu(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.
 
 def _scan_args(x, dt, A, B, C, dt_bias, D, seq_idx, num_seqs, initial_state, final_state, y,
                chunk_size, seg_chunks) -> SsdScanArgs:
+    if x.dim() != 4 or B.dim() != 4 or C.dim() != 4 or dt.dim() != 3:
+        raise ValueError("x (batch,L,H,P), B/C (batch,L,G,N) and dt (batch,L,H) expected")
     batch, L, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
+    _dtype_code(x)
+    _same_dtype(x, dt=dt, B=B, C=C, y=y)
+    _shape(B, "B", (batch, L, G, N))
+    _shape(C, "C", (batch, L, G, N))
+    _shape(dt, "dt", (batch, L, H))
+    _shape(y, "y", (batch, L, H, P))
+    _f32(A, "A", numel=H)
+    _f32(dt_bias, "dt_bias", numel=H)
+    _f32(D, "D", numel=H)
+    _seq_idx(seq_idx, L, num_seqs)
+    rows = int(num_seqs) if seq_idx is not None else batch
+    _f32(initial_state, "initial_state", shape=(rows, H, P, N))
+    _f32(final_state, "final_state", shape=(rows, H, P, N))
+    _on_gpu(x, dt=dt, A=A, B=B, C=C, y=y, dt_bias=dt_bias, D=D, seq_idx=seq_idx,
+            initial_state=initial_state, final_state=final_state)
     if L > 0:
         for t, name, inner in ((x, "x", P), (y, "y", P), (B, "B", N), (C, "C", N)):
             if t is not None and (t.stride(3) != 1 or t.stride(2) != inner):
@@ -233,13 +307,33 @@ def ssd_decode_step(xBC: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, ssm_st
                     y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """One decode token; updates ssm_state (and conv_state) in place.  Returns y (batch,H,P)."""
     lib = load_library()
+    if xBC.dim() != 2 or dt.dim() != 2:
+        raise ValueError("xBC (batch, conv_dim) and dt (batch, nheads) expected")
     batch = xBC.shape[0]
+    conv_dim = nheads * headdim + 2 * ngroups * dstate
     if xBC.stride(1) != 1 or dt.stride(1) != 1:
         raise ValueError("xBC and dt rows must be contiguous")
-    if not ssm_state.is_contiguous() or ssm_state.dtype != torch.float32:
-        raise TypeError("ssm_state must be a contiguous float32 tensor")
-    if conv_state is not None and not conv_state.is_contiguous():
-        raise TypeError("conv_state must be contiguous")
+    _dtype_code(xBC)
+    _same_dtype(xBC, dt=dt, conv_state=conv_state, y=y)
+    _shape(xBC, "xBC", (batch, conv_dim))
+    _shape(dt, "dt", (batch, nheads))
+    _f32(ssm_state, "ssm_state", shape=(batch, nheads, headdim, dstate))
+    _f32(A, "A", numel=nheads)
+    _f32(dt_bias, "dt_bias", numel=nheads)
+    _f32(D, "D", numel=nheads)
+    if conv_state is not None:
+        if conv_weight is None:
+            raise ValueError("conv_state needs conv_weight")
+        if conv_weight.dim() != 2 or conv_weight.shape[0] != conv_dim:
+            raise ValueError(f"conv_weight must be (conv_dim={conv_dim}, width)")
+        _f32(conv_weight, "conv_weight")
+        _f32(conv_bias, "conv_bias", numel=conv_dim)
+        _shape(conv_state, "conv_state", (batch, conv_weight.shape[1] - 1, conv_dim))
+        if not conv_state.is_contiguous():
+            raise TypeError("conv_state must be contiguous")
+    _shape(y, "y", (batch, nheads, headdim))
+    _on_gpu(xBC, dt=dt, A=A, ssm_state=ssm_state, dt_bias=dt_bias, D=D, conv_state=conv_state,
+            conv_weight=conv_weight, conv_bias=conv_bias, y=y)
     if y is None:
         y = torch.empty((batch, nheads, headdim), dtype=xBC.dtype, device=xBC.device)
     if y.stride(2) != 1 or y.stride(1) != headdim:

@@ -67,11 +67,25 @@ def gpu_layer(d, w, seg_chunks=0, final=True, chunk_size=128):
 def oracle_layer(d, w, heads=None, rows=None):
     """Oracle of the whole layer, optionally restricted to some heads / batch rows.
 
+    Without a restriction the oracle runs once over whole tensors (its OpenMP
+    loop spreads the (row, head) recurrences over the host cores).
     Restricting is exact: the conv is per channel, and each head only reads
     its own x channels, dt column and its group's B/C channels.
     Returns y (batch', L, H', P) and final_state (rows', H', P, N).
     """
     H, G, P, N = w.nheads, w.ngroups, w.headdim, w.dstate
+    if heads is None and rows is None:
+        seq_idx = d.get("seq_idx")
+        nseq = w.num_seqs if seq_idx is not None else None
+        if w.conv:
+            v = oracle.conv1d_silu(d["xBC"], d["conv_w"], seq_idx=seq_idx, num_seqs=nseq)
+            x, B, C = split_xbc(v, H, G, P, N)
+            del v
+        else:
+            x, B, C = d["x"], d["B"], d["C"]
+        return oracle.ssd_scan(x, d["dt"], d["dt_bias"], d["A"], B, C, d["D"], seq_idx=seq_idx,
+                               num_seqs=nseq, initial_state=d.get("initial_state"),
+                               want_final_state=True)
     heads = list(range(H)) if heads is None else list(heads)
     hpg = H // G
     groups = sorted({h // hpg for h in heads})

@@ -59,6 +59,31 @@ def pin_dt_zero(lib):
     assert np.array_equal(fs, d["h0"]), "dt=0 must freeze the state"
 
 
+def pin_softplus_large_argument(lib):
+    """dt_raw + dt_bias far above 30 (the oracle's overflow-safe softplus branch)
+    and just below it: with one token, zero state and P = N = 1,
+    y = C dt x B + D x gives dt back, which must equal numpy's logaddexp(0, z).
+    A two-head, many-token run against the masked quadratic form follows."""
+    z = np.array([45.0, 38.5, 31.0, 30.0, 29.5, 12.0, -3.0])
+    for zi in z:
+        for bias in (0.0, 40.0, -10.0):
+            d = {"x": np.full((1, 1, 1, 1), 1.5), "dt": np.full((1, 1, 1), zi - bias),
+                 "dt_bias": np.array([bias]), "A": np.array([-0.7]), "B": np.full((1, 1, 1, 1), 0.5),
+                 "C": np.full((1, 1, 1, 1), -2.0), "D": np.array([0.25])}
+            y, fs = _scan(lib, d)
+            dt = (y[0, 0, 0, 0] - 0.25 * 1.5) / (-2.0 * 1.5 * 0.5)
+            assert abs(dt - softplus(zi)) <= 1e-14 * max(1.0, softplus(zi)), ("softplus", zi, bias, dt)
+            assert abs(fs[0, 0, 0, 0] - softplus(zi) * 1.5 * 0.5) <= 1e-14 * max(1.0, softplus(zi))
+    H, P, N, G, L = 2, 3, 4, 1, 25
+    d = _rand(71, H, P, N, G, L)
+    d["dt_bias"] = np.array([40.0, 28.0])
+    d["A"] = np.array([-1e-3, -2e-3])
+    y, _ = _scan(lib, d)
+    assert np.all(d["dt"][0, :, 0] + 40.0 > 30.0)
+    ref = quadratic_form(d["x"][0], d["dt"][0], d["dt_bias"], d["A"], d["B"][0], d["C"][0], d["D"])
+    assert rel_err(y[0], ref) < 1e-11, ("large dt quadratic form", rel_err(y[0], ref))
+
+
 def pin_linear_attention(lib):
     """A = 0: causal linear attention y_i = sum_{j<=i} (C_i.B_j) dt_j x_j + D x_i,
     computed as a running sum of outer products."""

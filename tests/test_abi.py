@@ -197,3 +197,14 @@ def test_automatic_segments_follow_the_kernel_tile():
     assert need(dtype=ssd.SSD_DTYPE_F32) == expected(8)   # 64-token segments
     assert need() == expected(4)                          # bf16: 128-token segments
     assert need(dtype=ssd.SSD_DTYPE_F32, seg_chunks=2) == expected(2)
+
+
+def test_decode_heads_per_group_limit():
+    """One decode workgroup holds a group's conv outputs and y in LDS: up to
+    250 heads per group are accepted, 251 are UNSUPPORTED.  The accepted case
+    is stopped by a later check (a batch stride below the row width), so no
+    kernel is launched."""
+    lib = ssd.load_library()
+    for hpg, code in ((250, 1), (251, 2), (16, 1)):
+        a = decode_args(nheads=hpg, ngroups=1, xBC_stride_batch=8)
+        assert lib.ssd_decode_step(ctypes.byref(a), None) == code, hpg

@@ -6,6 +6,8 @@ term in bench.py's formulas shows up here.  The per-token figures match the
 measurement table of the hot-path scope (37,120 B/token for the Nemotron-H
 8B scan, 20,608 B/token for Nemotron 3 Nano).
 """
+import numpy as np
+
 import bench
 from state_space_sequence_ssd_amd import inputs
 
@@ -90,15 +92,29 @@ def test_bench_refuses_more_than_one_gpu():
     assert "one GPU" in r.stderr + r.stdout
 
 
-def test_cpu_baseline_single_core_restores_threads():
-    """The one-thread oracle timing reports cores = 1 and leaves the OpenMP
-    thread count as it found it."""
+def test_oracle_beside_restores_threads_and_reports_parity():
+    """The oracle is timed on all OpenMP threads and on one (cores = 1), the
+    thread count is left as it was found, and the parity error is taken
+    against the all-thread outputs of the sample (here an all-zero stand-in
+    for the GPU outputs, so the error is exactly 1)."""
     import ctypes
-    w = inputs.ScanWorkload("tiny_conv", 1, 256, 8, 2, bf16=True, conv=True, final_state=True)
-    d = inputs.make_scan_inputs(w, seed=3)
-    gomp = ctypes.CDLL("libgomp.so.1")
-    before = gomp.omp_get_max_threads()
-    r = bench.cpu_baseline_single_core(w, d)
-    assert gomp.omp_get_max_threads() == before
-    assert r["cores"] == 1 and r["kind"] == "oracle" and r["value"] > 0
-    assert "batch rows 0..0 of 1" in r["sample"]
+    from types import SimpleNamespace
+    import torch
+    for w, a, o in [
+        (inputs.ScanWorkload("tiny_conv", 2, 256, 8, 2, bf16=True, conv=True, final_state=True),
+         {}, {"rows": 1}),
+        (inputs.ScanWorkload("tiny_packed", 1, 300, 4, 2, bf16=False, conv=False, final_state=True,
+                             packed_lengths=np.array([100, 0, 150, 50]), init_std=0.3),
+         {}, {"seqs": 2}),
+    ]:
+        d = inputs.make_scan_inputs(w, seed=3)
+        run = SimpleNamespace(w=w, d=d, y=torch.zeros(w.batch, w.seqlen, w.nheads, 64),
+                              fs=torch.zeros(w.num_seqs, w.nheads, 64, 128))
+        gomp = ctypes.CDLL("libgomp.so.1")
+        before = gomp.omp_get_max_threads()
+        allc, one = bench.oracle_beside(run, a, o)
+        assert gomp.omp_get_max_threads() == before
+        assert allc["cores"] == before and one["cores"] == 1
+        assert allc["kind"] == one["kind"] == "oracle" and allc["value"] > 0 and one["value"] > 0
+        assert allc["parity"]["y_rel_err"] == 1.0 and allc["parity"]["final_state_rel_err"] == 1.0
+        assert allc["parity"]["bar"] == (2e-2 if w.bf16 else 1e-4)

@@ -21,6 +21,8 @@ MUTANTS = {
                           "S[p * N + n] = a * S[p * N + n] + xt[p] * Bt[n];"),
     "no_skip_D": ("yt[p] = acc + d_skip * xt[p];", "yt[p] = acc;"),
     "softplus_is_exp": ("return log1p(exp(z));", "return exp(z);"),
+    "softplus_large_drops_z": ("if (z > 30.0) return z + log1p(exp(-z));",
+                               "if (z > 30.0) return log1p(exp(-z));"),
     "decay_sign": ("const double a = exp(dt * A[h]);\n            const double *xt",
                    "const double a = exp(-dt * A[h]);\n            const double *xt"),
     "B_C_swapped": ("const double *Bt = B + (tok * G + g) * N;\n            const double *Ct = C + (tok * G + g) * N;",
