@@ -29,7 +29,9 @@
  *   - All tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA
  *     tensors) unless stated otherwise.  The caller allocates and owns every
  *     buffer, including the scan workspace.  The library never allocates
- *     device memory, never synchronises, and keeps no device state.
+ *     device memory and never synchronises; its only device state is the
+ *     workspace array of ssd_chunk_scan_fwd_noalloc, reserved with the code
+ *     object (below).
  *   - Strides are in ELEMENTS.  The innermost dimension of each tensor is
  *     unit-stride; the dimensions listed as "contiguous" are packed.
  *   - `stream` is a hipStream_t (NULL = the null stream).  Calls enqueue
@@ -195,6 +197,31 @@ size_t ssd_chunk_scan_workspace_size(const ssd_scan_args *args);
 
 int ssd_chunk_scan_fwd(const ssd_scan_args *args, void *workspace,
                        size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * ssd_chunk_scan_fwd_noalloc -- ssd_chunk_scan_fwd without a caller
+ * workspace, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same arguments, kernels and results as ssd_chunk_scan_fwd.  The workspace
+ * is a library-owned device array of SSD_NOALLOC_SCRATCH_BYTES (96 MiB) per
+ * GPU, reserved when the library's code object is loaded on that GPU and
+ * held until the process ends; its address is looked up on the calling
+ * thread's current device (which must be the stream's device) on the first
+ * call there.  The call allocates nothing.  That is enough for every
+ * automatic segmentation (seg_chunks = 0 needs at most 1,533 (segment, head)
+ * pairs of two 32 KiB states, 95.9 MiB, at 511 heads in one packed
+ * sequence); a call that needs more (an explicit seg_chunks) returns
+ * SSD_ERR_WORKSPACE_TOO_SMALL before any HIP call.
+ *
+ * All calls on one GPU share its array, and it keeps the last call's
+ * contents (nothing in it needs to start at zero).  Calls that overlap on one
+ * GPU -- on different streams, or from different host threads without
+ * ordering between them -- race on it; serialise them (one stream, or events).
+ * ---------------------------------------------------------------------- */
+#define SSD_NOALLOC_SCRATCH_BYTES (96u * 1024u * 1024u)
+
+int ssd_chunk_scan_fwd_noalloc(const ssd_scan_args *args, void *stream);
 
 /* ------------------------------------------------------------------------
  * ssd_decode_step -- one token of the recurrence for every batch row,

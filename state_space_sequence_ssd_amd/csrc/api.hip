@@ -2,11 +2,13 @@
 // error reporting and dispatch to the gfx950 kernels.  Every check here is
 // host arithmetic on the argument struct and runs before any HIP call.
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <cstdarg>
 #include <cstdlib>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "debug_checks.h"
 #include "kernels.h"
@@ -120,6 +122,42 @@ int check_scan(const ssd_scan_args *a, ssd::ScanParams &p) {
   return SSD_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Library-owned scan workspace for ssd_chunk_scan_fwd_noalloc: one array per
+// GPU, in device memory the code object reserves when it is loaded (each GPU
+// that runs the library holds it until the process ends).  In host code the
+// array's name is only a host-side stand-in; its device address on the
+// current GPU comes from hipGetSymbolAddress, looked up once per device and
+// kept, and only that address is ever passed to a kernel.
+// ---------------------------------------------------------------------------
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) char scratch[SSD_NOALLOC_SCRATCH_BYTES];
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_address(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SSD_ERR_HIP, "ssd_chunk_scan_fwd_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SSD_ERR_UNSUPPORTED, "ssd_chunk_scan_fwd_noalloc: device %d beyond the %d this build tracks", dev,
+                kMaxDevices);
+  void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !p)
+        return fail(SSD_ERR_HIP, "ssd_chunk_scan_fwd_noalloc: hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                    hipGetErrorString(e));
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return SSD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -195,6 +233,29 @@ int ssd_chunk_scan_fwd(const ssd_scan_args *a, void *workspace, size_t ws_bytes,
   if (drc != SSD_OK) return drc;
   const hipError_t e = ssd::launch_chunk_scan(p, plan, workspace, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SSD_ERR_HIP, "ssd_chunk_scan_fwd: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int ssd_chunk_scan_fwd_noalloc(const ssd_scan_args *a, void *stream) {
+  ssd::ScanParams p;
+  const int rc = check_scan(a, p);
+  if (rc != SSD_OK) return rc;
+  // the same plan (and so the same kernels and results) as ssd_chunk_scan_fwd
+  const ssd::ScanPlan plan = ssd::make_scan_plan(p, a->seg_chunks);
+  if (plan.ws_bytes > (size_t)SSD_NOALLOC_SCRATCH_BYTES)
+    return fail(SSD_ERR_WORKSPACE_TOO_SMALL,
+                "ssd_chunk_scan_fwd_noalloc: this call needs %zu bytes of workspace, more than the library's "
+                "%zu-byte array (use ssd_chunk_scan_fwd with a caller workspace)",
+                plan.ws_bytes, (size_t)SSD_NOALLOC_SCRATCH_BYTES);
+  void *ws = nullptr;
+  if (plan.ws_bytes > 0) {
+    const int src = scratch_address(&ws);
+    if (src != SSD_OK) return src;
+  }
+  const int drc = debug_check_seq_idx("ssd_chunk_scan_fwd_noalloc", a->seq_idx, a->seqlen, a->num_seqs, stream);
+  if (drc != SSD_OK) return drc;
+  const hipError_t e = ssd::launch_chunk_scan(p, plan, ws, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SSD_ERR_HIP, "ssd_chunk_scan_fwd_noalloc: %s", hipGetErrorString(e));
   return ok();
 }
 

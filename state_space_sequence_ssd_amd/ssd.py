@@ -58,7 +58,8 @@ class SsdDecodeArgs(ctypes.Structure):
 
 
 EXPORTS = ["ssd_conv1d_silu", "ssd_chunk_scan_workspace_size", "ssd_chunk_scan_fwd",
-           "ssd_decode_step", "ssd_last_error", "ssd_version"]
+           "ssd_chunk_scan_fwd_noalloc", "ssd_decode_step", "ssd_last_error", "ssd_version"]
+NOALLOC_SCRATCH_BYTES = 96 * 1024 * 1024   # SSD_NOALLOC_SCRATCH_BYTES
 
 _lib = None
 
@@ -78,6 +79,8 @@ def load_library(path: str = LIB_PATH):
     lib.ssd_chunk_scan_workspace_size.restype = ctypes.c_size_t
     lib.ssd_chunk_scan_fwd.argtypes = [ctypes.POINTER(SsdScanArgs), _vp, ctypes.c_size_t, _vp]
     lib.ssd_chunk_scan_fwd.restype = ctypes.c_int
+    lib.ssd_chunk_scan_fwd_noalloc.argtypes = [ctypes.POINTER(SsdScanArgs), _vp]
+    lib.ssd_chunk_scan_fwd_noalloc.restype = ctypes.c_int
     lib.ssd_decode_step.argtypes = [ctypes.POINTER(SsdDecodeArgs), _vp]
     lib.ssd_decode_step.restype = ctypes.c_int
     lib.ssd_last_error.argtypes = []
@@ -295,6 +298,25 @@ def ssd_chunk_scan_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: to
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.ssd_chunk_scan_fwd(ctypes.byref(a), _ptr(workspace), ws_bytes, _stream(stream)))
+    return y
+
+
+def ssd_chunk_scan_fwd_noalloc(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                               C: torch.Tensor, y: torch.Tensor, dt_bias: Optional[torch.Tensor] = None,
+                               D: Optional[torch.Tensor] = None, seq_idx: Optional[torch.Tensor] = None,
+                               num_seqs: Optional[int] = None,
+                               initial_state: Optional[torch.Tensor] = None,
+                               final_state: Optional[torch.Tensor] = None,
+                               chunk_size: int = 128, seg_chunks: int = 0, stream=None) -> torch.Tensor:
+    """ssd_chunk_scan_fwd with the library's own workspace array: nothing is
+    allocated (y is required).  Calls that overlap on one GPU race on that
+    array; the current device must be the stream's.  Returns y."""
+    lib = load_library()
+    if y is None:
+        raise ValueError("y is required (this entry point allocates nothing)")
+    a = _scan_args(x, dt, A, B, C, dt_bias, D, seq_idx, num_seqs, initial_state, final_state, y,
+                   chunk_size, seg_chunks)
+    _check(lib.ssd_chunk_scan_fwd_noalloc(ctypes.byref(a), _stream(stream)))
     return y
 
 

@@ -208,3 +208,48 @@ def test_decode_heads_per_group_limit():
     for hpg, code in ((250, 1), (251, 2), (16, 1)):
         a = decode_args(nheads=hpg, ngroups=1, xBC_stride_batch=8)
         assert lib.ssd_decode_step(ctypes.byref(a), None) == code, hpg
+
+
+def test_noalloc_scratch_size_constant_matches_header():
+    src = open(os.path.join(ROOT, "include", "ssd.h")).read()
+    m = re.search(r"#define SSD_NOALLOC_SCRATCH_BYTES \((\d+)u \* 1024u \* 1024u\)", src)
+    assert m and int(m.group(1)) * 1024 * 1024 == ssd.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_fits_every_automatic_segmentation():
+    """With seg_chunks = 0 the workspace of any shape fits the no-allocation
+    entry point's array: batch rows and packed streams (one to four
+    sequences, where segmentation is deepest), both dtypes, 1 to 600 heads."""
+    lib = ssd.load_library()
+    worst = 0
+    for dtype in (ssd.SSD_DTYPE_BF16, ssd.SSD_DTYPE_F32):
+        for H in list(range(1, 64)) + list(range(64, 601, 7)) + [255, 256, 257, 500, 510, 511, 512, 513]:
+            for rows in (1, 2, 3, 4):
+                for L in (100_000, 1 << 20):
+                    for packed in (False, True):
+                        a = scan_args(dtype=dtype, nheads=H, ngroups=1, seqlen=L,
+                                      batch=1 if packed else rows)
+                        for t in ("x", "y"):
+                            setattr(a, t + "_stride_token", ((H * 64 + 7) // 8) * 8)
+                        a.dt_stride_token = H
+                        if packed:
+                            a.seq_idx, a.num_seqs = FAKE, rows
+                        n = lib.ssd_chunk_scan_workspace_size(ctypes.byref(a))
+                        assert n != ctypes.c_size_t(-1).value, lib.ssd_last_error()
+                        worst = max(worst, n)
+    assert worst <= ssd.NOALLOC_SCRATCH_BYTES, worst
+    assert worst > 0.9 * ssd.NOALLOC_SCRATCH_BYTES   # the bound is tight, not padded
+
+
+def test_noalloc_rejects_a_workspace_beyond_its_array():
+    """An explicit one-tile segmentation of the Nemotron-H 8B shape needs
+    1 GiB of segment states: refused before any HIP call."""
+    lib = ssd.load_library()
+    a = scan_args(seg_chunks=1)
+    need = lib.ssd_chunk_scan_workspace_size(ctypes.byref(a))
+    assert need > ssd.NOALLOC_SCRATCH_BYTES
+    assert lib.ssd_chunk_scan_fwd_noalloc(ctypes.byref(a), None) == 3
+    msg = lib.ssd_last_error().decode()
+    assert "noalloc" in msg and str(need) in msg
+    # argument errors come first, as in ssd_chunk_scan_fwd
+    assert lib.ssd_chunk_scan_fwd_noalloc(ctypes.byref(scan_args(ngroups=3)), None) == 1
