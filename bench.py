@@ -273,6 +273,8 @@ def oracle_scan_sample(w, d, rows=None, seqs=None, tokens=None):
     H, G, P, N = w.nheads, w.ngroups, w.headdim, w.dstate
     seq_idx = d.get("seq_idx")
     init = d.get("initial_state")
+    if seqs is None and rows is None and tokens is None and seq_idx is not None:
+        seqs = w.num_seqs            # a packed stream: the sample is whole sequences
     if seqs is not None:
         T = int(np.sum(w.packed_lengths[:seqs]))
         bsel, tsel = slice(0, 1), slice(0, T)
@@ -450,8 +452,6 @@ def run_decode(args, stream):
            "parity": {"y_rel_err": float(f"{rel_err(y_first, ry):.3e}"),
                       "state_rel_err": float(f"{rel_err(s_first, rs):.3e}"), "bar": 2e-2,
                       "sample": f"layer 0, batch rows 0..{prow - 1}, first application"}}
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"], out["cpu_baseline_single_core"] = oracle_decode_beside(dw, 64, 8)
     return out
 
 
@@ -505,6 +505,7 @@ def main():
 
     # ---------------- the other synthetic configs (parity workloads) ----------------
     configs = None
+    config_runs = []
     if not args.no_configs or args.only in ("tiny_fp32", "nemotron3_nano", "packed_3b"):
         configs = {}
         for key, cw, seed in [("tiny_fp32", inputs.tiny_fp32(), 0), ("nemotron3_nano", inputs.nemotron3_nano(), 2),
@@ -513,14 +514,22 @@ def main():
                 continue
             run = ScanRun(cw, seed)
             configs[cw.name] = config_result(run, args.steps, args.warmup)
+            config_runs.append(run)
+
+    def oracle_configs():
+        # the oracle runs after every GPU measurement, so the GPU never idles
+        # (and its clock never drops) between the timed parts
+        for run in config_runs:
             if cpu_on:
-                a, o = CONFIG_SAMPLES[cw.name]
-                configs[cw.name]["cpu_baseline"], configs[cw.name]["cpu_baseline_single_core"] = \
+                a, o = CONFIG_SAMPLES[run.w.name]
+                configs[run.w.name]["cpu_baseline"], configs[run.w.name]["cpu_baseline_single_core"] = \
                     oracle_beside(run, a, o)
-            del run
-            torch.cuda.empty_cache()
+        if decode is not None and cpu_on:
+            decode["cpu_baseline"], decode["cpu_baseline_single_core"] = oracle_decode_beside(
+                inputs.decode_29_layers(), 128, 16)
 
     if not want("nemotron_h_8b"):
+        oracle_configs()
         print(json.dumps({"only": args.only, "decode": decode, "configs": configs}))
         return
 
@@ -567,6 +576,7 @@ def main():
     cpu = cpu1 = None
     if cpu_on:
         cpu, cpu1 = oracle_beside(run, {"rows": args.cpu_rows}, {"rows": 1})
+    oracle_configs()
 
     line = {
         "metric": "SSD scan tokens/s/layer @Nemotron-H-8B shape; decode-step HBM GB/s",
