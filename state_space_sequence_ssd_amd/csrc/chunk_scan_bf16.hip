@@ -8,8 +8,8 @@
 // study", sec. 1.4) is
 //
 //   G      = B C^T                                   (C B^T, K = d_state)
-//   M[i][j] = G[j][i] exp(cs_i - cs_j) dt_j  (j < i),  G[i][i] dt_i + D (j = i)
-//   y      = exp(cs_i) (C_i H_prev^T)  +  sum_j M[i][j] x_j
+//   M[i][j] = G[j][i] exp(cs_i - cs_j) dt_j  (j <= i)
+//   y      = exp(cs_i) (C_i H_prev^T)  +  sum_j M[i][j] x_j  +  D x_i
 //   H      = exp(cs_last) H_prev  +  sum_j w_j x_j B_j^T,  w_j = exp(cs_last - cs_j) dt_j
 //
 // and every exponent is a difference cs_i - cs_j with j <= i (<= 0).
@@ -583,7 +583,7 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
       for (int q = 0; q < 2; ++q)
 #pragma unroll
         for (int r = 0; r < 16; ++r) yo[q][r] *= ecs;
-      // decay mask, dt and D -> bf16 M operand (rows j, col i) in registers,
+      // decay mask and dt -> bf16 M operand (rows j, col i) in registers,
       // then y^T[p][i] += sum_j x[j][p] M[j][i]
 #pragma unroll
       for (int jb = 0; jb < NCB; ++jb) {
@@ -639,9 +639,9 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
             for (int t = 0; t < 4; ++t) {
               const int r = 4 * q + t;
               const int d = ci - (jq + t);
-              // exp(-inf) = 0 above the diagonal; D joins on it (exp(0) = 1)
+              // exp(-inf) = 0 above the diagonal
               const float e = __expf(d >= 0 ? cs_i - cj[t] : -INFINITY);
-              Mb[r >> 3][r & 7] = (__bf16)fmaf(G[jb][r] * e, dj[t], d == 0 ? Dh : 0.f);
+              Mb[r >> 3][r & 7] = (__bf16)(G[jb][r] * e * dj[t]);
             }
           }
         }
@@ -650,6 +650,18 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
 #pragma unroll
           for (int q = 0; q < 2; ++q) yo[q] = mfma32(xf[s2][q], Mb[s2], yo[q]);
       }
+      // the skip term D x_i in fp32 (x rows are still this chunk's until
+      // barrier A): the lane holds p = 32 q + 8 r4 + 4 hh + 0..3 of row ci
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const u32x2 xv = lds_ld<u32x2>(sm.X + off128(ci, 32 * q + 8 * r4 + 4 * L.hh));
+          yo[q][4 * r4 + 0] = fmaf(Dh, lo_bf16(xv[0]), yo[q][4 * r4 + 0]);
+          yo[q][4 * r4 + 1] = fmaf(Dh, hi_bf16(xv[0]), yo[q][4 * r4 + 1]);
+          yo[q][4 * r4 + 2] = fmaf(Dh, lo_bf16(xv[1]), yo[q][4 * r4 + 2]);
+          yo[q][4 * r4 + 3] = fmaf(Dh, hi_bf16(xv[1]), yo[q][4 * r4 + 3]);
+        }
     }
     if (has_next && __builtin_amdgcn_readfirstlane(done) == 3)
       issue_b(L.lane, c1, nvn, 0, std::integral_constant<int, 32>{});
