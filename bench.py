@@ -42,6 +42,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 SCAN_SOURCES = ["chunk_scan.hip", "chunk_scan_bf16.hip", "scan_items.h", "common.h", "kernels.h"]
 CONV_SOURCES = ["conv1d_silu.hip", "common.h", "kernels.h"]
 DECODE_SOURCES = ["decode_step.hip", "common.h", "kernels.h"]
+NORM_SOURCES = ["gated_rmsnorm.hip", "common.h", "kernels.h"]
 
 
 def source_hash(files):
@@ -323,7 +324,9 @@ def oracle_beside(run, all_sample, one_sample, parity=True):
     res = {"value": round(ntok / el, 1), "unit": "tokens/s/layer", "cores": n, "kind": "oracle",
            "sample": f"{desc}, {el:.2f} s wall"}
     if parity:
-        bs = all_sample
+        bs = dict(all_sample)
+        if d.get("seq_idx") is not None and not bs:
+            bs["seqs"] = w.num_seqs       # a packed stream: the whole-sequence sample
         if "seqs" in bs:
             T = y.shape[1]
             yg = run.y[:, :T]
@@ -380,35 +383,39 @@ def oracle_decode_beside(dw, rows_all, rows_one):
 
 
 # ---------------------------------------------------------------------------
-def run_decode(args, stream):
-    """Batch-256 decode through 29 layers: HBM GB/s of the whole sweep, one
-    layer's event-timed kernel, and the parity of the first application on
-    16 rows of layer 0 against the oracle."""
-    import numpy as np
-    import torch
-    import oracle
-    from state_space_sequence_ssd_amd import inputs, ssd
-    dev = torch.device("cuda:0")
-    bf = torch.bfloat16
-    dw = inputs.decode_29_layers()
-    layers = []
-    for l in range(dw.layers):
-        dd = inputs.make_decode_small_inputs(dw, seed=4, layer=l)
-        layers.append({
-            "host": dd if l == 0 else None,
-            "xBC": torch.from_numpy(dd["xBC"]).to(dev, bf),
-            "dt": torch.from_numpy(dd["dt"]).to(dev, bf),
-            "conv_state": torch.from_numpy(dd["conv_state"]).to(dev, bf),
-            "conv_w": torch.from_numpy(dd["conv_w"]).to(dev),
-            "A": torch.from_numpy(dd["A"]).to(dev), "D": torch.from_numpy(dd["D"]).to(dev),
-            "dt_bias": torch.from_numpy(dd["dt_bias"]).to(dev),
-            "state": inputs.decode_state_device(dw, 4, l, dev),
-            "y": torch.empty((dw.batch, dw.nheads, dw.headdim), dtype=bf, device=dev)})
-    prow = 16
-    st0 = layers[0]["state"][:prow].cpu().numpy()
+class DecodeRun:
+    """Batch-256 decode through 29 layers, inputs resident on the device:
+    HBM GB/s of the whole sweep, one layer's event-timed kernel, and the
+    parity of the first application on 16 rows of layer 0 against the oracle."""
 
-    def dstep(ev=None):
-        for li, L_ in enumerate(layers):
+    PROW = 16
+
+    def __init__(self):
+        import torch
+        from state_space_sequence_ssd_amd import inputs
+        dev = torch.device("cuda:0")
+        bf = torch.bfloat16
+        self.dw = dw = inputs.decode_29_layers()
+        self.layers = []
+        for l in range(dw.layers):
+            dd = inputs.make_decode_small_inputs(dw, seed=4, layer=l)
+            self.layers.append({
+                "xBC": torch.from_numpy(dd["xBC"]).to(dev, bf),
+                "dt": torch.from_numpy(dd["dt"]).to(dev, bf),
+                "conv_state": torch.from_numpy(dd["conv_state"]).to(dev, bf),
+                "conv_w": torch.from_numpy(dd["conv_w"]).to(dev),
+                "A": torch.from_numpy(dd["A"]).to(dev), "D": torch.from_numpy(dd["D"]).to(dev),
+                "dt_bias": torch.from_numpy(dd["dt_bias"]).to(dev),
+                "state": inputs.decode_state_device(dw, 4, l, dev),
+                "y": torch.empty((dw.batch, dw.nheads, dw.headdim), dtype=bf, device=dev)})
+            if l == 0:
+                self.host0 = dd
+        self.st0 = self.layers[0]["state"][:self.PROW].cpu().numpy()
+
+    def dstep(self, stream, ev=None):
+        from state_space_sequence_ssd_amd import ssd
+        dw = self.dw
+        for li, L_ in enumerate(self.layers):
             if ev is not None and li == 0:
                 ev[0].record(stream)
             ssd.ssd_decode_step(L_["xBC"], L_["dt"], L_["A"], L_["state"], dw.nheads, dw.ngroups,
@@ -417,42 +424,48 @@ def run_decode(args, stream):
             if ev is not None and li == 0:
                 ev[1].record(stream)
 
-    dstep()
-    torch.cuda.synchronize()
-    y_first = layers[0]["y"][:prow].float().cpu().numpy()
-    s_first = layers[0]["state"][:prow].cpu().numpy()
-    for _ in range(2):
-        dstep()
-    torch.cuda.synchronize()
-    devs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.decode_steps)]
-    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    d0.record(stream)
-    for i in range(args.decode_steps):
-        dstep(devs[i])
-    d1.record(stream)
-    torch.cuda.synchronize()
-    dms = d0.elapsed_time(d1) / args.decode_steps
-    one_layer_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in devs]))
-    dbytes = decode_algorithmic_bytes(dw)
-    gbs = dbytes * dw.layers / (dms * 1e-3) / 1e9
-    h = layers[0]["host"]
-    del layers
-    torch.cuda.empty_cache()
-    ry, rs, _ = oracle.decode_step(h["xBC"][:prow], h["dt"][:prow], h["dt_bias"], h["A"], h["D"], st0,
-                                   dw.nheads, dw.headdim, dw.dstate, dw.ngroups, conv_w=h["conv_w"],
-                                   conv_state=h["conv_state"][:prow])
-    out = {"metric": "decode-step HBM GB/s", "value": round(gbs, 1), "unit": "GB/s",
-           "frac": round(gbs / HBM_PEAK_GBS, 4), "ms_per_29_layers": round(dms, 4),
-           "tokens_per_s": round(dw.batch / (dms * 1e-3), 1),
-           "layer_kernel_avg_ms": round(one_layer_ms, 4),
-           "layer_kernel_gbs": round(dbytes / (one_layer_ms * 1e-3) / 1e9, 1),
-           "algorithmic_bytes_per_layer": dbytes,
-           "traffic": read_traffic("decode_step_b256_h128", DECODE_SOURCES),
-           "workload": dw.name,
-           "parity": {"y_rel_err": float(f"{rel_err(y_first, ry):.3e}"),
-                      "state_rel_err": float(f"{rel_err(s_first, rs):.3e}"), "bar": 2e-2,
-                      "sample": f"layer 0, batch rows 0..{prow - 1}, first application"}}
-    return out
+    def timed(self, args, stream):
+        import numpy as np
+        import torch
+        dw, prow = self.dw, self.PROW
+        self.dstep(stream)
+        torch.cuda.synchronize()
+        self.y_first = self.layers[0]["y"][:prow].float().cpu().numpy()
+        self.s_first = self.layers[0]["state"][:prow].cpu().numpy()
+        for _ in range(2):
+            self.dstep(stream)
+        torch.cuda.synchronize()
+        devs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.decode_steps)]
+        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        d0.record(stream)
+        for i in range(args.decode_steps):
+            self.dstep(stream, devs[i])
+        d1.record(stream)
+        torch.cuda.synchronize()
+        dms = d0.elapsed_time(d1) / args.decode_steps
+        one_layer_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in devs]))
+        dbytes = decode_algorithmic_bytes(dw)
+        gbs = dbytes * dw.layers / (dms * 1e-3) / 1e9
+        self.layers = None
+        torch.cuda.empty_cache()
+        return {"metric": "decode-step HBM GB/s", "value": round(gbs, 1), "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "ms_per_29_layers": round(dms, 4),
+                "tokens_per_s": round(dw.batch / (dms * 1e-3), 1),
+                "layer_kernel_avg_ms": round(one_layer_ms, 4),
+                "layer_kernel_gbs": round(dbytes / (one_layer_ms * 1e-3) / 1e9, 1),
+                "algorithmic_bytes_per_layer": dbytes,
+                "traffic": read_traffic("decode_step_b256_h128", DECODE_SOURCES),
+                "workload": dw.name}
+
+    def parity(self):
+        import oracle
+        h, dw, prow = self.host0, self.dw, self.PROW
+        ry, rs, _ = oracle.decode_step(h["xBC"][:prow], h["dt"][:prow], h["dt_bias"], h["A"], h["D"], self.st0,
+                                       dw.nheads, dw.headdim, dw.dstate, dw.ngroups, conv_w=h["conv_w"],
+                                       conv_state=h["conv_state"][:prow])
+        return {"y_rel_err": float(f"{rel_err(self.y_first, ry):.3e}"),
+                "state_rel_err": float(f"{rel_err(self.s_first, rs):.3e}"), "bar": 2e-2,
+                "sample": f"layer 0, batch rows 0..{prow - 1}, first application"}
 
 
 CONFIG_SAMPLES = {
@@ -461,6 +474,65 @@ CONFIG_SAMPLES = {
     "nemotron3_nano_b1_l16384": ({}, {"tokens": 2048}),
     "packed_3b_h40_32seqs": ({}, {"seqs": 2}),
 }
+
+
+def progress(msg):
+    """One line per finished part on stderr (the JSON line alone goes to stdout)."""
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
+class NormRun:
+    """The gated RMSNorm after the scan at the headline shape: y is the scan's
+    output tensor, z the gate half of a synthetic in-projection output."""
+
+    def __init__(self, w, y):
+        import torch
+        from state_space_sequence_ssd_amd import inputs
+        dev = torch.device("cuda:0")
+        self.w, self.y = w, y
+        CH = w.nheads * w.headdim
+        self.gs = CH // w.ngroups
+        d = inputs.norm_inputs(w.batch, w.seqlen, CH, seed=1)
+        self.z = torch.from_numpy(d["z"]).to(dev, y.dtype)
+        self.wt = torch.from_numpy(d["w"]).to(dev)
+        self.z_host, self.w_host = d["z"], d["w"]
+        self.out = torch.empty((w.batch, w.seqlen, CH), dtype=y.dtype, device=dev)
+
+    def step(self):
+        from state_space_sequence_ssd_amd import ssd
+        ssd.ssd_gated_rmsnorm(self.y, self.wt, self.gs, z=self.z, out=self.out)
+
+    def timed(self, steps, warmup, stream):
+        import numpy as np
+        import torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for e in evs:
+            e[0].record(stream)
+            self.step()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        w = self.w
+        T, CH = w.batch * w.seqlen, w.nheads * w.headdim
+        nbytes = 3 * T * CH * 2 + CH * 4          # y, z, out (bf16), weights
+        return {"avg_ms": round(ms, 5), "algorithmic_bytes": nbytes,
+                "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "tokens_per_s": round(T / (ms * 1e-3), 1), "group_size": self.gs,
+                "gate": "after (y * SiLU(z), then the norm)",
+                "traffic": read_traffic("gated_rmsnorm_nemotron_h_8b", NORM_SOURCES)}
+
+    def parity(self, rows):
+        """Oracle on the first `rows` token rows of batch row 0 (all channels)."""
+        import oracle
+        yh = self.y[0, :rows].float().cpu().numpy().reshape(rows, -1)
+        ref = oracle.gated_rmsnorm(yh, self.z_host[0, :rows], self.w_host, self.gs)
+        og = self.out[0, :rows].float().cpu().numpy()
+        return {"out_rel_err": float(f"{rel_err(og, ref):.3e}"), "bar": 2e-2,
+                "sample": f"batch row 0, tokens 0..{rows - 1}, all channels"}
 
 
 def main():
@@ -472,6 +544,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing and parity (profiler runs)")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
+    ap.add_argument("--no-norm", action="store_true", help="skip the gated RMSNorm measurement")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other synthetic configs (profiler runs: same kernel names)")
     ap.add_argument("--only", choices=["nemotron_h_8b", "decode", "tiny_fp32", "nemotron3_nano", "packed_3b"],
@@ -498,46 +571,53 @@ def main():
     want = (lambda part: args.only is None or args.only == part)
     cpu_on = not args.no_cpu_baseline
 
-    # ---------------- decode: batch 256 through 29 layers ----------------
-    decode = None
-    if want("decode") and not args.no_decode:
-        decode = run_decode(args, stream)
-
-    # ---------------- the other synthetic configs (parity workloads) ----------------
-    configs = None
+    # Every input is drawn and made resident first; then the timed parts run
+    # back to back (decode, the other configs, the headline step), so the GPU
+    # never idles between them; the oracle runs after all of them.
+    drun = DecodeRun() if want("decode") and not args.no_decode else None
     config_runs = []
     if not args.no_configs or args.only in ("tiny_fp32", "nemotron3_nano", "packed_3b"):
-        configs = {}
         for key, cw, seed in [("tiny_fp32", inputs.tiny_fp32(), 0), ("nemotron3_nano", inputs.nemotron3_nano(), 2),
                               ("packed_3b", inputs.packed_3b(), 3)]:
-            if not want(key):
-                continue
-            run = ScanRun(cw, seed)
-            configs[cw.name] = config_result(run, args.steps, args.warmup)
-            config_runs.append(run)
+            if want(key):
+                config_runs.append(ScanRun(cw, seed))
+    run = ScanRun(inputs.nemotron_h_8b(), seed=1) if want("nemotron_h_8b") else None
+
+    nrun = NormRun(run.w, run.y) if run is not None and not args.no_norm else None
+    progress("inputs resident")
+
+    # ---------------- decode: batch 256 through 29 layers ----------------
+    decode = drun.timed(args, stream) if drun is not None else None
+    if decode is not None:
+        progress(f"decode timed: {decode['value']} GB/s")
+
+    # ---------------- the other synthetic configs (parity workloads) ----------------
+    configs = None if not config_runs else {}
+    for crun in config_runs:
+        configs[crun.w.name] = config_result(crun, args.steps, args.warmup)
+        progress(f"{crun.w.name} timed: scan {configs[crun.w.name]['scan_avg_ms']} ms")
 
     def oracle_configs():
-        # the oracle runs after every GPU measurement, so the GPU never idles
-        # (and its clock never drops) between the timed parts
-        for run in config_runs:
+        for crun in config_runs:
             if cpu_on:
-                a, o = CONFIG_SAMPLES[run.w.name]
-                configs[run.w.name]["cpu_baseline"], configs[run.w.name]["cpu_baseline_single_core"] = \
-                    oracle_beside(run, a, o)
-        if decode is not None and cpu_on:
-            decode["cpu_baseline"], decode["cpu_baseline_single_core"] = oracle_decode_beside(
-                inputs.decode_29_layers(), 128, 16)
+                a, o = CONFIG_SAMPLES[crun.w.name]
+                configs[crun.w.name]["cpu_baseline"], configs[crun.w.name]["cpu_baseline_single_core"] = \
+                    oracle_beside(crun, a, o)
+        if drun is not None and cpu_on:
+            decode["parity"] = drun.parity()
+            decode["cpu_baseline"], decode["cpu_baseline_single_core"] = oracle_decode_beside(drun.dw, 128, 16)
 
-    if not want("nemotron_h_8b"):
+    if run is None:
         oracle_configs()
         print(json.dumps({"only": args.only, "decode": decode, "configs": configs}))
         return
 
     # ---------------- headline: prefill step at the Nemotron-H 8B layer shape ----------------
-    w = inputs.nemotron_h_8b()
-    run = ScanRun(w, seed=1)
+    w = run.w
     H, G, P, N = w.nheads, w.ngroups, w.headdim, w.dstate
     total_ms, conv_ms, scan_ms, wall = run.timed(args.steps, args.warmup)
+    progress(f"headline timed: {total_ms / args.steps:.4f} ms per step")
+    norm = nrun.timed(args.steps, args.warmup, stream) if nrun is not None else None
     ms_per_step = total_ms / args.steps
     tokens = w.batch * w.seqlen
     value = tokens / (ms_per_step / 1e3)
@@ -576,7 +656,10 @@ def main():
     cpu = cpu1 = None
     if cpu_on:
         cpu, cpu1 = oracle_beside(run, {"rows": args.cpu_rows}, {"rows": 1})
+        if norm is not None:
+            norm["parity"] = nrun.parity(512)
     oracle_configs()
+    progress("oracle done")
 
     line = {
         "metric": "SSD scan tokens/s/layer @Nemotron-H-8B shape; decode-step HBM GB/s",
@@ -601,6 +684,7 @@ def main():
         "cpu_baseline_single_core": cpu1,
         "kernels": kernels,
         "decode": decode,
+        "gated_rmsnorm": norm,
         "configs": configs,
         "host": host_info(),
     }

@@ -267,6 +267,45 @@ typedef struct ssd_decode_args {
 
 int ssd_decode_step(const ssd_decode_args *args, void *stream);
 
+/* ------------------------------------------------------------------------
+ * ssd_gated_rmsnorm -- the gated RMSNorm that follows the scan in the
+ * Mamba-2 mixer.
+ *
+ * Passage: Mamba-2 keeps an RMSNorm together with the output gate; the norm
+ * may sit before or after the gate and be taken per group of channels or
+ * over the whole width ("Mamba-3: an inference-first state space model",
+ * the normalization paragraph and the later remark on the norm's placement
+ * and grouped or plain type).
+ *
+ * Per token row and per group of group_size consecutive channels, with
+ * SiLU(u) = u / (1 + e^-u) and rms(v) = sqrt(mean over the group of v^2 + eps):
+ *   norm_before_gate = 0:  g = y * SiLU(z);  out = g / rms(g) * weight
+ *   norm_before_gate = 1:  out = y / rms(y) * weight * SiLU(z)
+ * z may be NULL (no gate).  Arithmetic in fp32; out rounded to the dtype.
+ *
+ *   y, z, out (batch, seqlen, channels), unit channel stride, strides in
+ *   elements for batch and token (z may be a view into the in-projection
+ *   output); weight (channels) fp32 contiguous, required.
+ *
+ * Supported: dtype F32 or BF16; channels a multiple of group_size;
+ * group_size a multiple of 8 (bf16) or 4 (fp32) and at most 8192 (bf16) or
+ * 4096 (fp32); y, z, out
+ * and weight 16-byte aligned, strides multiples of the 16-byte vector;
+ * eps finite and >= 0.  out must not overlap y or z.
+ * ---------------------------------------------------------------------- */
+typedef struct ssd_norm_args {
+  uint32_t struct_size;          /* sizeof(ssd_norm_args) */
+  int32_t dtype;                 /* ssd_dtype of y, z, out */
+  int32_t batch, seqlen, channels, group_size, norm_before_gate;
+  float eps;
+  const void *y;  int64_t y_stride_batch, y_stride_token;
+  const void *z;  int64_t z_stride_batch, z_stride_token;   /* NULL = no gate */
+  const float *weight;
+  void *out;      int64_t out_stride_batch, out_stride_token;
+} ssd_norm_args;
+
+int ssd_gated_rmsnorm(const ssd_norm_args *args, void *stream);
+
 /* Message describing the last error on the calling thread ("" if none). */
 const char *ssd_last_error(void);
 

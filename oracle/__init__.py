@@ -32,7 +32,9 @@ def _load(path: str = LIB):
                                         ip, i, dp, dp, dp]
         lib.oracle_decode_step.argtypes = [i, i, i, i, i, i, dp, dp, dp, dp, dp, dp, dp,
                                            dp, dp, dp]
-        for f in (lib.oracle_conv1d_silu, lib.oracle_ssd_scan, lib.oracle_decode_step):
+        lib.oracle_gated_rmsnorm.argtypes = [i, i, i, i, ctypes.c_double, dp, dp, dp, dp]
+        for f in (lib.oracle_conv1d_silu, lib.oracle_ssd_scan, lib.oracle_decode_step,
+                  lib.oracle_gated_rmsnorm):
             f.restype = ctypes.c_int
         if path != LIB:
             return lib
@@ -137,3 +139,19 @@ def decode_step(xBC, dt_raw, dt_bias, A, D, ssm_state, H, P, N, G, conv_w=None,
     if rc:
         raise ValueError("oracle_decode_step: invalid argument")
     return y, ss, cs
+
+
+def gated_rmsnorm(y, z, w, group_size, norm_before_gate=False, eps=1e-5, lib=None):
+    """y, z (..., CH) (z may be None), w (CH) -> out (..., CH) in float64."""
+    lib = lib or _load()
+    y_, yp = _d(y)
+    z_, zp = _d(z)
+    w_, wp = _d(w)
+    CH = y_.shape[-1]
+    T = int(y_.size // CH) if CH else 0
+    out = np.zeros(y_.shape, np.float64)
+    rc = lib.oracle_gated_rmsnorm(T, CH, int(group_size), int(bool(norm_before_gate)), float(eps),
+                                  yp, zp, wp, out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
+    if rc:
+        raise ValueError("oracle_gated_rmsnorm: invalid argument")
+    return out

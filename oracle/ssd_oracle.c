@@ -272,3 +272,48 @@ int oracle_decode_step(int batch, int H, int P, int N, int G, int K,
     }
     return 0;
 }
+
+/*
+ * Gated RMSNorm of the mixer output.  Mamba-2 keeps an RMSNorm together
+ * with the output gate z; where the norm sits relative to the gate and
+ * whether it is taken per group of channels or over the whole width are
+ * model choices ("Mamba-3: an inference-first state space model": the
+ * normalization paragraph, which keeps Mamba-2's RMSNorm in hybrid models,
+ * and the later remark on the norm's position before or after the gate and
+ * its grouped or plain type).  With SiLU(u) = u / (1 + e^-u) and, for each
+ * token row and each group of group_size consecutive channels,
+ * rms(v) = sqrt(mean over the group of v^2 + eps):
+ *   norm after the gate (norm_before_gate = 0):
+ *       g = y * SiLU(z);   out = g / rms(g) * w
+ *   norm before the gate (norm_before_gate = 1):
+ *       out = y / rms(y) * w * SiLU(z)
+ * z may be NULL (no gate: out = y / rms(y) * w).
+ * Layouts: y, z, out (T, CH) row-major; w (CH); CH a multiple of group_size.
+ */
+int oracle_gated_rmsnorm(int T, int CH, int group_size, int norm_before_gate,
+                         double eps, const double *y, const double *z,
+                         const double *w, double *out) {
+    if (T < 0 || CH < 1 || group_size < 1 || CH % group_size != 0 || eps < 0.0) return -1;
+    const int ngroups = CH / group_size;
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t) {
+        for (int gi = 0; gi < ngroups; ++gi) {
+            const size_t base = (size_t)t * CH + (size_t)gi * group_size;
+            double ss = 0.0;
+            for (int c = 0; c < group_size; ++c) {
+                double v = y[base + c];
+                if (z && !norm_before_gate) v *= silu(z[base + c]);
+                ss += v * v;
+            }
+            const double rms = sqrt(ss / group_size + eps);
+            for (int c = 0; c < group_size; ++c) {
+                double v = y[base + c];
+                if (z && !norm_before_gate) v *= silu(z[base + c]);
+                double o = v / rms * w[(size_t)gi * group_size + c];
+                if (z && norm_before_gate) o *= silu(z[base + c]);
+                out[base + c] = o;
+            }
+        }
+    }
+    return 0;
+}

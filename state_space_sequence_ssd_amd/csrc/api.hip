@@ -259,6 +259,53 @@ int ssd_chunk_scan_fwd_noalloc(const ssd_scan_args *a, void *stream) {
   return ok();
 }
 
+int ssd_gated_rmsnorm(const ssd_norm_args *a, void *stream) {
+  if (!a) return fail(SSD_ERR_INVALID_ARG, "ssd_gated_rmsnorm: args is NULL");
+  if (a->struct_size != sizeof(ssd_norm_args))
+    return fail(SSD_ERR_INVALID_ARG, "ssd_gated_rmsnorm: struct_size %u != %zu", a->struct_size,
+                sizeof(ssd_norm_args));
+  if (a->dtype != SSD_DTYPE_F32 && a->dtype != SSD_DTYPE_BF16)
+    return fail(SSD_ERR_UNSUPPORTED, "ssd_gated_rmsnorm: dtype %d not supported", a->dtype);
+  if (a->batch < 1 || a->seqlen < 0 || a->channels < 1 || a->group_size < 1)
+    return fail(SSD_ERR_INVALID_ARG, "ssd_gated_rmsnorm: non-positive dims (batch %d seqlen %d channels %d group %d)",
+                a->batch, a->seqlen, a->channels, a->group_size);
+  if (a->channels % a->group_size != 0)
+    return fail(SSD_ERR_INVALID_ARG, "ssd_gated_rmsnorm: channels %d not a multiple of group_size %d", a->channels,
+                a->group_size);
+  const int es = dtype_size(a->dtype);
+  const int gmax = es == 2 ? 8192 : 4096;  // 16 vectors of 16 bytes per lane
+  if (a->group_size % (16 / es) != 0 || a->group_size > gmax)
+    return fail(SSD_ERR_UNSUPPORTED, "ssd_gated_rmsnorm: group_size %d must be a multiple of %d and at most %d",
+                a->group_size, 16 / es, gmax);
+  if (!(a->eps >= 0.f) || a->eps > 3.0e38f)
+    return fail(SSD_ERR_INVALID_ARG, "ssd_gated_rmsnorm: eps must be finite and >= 0");
+  if (!a->weight) return fail(SSD_ERR_INVALID_ARG, "ssd_gated_rmsnorm: weight is NULL");
+  if (a->seqlen > 0 && (!a->y || !a->out))
+    return fail(SSD_ERR_INVALID_ARG, "ssd_gated_rmsnorm: y and out are required");
+  if (a->seqlen > 0) {
+    if (!vec_ok(a->y, a->y_stride_batch, a->y_stride_token, es) ||
+        !vec_ok(a->out, a->out_stride_batch, a->out_stride_token, es) ||
+        (a->z && !vec_ok(a->z, a->z_stride_batch, a->z_stride_token, es)) || !aligned16(a->weight))
+      return fail(SSD_ERR_MISALIGNED,
+                  "ssd_gated_rmsnorm: y, z, out, weight need 16-byte aligned bases and strides multiple of %d",
+                  16 / es);
+    if (a->y_stride_token < a->channels || a->out_stride_token < a->channels ||
+        (a->z && a->z_stride_token < a->channels))
+      return fail(SSD_ERR_INVALID_ARG, "ssd_gated_rmsnorm: token strides smaller than channels");
+  }
+  ssd::NormParams p{};
+  p.bf16 = a->dtype == SSD_DTYPE_BF16;
+  p.batch = a->batch; p.L = a->seqlen; p.CH = a->channels; p.gs = a->group_size;
+  p.before = a->norm_before_gate != 0; p.eps = a->eps;
+  p.y = a->y; p.y_sb = a->y_stride_batch; p.y_st = a->y_stride_token;
+  p.z = a->z; p.z_sb = a->z_stride_batch; p.z_st = a->z_stride_token;
+  p.w = a->weight;
+  p.out = a->out; p.o_sb = a->out_stride_batch; p.o_st = a->out_stride_token;
+  const hipError_t e = ssd::launch_gated_rmsnorm(p, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SSD_ERR_HIP, "ssd_gated_rmsnorm: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int ssd_decode_step(const ssd_decode_args *a, void *stream) {
   if (!a) return fail(SSD_ERR_INVALID_ARG, "ssd_decode_step: args is NULL");
   if (a->struct_size != sizeof(ssd_decode_args))

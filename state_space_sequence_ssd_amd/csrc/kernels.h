@@ -38,6 +38,17 @@ struct DecodeParams {
 };
 hipError_t launch_decode_step(const DecodeParams &p, hipStream_t stream);
 
+struct NormParams {
+  int bf16;
+  int batch, L, CH, gs, before;
+  float eps;
+  const void *y; int64_t y_sb, y_st;
+  const void *z; int64_t z_sb, z_st;
+  const float *w;
+  void *out; int64_t o_sb, o_st;
+};
+hipError_t launch_gated_rmsnorm(const NormParams &p, hipStream_t stream);
+
 // Work decomposition of one chunk-scan call.  A work item is one segment of
 // one sequence; each (item, head) pair is one workgroup.
 struct ScanPlan {

@@ -227,3 +227,11 @@ def packed_3b(seed: int = 3) -> ScanWorkload:
 def decode_29_layers() -> DecodeWorkload:
     """Batch-256 decode at the Nemotron-H 8B shape through 29 Mamba-2 layers."""
     return DecodeWorkload("decode_b256_h128_29layers", 256, 128, 8, 29)
+
+
+def norm_inputs(batch: int, seqlen: int, channels: int, seed: int, bf16: bool = True) -> dict:
+    """Inputs of the gated RMSNorm: y and z ~ N(0, 1) (the scan output and the
+    gate half of the in-projection), weight ~ 1 + N(0, 0.01)."""
+    return {"y": normal((batch, seqlen, channels), 1.0, seed, 21, bf16),
+            "z": normal((batch, seqlen, channels), 1.0, seed, 22, bf16),
+            "w": (1.0 + normal((channels,), 0.1, seed, 23, False)).astype(np.float32)}

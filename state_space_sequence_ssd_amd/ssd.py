@@ -57,8 +57,19 @@ class SsdDecodeArgs(ctypes.Structure):
                 ("conv_state", _vp), ("ssm_state", _vp), ("y", _vp), ("y_stride_batch", _i64)]
 
 
+class SsdNormArgs(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("dtype", _i32),
+                ("batch", _i32), ("seqlen", _i32), ("channels", _i32), ("group_size", _i32),
+                ("norm_before_gate", _i32), ("eps", ctypes.c_float),
+                ("y", _vp), ("y_stride_batch", _i64), ("y_stride_token", _i64),
+                ("z", _vp), ("z_stride_batch", _i64), ("z_stride_token", _i64),
+                ("weight", _vp),
+                ("out", _vp), ("out_stride_batch", _i64), ("out_stride_token", _i64)]
+
+
 EXPORTS = ["ssd_conv1d_silu", "ssd_chunk_scan_workspace_size", "ssd_chunk_scan_fwd",
-           "ssd_chunk_scan_fwd_noalloc", "ssd_decode_step", "ssd_last_error", "ssd_version"]
+           "ssd_chunk_scan_fwd_noalloc", "ssd_gated_rmsnorm", "ssd_decode_step", "ssd_last_error",
+           "ssd_version"]
 NOALLOC_SCRATCH_BYTES = 96 * 1024 * 1024   # SSD_NOALLOC_SCRATCH_BYTES
 
 _lib = None
@@ -81,6 +92,8 @@ def load_library(path: str = LIB_PATH):
     lib.ssd_chunk_scan_fwd.restype = ctypes.c_int
     lib.ssd_chunk_scan_fwd_noalloc.argtypes = [ctypes.POINTER(SsdScanArgs), _vp]
     lib.ssd_chunk_scan_fwd_noalloc.restype = ctypes.c_int
+    lib.ssd_gated_rmsnorm.argtypes = [ctypes.POINTER(SsdNormArgs), _vp]
+    lib.ssd_gated_rmsnorm.restype = ctypes.c_int
     lib.ssd_decode_step.argtypes = [ctypes.POINTER(SsdDecodeArgs), _vp]
     lib.ssd_decode_step.restype = ctypes.c_int
     lib.ssd_last_error.argtypes = []
@@ -318,6 +331,55 @@ def ssd_chunk_scan_fwd_noalloc(x: torch.Tensor, dt: torch.Tensor, A: torch.Tenso
                    chunk_size, seg_chunks)
     _check(lib.ssd_chunk_scan_fwd_noalloc(ctypes.byref(a), _stream(stream)))
     return y
+
+
+def _flat3(t: torch.Tensor, name: str):
+    """(batch, seqlen, channels) view of a (batch, seqlen, ..., ) tensor whose
+    trailing dims are packed; returns (tensor3, batch stride, token stride)."""
+    if t.dim() < 3:
+        raise ValueError(f"{name} must be (batch, seqlen, channels...)")
+    inner = 1
+    for d in range(t.dim() - 1, 1, -1):
+        if t.stride(d) != inner:
+            raise ValueError(f"{name}: the channel dims must be packed")
+        inner *= t.shape[d]
+    return t.shape[0], t.shape[1], inner, t.stride(0), t.stride(1)
+
+
+def ssd_gated_rmsnorm(y: torch.Tensor, weight: torch.Tensor, group_size: int,
+                      z: Optional[torch.Tensor] = None, norm_before_gate: bool = False,
+                      eps: float = 1e-5, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Gated RMSNorm of the mixer output.  y, z (batch, seqlen, ...channels),
+    weight (channels) fp32.  Returns out (y's shape, allocated if not given)."""
+    lib = load_library()
+    batch, L, CH, y_sb, y_st = _flat3(y, "y")
+    _dtype_code(y)
+    _same_dtype(y, z=z, out=out)
+    _f32(weight, "weight", numel=CH)
+    if z is not None:
+        zb, zl, zc, z_sb, z_st = _flat3(z, "z")
+        if (zb, zl, zc) != (batch, L, CH):
+            raise ValueError(f"z must match y's (batch, seqlen, channels) = {(batch, L, CH)}")
+    if out is not None:
+        ob, ol, oc, o_sb, o_st = _flat3(out, "out")
+        if (ob, ol, oc) != (batch, L, CH):
+            raise ValueError(f"out must match y's (batch, seqlen, channels) = {(batch, L, CH)}")
+    _on_gpu(y, z=z, weight=weight, out=out)
+    if out is None:
+        out = torch.empty(y.shape, dtype=y.dtype, device=y.device)
+        _, _, _, o_sb, o_st = _flat3(out, "out")
+    a = SsdNormArgs()
+    a.struct_size = ctypes.sizeof(SsdNormArgs)
+    a.dtype = _dtype_code(y)
+    a.batch, a.seqlen, a.channels, a.group_size = batch, L, CH, int(group_size)
+    a.norm_before_gate, a.eps = int(bool(norm_before_gate)), float(eps)
+    a.y, a.y_stride_batch, a.y_stride_token = _ptr(y), y_sb, y_st
+    if z is not None:
+        a.z, a.z_stride_batch, a.z_stride_token = _ptr(z), z_sb, z_st
+    a.weight = _ptr(weight)
+    a.out, a.out_stride_batch, a.out_stride_token = _ptr(out), o_sb, o_st
+    _check(lib.ssd_gated_rmsnorm(ctypes.byref(a), _stream(stream)))
+    return out
 
 
 def ssd_decode_step(xBC: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, ssm_state: torch.Tensor,

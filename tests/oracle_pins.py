@@ -357,4 +357,87 @@ def pin_scalar_golden(lib):
         "golden final state"
 
 
+# ---------------------------------------------------------------------------
+# gated RMSNorm of the mixer output
+# ---------------------------------------------------------------------------
+def _silu(u):
+    from scipy.special import expit
+    return np.asarray(u, np.float64) * expit(np.asarray(u, np.float64))
+
+
+def pin_norm_golden(lib):
+    """One group of two channels, no gate, eps 0: y = (3, 4) has rms
+    sqrt(12.5), so out = (3, 4) sqrt(2) / 5 times the weight; eps = 12.5
+    doubles the mean square (out divided by sqrt 2)."""
+    y = np.array([[3.0, 4.0]])
+    w = np.array([2.0, -1.0])
+    out = oracle.gated_rmsnorm(y, None, w, 2, eps=0.0, lib=lib)
+    assert np.allclose(out, [[6.0 * np.sqrt(2) / 5, -4.0 * np.sqrt(2) / 5]], rtol=1e-15, atol=0)
+    out = oracle.gated_rmsnorm(y, None, w, 2, eps=12.5, lib=lib)
+    assert np.allclose(out, [[6.0 / 5, -4.0 / 5]], rtol=1e-15, atol=0)
+
+
+def pin_norm_unit_rms_per_group(lib):
+    """eps 0, unit weight: every group of the output has mean square 1 and
+    is a positive multiple of its input group (after the gate: of y SiLU(z),
+    with SiLU from scipy's expit); groups are independent of each other."""
+    r = np.random.default_rng(73)
+    T, CH, gs = 5, 48, 12
+    y, z = r.standard_normal((T, CH)), r.standard_normal((T, CH))
+    for gate in (False, True):
+        out = oracle.gated_rmsnorm(y, z if gate else None, np.ones(CH), gs, eps=0.0, lib=lib)
+        v = y * _silu(z) if gate else y
+        for gi in range(CH // gs):
+            sl = slice(gi * gs, (gi + 1) * gs)
+            assert np.allclose(np.mean(out[:, sl] ** 2, axis=1), 1.0, rtol=1e-14, atol=0)
+            ratio = out[:, sl] / v[:, sl]
+            assert np.all(ratio > 0) and np.allclose(ratio, ratio[:, :1], rtol=1e-13, atol=0)
+        # changing one group's input leaves every other group's output unchanged
+        y2 = y.copy()
+        y2[:, :gs] *= 3.7
+        y2[:, gs:2 * gs] = r.standard_normal((T, gs))
+        out2 = oracle.gated_rmsnorm(y2, z if gate else None, np.ones(CH), gs, eps=0.0, lib=lib)
+        assert np.array_equal(out2[:, 2 * gs:], out[:, 2 * gs:])
+        assert np.allclose(out2[:, :gs], out[:, :gs], rtol=1e-13, atol=1e-15)
+
+
+def pin_norm_gate_placement(lib):
+    """Before the gate the output is the plain norm of y times SiLU(z); after
+    the gate a gate that is constant over a group cancels in the norm (eps 0).
+    The weight multiplies channel by channel."""
+    r = np.random.default_rng(79)
+    T, CH, gs = 4, 32, 16
+    y, z = r.standard_normal((T, CH)), r.standard_normal((T, CH))
+    w = r.standard_normal(CH)
+    plain = oracle.gated_rmsnorm(y, None, w, gs, eps=1e-3, lib=lib)
+    before = oracle.gated_rmsnorm(y, z, w, gs, norm_before_gate=True, eps=1e-3, lib=lib)
+    assert np.allclose(before, plain * _silu(z), rtol=1e-14, atol=1e-300)
+    zc = np.repeat(r.standard_normal((T, CH // gs)) + 2.0, gs, axis=1)
+    after = oracle.gated_rmsnorm(y, zc, w, gs, eps=0.0, lib=lib)
+    plain0 = oracle.gated_rmsnorm(y, None, w, gs, eps=0.0, lib=lib)
+    assert np.allclose(after, plain0 * np.sign(_silu(zc)), rtol=1e-13, atol=0)
+    unit = oracle.gated_rmsnorm(y, z, np.ones(CH), gs, eps=1e-3, lib=lib)
+    assert np.allclose(oracle.gated_rmsnorm(y, z, w, gs, eps=1e-3, lib=lib), unit * w[None, :],
+                       rtol=1e-14, atol=1e-300)
+
+
+def pin_norm_scale_and_eps(lib):
+    """eps 0: the output does not change when y is scaled by c > 0 and flips
+    sign with y; a zero input gives zero (no NaN) when eps > 0, and with eps
+    far above the mean square the output tends to y w / sqrt(eps)."""
+    r = np.random.default_rng(83)
+    y, z, w = r.standard_normal((3, 64)), r.standard_normal((3, 64)), r.standard_normal(64)
+    for nbg in (False, True):
+        o = oracle.gated_rmsnorm(y, z, w, 64, norm_before_gate=nbg, eps=0.0, lib=lib)
+        assert np.allclose(oracle.gated_rmsnorm(7.5 * y, z, w, 64, norm_before_gate=nbg, eps=0.0, lib=lib), o,
+                           rtol=1e-14, atol=0)
+        assert np.allclose(oracle.gated_rmsnorm(-y, z, w, 64, norm_before_gate=nbg, eps=0.0, lib=lib), -o,
+                           rtol=1e-15, atol=0)
+    assert np.array_equal(oracle.gated_rmsnorm(np.zeros((2, 8)), None, np.ones(8), 8, eps=1e-6, lib=lib),
+                          np.zeros((2, 8)))
+    small = 1e-6 * y
+    o = oracle.gated_rmsnorm(small, None, w, 64, eps=1e4, lib=lib)
+    assert np.allclose(o, small * w / 100.0, rtol=1e-12, atol=0)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -33,7 +33,7 @@ def test_struct_layouts_match_header(tmp_path):
     """Every ctypes mirror field sits at the offset the C compiler gives it."""
     import subprocess
     structs = {"ssd_conv_args": ssd.SsdConvArgs, "ssd_scan_args": ssd.SsdScanArgs,
-               "ssd_decode_args": ssd.SsdDecodeArgs}
+               "ssd_decode_args": ssd.SsdDecodeArgs, "ssd_norm_args": ssd.SsdNormArgs}
     lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "ssd.h"', "int main(void) {"]
     for cname, py in structs.items():
         lines.append(f'printf("{cname} sizeof %zu\\n", sizeof({cname}));')
@@ -253,3 +253,38 @@ def test_noalloc_rejects_a_workspace_beyond_its_array():
     assert "noalloc" in msg and str(need) in msg
     # argument errors come first, as in ssd_chunk_scan_fwd
     assert lib.ssd_chunk_scan_fwd_noalloc(ctypes.byref(scan_args(ngroups=3)), None) == 1
+
+
+def norm_args(**kw):
+    a = ssd.SsdNormArgs()
+    a.struct_size = ctypes.sizeof(ssd.SsdNormArgs)
+    a.dtype = ssd.SSD_DTYPE_BF16
+    a.batch, a.seqlen, a.channels, a.group_size, a.eps = 4, 4096, 8192, 1024, 1e-5
+    a.y, a.y_stride_batch, a.y_stride_token = FAKE, 4096 * 8192, 8192
+    a.z, a.z_stride_batch, a.z_stride_token = FAKE, 4096 * 18560, 18560
+    a.weight = FAKE
+    a.out, a.out_stride_batch, a.out_stride_token = FAKE, 4096 * 8192, 8192
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("struct_size", 4, 1), ("dtype", 5, 2), ("channels", 1000, 1), ("group_size", 1020, 2),
+    ("group_size", 8200 * 2, 2), ("eps", -1.0, 1), ("eps", float("inf"), 1), ("eps", float("nan"), 1),
+    ("weight", None, 1), ("y", None, 1), ("out", FAKE + 8, 4), ("z_stride_token", 18561, 4),
+    ("y_stride_token", 4096, 1), ("batch", 0, 1),
+])
+def test_norm_argument_errors(field, value, code):
+    lib = ssd.load_library()
+    kw = {field: value}
+    if field == "group_size":
+        kw["channels"] = value * 8
+    assert lib.ssd_gated_rmsnorm(ctypes.byref(norm_args(**kw)), None) == code
+    assert lib.ssd_last_error().decode()
+
+
+def test_norm_fp32_group_limit():
+    lib = ssd.load_library()
+    a = norm_args(dtype=ssd.SSD_DTYPE_F32, group_size=8192, channels=8192)
+    assert lib.ssd_gated_rmsnorm(ctypes.byref(a), None) == 2

@@ -40,6 +40,18 @@ MUTANTS = {
     "decode_no_shift": ("cs[(size_t)r * CH + c] = cs[(size_t)(r + 1) * CH + c];", "(void)0;"),
     "decode_state_transposed": ("S[p * N + n] = a * S[p * N + n] + dt * xv[h * P + p] * Bv[g * N + n];",
                                 "S[p * N + n] = a * S[p * N + n] + dt * xv[h * P + (n % P)] * Bv[g * N + (p % N)];"),
+    "norm_divides_by_width": ("const double rms = sqrt(ss / group_size + eps);",
+                              "const double rms = sqrt(ss / CH + eps);"),
+    "norm_no_sqrt": ("const double rms = sqrt(ss / group_size + eps);",
+                     "const double rms = ss / group_size + eps;"),
+    "norm_eps_outside_sqrt": ("const double rms = sqrt(ss / group_size + eps);",
+                              "const double rms = sqrt(ss / group_size) + eps;"),
+    "norm_weight_group_local": ("double o = v / rms * w[(size_t)gi * group_size + c];",
+                                "double o = v / rms * w[c];"),
+    "norm_gate_ignored_in_rms": ("if (z && !norm_before_gate) v *= silu(z[base + c]);\n                ss += v * v;",
+                                 "ss += v * v;"),
+    "norm_gate_sigmoid_only": ("if (z && norm_before_gate) o *= silu(z[base + c]);",
+                               "if (z && norm_before_gate) o *= silu(z[base + c]) / z[base + c];"),
     "decode_no_D": ("y[((size_t)b * H + h) * P + p] = acc + (D ? D[h] : 0.0) * xv[h * P + p];",
                     "y[((size_t)b * H + h) * P + p] = acc;"),
 }
