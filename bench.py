@@ -72,6 +72,36 @@ def read_traffic(kernel_tag, files):
         return None
 
 
+def read_traffic_all(workload):
+    """Per-kernel HBM bytes per launch of one workload (profiles/traffic_<workload>.txt),
+    keeping only kernels whose source is unchanged since the counters were taken."""
+    path = os.path.join(PROFILES, f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    out, cur = {}, {}
+    sources = {"chunk_scan": SCAN_SOURCES, "plan": SCAN_SOURCES, "combine": SCAN_SOURCES, "conv1d_silu": CONV_SOURCES,
+               "decode_step": DECODE_SOURCES, "gated_rmsnorm": NORM_SOURCES,
+               "decode_mimo": ["decode_mimo.hip", "common.h", "kernels.h"]}
+
+    def flush():
+        t = cur.get("tag")
+        if not t or "hbm_bytes_per_launch" not in cur:
+            return
+        key = next((k for k in sources if t.startswith(k)), None)
+        if key and cur.get("kernel_source_sha256") == source_hash(sources[key]):
+            out[t] = float(cur["hbm_bytes_per_launch"])
+
+    for line in open(path):
+        if line.startswith("kernel:"):
+            flush()
+            cur = {}
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            cur[k.strip()] = v.strip()
+    flush()
+    return out or None
+
+
 def scan_algorithmic_bytes(w, with_final=True):
     """Each input / output tensor of the scan moved once (chunk states excluded):
     x, y, B, C, dt per token in the I/O dtype, seq_idx (int32) when packed, the
@@ -217,6 +247,7 @@ def config_result(run, steps, warmup):
         step_ms += conv_ms
     out["layer_tokens_per_s"] = round(tokens / (step_ms * 1e-3), 1)
     out["step_launch_inclusive_ms"] = round(run.launch_inclusive_ms(steps), 5)
+    out["traffic_per_kernel"] = read_traffic_all(w.name)
     return out
 
 
@@ -535,6 +566,67 @@ class NormRun:
                 "sample": f"batch row 0, tokens 0..{rows - 1}, all channels"}
 
 
+def mimo_algorithmic_bytes(dw, R, trap, es=2):
+    """MIMO decode step: state read + written once (fp32), x, B, C, dt, lam, y
+    in the I/O dtype, and with the trapezoidal term the previous-input caches
+    read and rewritten, per-head params."""
+    b, H, G, P, N = dw.batch, dw.nheads, dw.ngroups, dw.headdim, dw.dstate
+    n = 2 * b * H * P * N * 4 + (2 * b * H * P * R + 2 * b * G * N * R + b * H) * es + 3 * H * 4
+    if trap:
+        n += b * H * es + 2 * (b * H * P * R + b * G * N * R) * es
+    return n
+
+
+class MimoRun:
+    """MIMO decode step at the decode workload's shape (batch 256, 128 heads,
+    8 groups, 1 GiB fp32 state): rank 1 and 4, Euler and trapezoidal."""
+
+    VARIANTS = [(1, False), (4, False), (4, True), (8, True)]
+
+    def __init__(self):
+        import torch
+        from state_space_sequence_ssd_amd import inputs
+        dev = torch.device("cuda:0")
+        self.dw = dw = inputs.decode_29_layers()
+        self.state = inputs.decode_state_device(dw, 12, 0, dev)
+        self.t = {}
+        for R, trap in self.VARIANTS:
+            d = inputs.mimo_decode_inputs(dw.batch, dw.nheads, dw.ngroups, R, seed=12)
+            self.t[(R, trap)] = {k: torch.from_numpy(v).to(dev, torch.bfloat16 if k not in ("dt_bias", "A", "D")
+                                                         else None) for k, v in d.items()}
+
+    def timed(self, steps, stream):
+        import numpy as np
+        import torch
+        from state_space_sequence_ssd_amd import ssd
+        out = {}
+        traffic = read_traffic_all("decode_b256_h128") or {}
+        for (R, trap), t in self.t.items():
+            def step():
+                ssd.ssd_decode_step_mimo(t["x"], t["B"], t["C"], t["dt"], t["A"], self.state, dt_bias=t["dt_bias"],
+                                         D=t["D"], trapezoid=trap, lam=t["lam"] if trap else None,
+                                         prev_x=t["prev_x"] if trap else None, prev_B=t["prev_B"] if trap else None)
+            for _ in range(3):
+                step()
+            torch.cuda.synchronize()
+            evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+            for e in evs:
+                e[0].record(stream)
+                step()
+                e[1].record(stream)
+            torch.cuda.synchronize()
+            ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+            nb = mimo_algorithmic_bytes(self.dw, R, trap)
+            out[f"rank{R}_{'trapezoid' if trap else 'euler'}"] = {
+                "avg_ms": round(ms, 4), "algorithmic_bytes": nb, "gbs": round(nb / (ms * 1e-3) / 1e9, 1),
+                "hbm_frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "tokens_per_s": round(self.dw.batch / (ms * 1e-3), 1),
+                "traffic": traffic.get(f"decode_mimo_r{R}_{'trapezoid' if trap else 'euler'}")}
+        self.state = None
+        torch.cuda.empty_cache()
+        return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -545,6 +637,7 @@ def main():
                     help="skip the oracle timing and parity (profiler runs)")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
     ap.add_argument("--no-norm", action="store_true", help="skip the gated RMSNorm measurement")
+    ap.add_argument("--no-mimo", action="store_true", help="skip the MIMO decode measurement")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other synthetic configs (profiler runs: same kernel names)")
     ap.add_argument("--only", choices=["nemotron_h_8b", "decode", "tiny_fp32", "nemotron3_nano", "packed_3b"],
@@ -571,6 +664,16 @@ def main():
     want = (lambda part: args.only is None or args.only == part)
     cpu_on = not args.no_cpu_baseline
 
+    if args.copy_calibration:
+        # a plain 1 GiB device copy, three times: the HBM counters' scale
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
+
     # Every input is drawn and made resident first; then the timed parts run
     # back to back (decode, the other configs, the headline step), so the GPU
     # never idles between them; the oracle runs after all of them.
@@ -584,12 +687,16 @@ def main():
     run = ScanRun(inputs.nemotron_h_8b(), seed=1) if want("nemotron_h_8b") else None
 
     nrun = NormRun(run.w, run.y) if run is not None and not args.no_norm else None
+    mimo_run = MimoRun() if want("decode") and not args.no_decode and not args.no_mimo else None
     progress("inputs resident")
 
     # ---------------- decode: batch 256 through 29 layers ----------------
     decode = drun.timed(args, stream) if drun is not None else None
     if decode is not None:
         progress(f"decode timed: {decode['value']} GB/s")
+    if mimo_run is not None and decode is not None:
+        decode["mimo"] = mimo_run.timed(args.decode_steps, stream)
+        progress("mimo decode timed")
 
     # ---------------- the other synthetic configs (parity workloads) ----------------
     configs = None if not config_runs else {}
@@ -645,13 +752,6 @@ def main():
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom["gbs"] / HBM_PEAK_GBS, 4),
                 "traffic": dom["traffic"]}
 
-    if args.copy_calibration:
-        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
 
     cpu = cpu1 = None
     if cpu_on:

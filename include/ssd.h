@@ -306,6 +306,60 @@ typedef struct ssd_norm_args {
 
 int ssd_gated_rmsnorm(const ssd_norm_args *args, void *stream);
 
+/* ------------------------------------------------------------------------
+ * ssd_decode_step_mimo -- one decode token of the multi-input multi-output
+ * (MIMO) SSM, optionally with an exponential-trapezoidal input term.
+ *
+ * Passage: "Mamba-3: an inference-first state space model" lists the changes
+ * to Mamba-2: a more general recurrence from an exponential-trapezoidal
+ * discretization, and MIMO instead of SISO, whose projection widens B and C
+ * to rank R and adds parallel work to each update at almost no extra decode
+ * latency.  The page states no formulas; this is the plainest reading, which
+ * is the Mamba-2 decode step at R = 1 with the Euler form.  Per head h
+ * (group g = h / (nheads / ngroups)), dt = softplus(dt_raw + dt_bias[h]),
+ * a = exp(dt * A[h]), state S (headdim x dstate):
+ *   trapezoid = 0:  S <- a S + dt X B^T
+ *   trapezoid = 1:  S <- a S + (1 - lam) dt a Xp Bp^T + lam dt X B^T
+ *   Y = S C + D[h] X
+ * X (headdim x rank) is the head's input, B and C (dstate x rank) the
+ * group's; Xp and Bp are the previous token's X and B, held in prev_x and
+ * prev_B and replaced by X and B after the step.  lam per (row, head), NULL
+ * = 1/2 (the trapezoid rule); lam = 1 gives the Euler form.
+ *
+ *   x, y     (batch, nheads, headdim, rank), batch strides in elements
+ *   B, C     (batch, ngroups, dstate, rank), batch strides in elements
+ *   dt, lam  (batch, nheads) raw, batch strides; dt_bias, A, D (nheads) fp32
+ *   ssm_state (batch, nheads, headdim, dstate) fp32 contiguous, in/out
+ *   prev_x (batch, nheads, headdim, rank), prev_B (batch, ngroups, dstate,
+ *   rank): contiguous, dtype of x, in/out; required when trapezoid != 0.
+ * No conv: the MIMO form drops the short convolution (the same page), so x,
+ * B and C are the projections' outputs.  Inputs must not alias outputs.
+ *
+ * Supported: headdim 64, dstate 128, rank 1, 2, 4 or 8, dtype F32 or BF16,
+ * ssm_state 16-byte aligned; nheads / ngroups small enough that the group's
+ * X, previous X and Y (and B, C, Bp) fit in 160 KiB of LDS
+ * (SSD_ERR_UNSUPPORTED beyond).
+ * ---------------------------------------------------------------------- */
+typedef struct ssd_mimo_decode_args {
+  uint32_t struct_size;          /* sizeof(ssd_mimo_decode_args) */
+  int32_t dtype;                 /* ssd_dtype of x, B, C, dt, lam, y, prev_x, prev_B */
+  int32_t batch, nheads, headdim, dstate, ngroups, rank, trapezoid;
+  const void *x;   int64_t x_stride_batch;
+  const void *B;   int64_t B_stride_batch;
+  const void *C;   int64_t C_stride_batch;
+  const void *dt;  int64_t dt_stride_batch;
+  const void *lam; int64_t lam_stride_batch;   /* NULL = 1/2 */
+  const float *dt_bias;          /* (nheads) or NULL */
+  const float *A;                /* (nheads), required */
+  const float *D;                /* (nheads) or NULL */
+  float *ssm_state;
+  void *prev_x;
+  void *prev_B;
+  void *y;         int64_t y_stride_batch;
+} ssd_mimo_decode_args;
+
+int ssd_decode_step_mimo(const ssd_mimo_decode_args *args, void *stream);
+
 /* Message describing the last error on the calling thread ("" if none). */
 const char *ssd_last_error(void);
 

@@ -306,6 +306,53 @@ int ssd_gated_rmsnorm(const ssd_norm_args *a, void *stream) {
   return ok();
 }
 
+int ssd_decode_step_mimo(const ssd_mimo_decode_args *a, void *stream) {
+  if (!a) return fail(SSD_ERR_INVALID_ARG, "ssd_decode_step_mimo: args is NULL");
+  if (a->struct_size != sizeof(ssd_mimo_decode_args))
+    return fail(SSD_ERR_INVALID_ARG, "ssd_decode_step_mimo: struct_size %u != %zu", a->struct_size,
+                sizeof(ssd_mimo_decode_args));
+  if (a->dtype != SSD_DTYPE_F32 && a->dtype != SSD_DTYPE_BF16)
+    return fail(SSD_ERR_UNSUPPORTED, "ssd_decode_step_mimo: dtype %d not supported", a->dtype);
+  if (a->batch < 1 || a->nheads < 1 || a->ngroups < 1)
+    return fail(SSD_ERR_INVALID_ARG, "ssd_decode_step_mimo: non-positive dims");
+  if (a->nheads % a->ngroups != 0)
+    return fail(SSD_ERR_INVALID_ARG, "ssd_decode_step_mimo: nheads %d not a multiple of ngroups %d", a->nheads,
+                a->ngroups);
+  if (a->headdim != ssd::kHeadDim || a->dstate != ssd::kDState)
+    return fail(SSD_ERR_UNSUPPORTED, "ssd_decode_step_mimo: built for headdim 64, dstate 128 (got %d, %d)",
+                a->headdim, a->dstate);
+  if (a->rank != 1 && a->rank != 2 && a->rank != 4 && a->rank != 8)
+    return fail(SSD_ERR_UNSUPPORTED, "ssd_decode_step_mimo: rank %d not in {1, 2, 4, 8}", a->rank);
+  if (!a->x || !a->B || !a->C || !a->dt || !a->A || !a->ssm_state || !a->y)
+    return fail(SSD_ERR_INVALID_ARG, "ssd_decode_step_mimo: x, B, C, dt, A, ssm_state and y are required");
+  if (a->trapezoid && (!a->prev_x || !a->prev_B))
+    return fail(SSD_ERR_INVALID_ARG, "ssd_decode_step_mimo: the trapezoidal form needs prev_x and prev_B");
+  const int hpg = a->nheads / a->ngroups;
+  if (ssd::mimo_lds_bytes(hpg, a->rank, a->trapezoid != 0) > 160 * 1024)
+    return fail(SSD_ERR_UNSUPPORTED, "ssd_decode_step_mimo: nheads / ngroups = %d at rank %d exceeds the LDS of one "
+                "workgroup", hpg, a->rank);
+  if (!aligned16(a->ssm_state)) return fail(SSD_ERR_MISALIGNED, "ssd_decode_step_mimo: ssm_state must be 16-byte aligned");
+  const int64_t R = a->rank;
+  if (a->x_stride_batch < (int64_t)a->nheads * a->headdim * R || a->y_stride_batch < (int64_t)a->nheads * a->headdim * R ||
+      a->B_stride_batch < (int64_t)a->ngroups * a->dstate * R || a->C_stride_batch < (int64_t)a->ngroups * a->dstate * R ||
+      a->dt_stride_batch < a->nheads || (a->lam && a->lam_stride_batch < a->nheads))
+    return fail(SSD_ERR_INVALID_ARG, "ssd_decode_step_mimo: batch strides smaller than the row width");
+  ssd::MimoParams p{};
+  p.bf16 = a->dtype == SSD_DTYPE_BF16;
+  p.batch = a->batch; p.H = a->nheads; p.G = a->ngroups; p.R = a->rank; p.trapezoid = a->trapezoid != 0;
+  p.x = a->x; p.x_sb = a->x_stride_batch;
+  p.B = a->B; p.B_sb = a->B_stride_batch;
+  p.C = a->C; p.C_sb = a->C_stride_batch;
+  p.dt = a->dt; p.dt_sb = a->dt_stride_batch;
+  p.lam = a->lam; p.lam_sb = a->lam_stride_batch;
+  p.dt_bias = a->dt_bias; p.A = a->A; p.D = a->D;
+  p.ssm_state = a->ssm_state; p.prev_x = a->prev_x; p.prev_B = a->prev_B;
+  p.y = a->y; p.y_sb = a->y_stride_batch;
+  const hipError_t e = ssd::launch_decode_mimo(p, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SSD_ERR_HIP, "ssd_decode_step_mimo: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int ssd_decode_step(const ssd_decode_args *a, void *stream) {
   if (!a) return fail(SSD_ERR_INVALID_ARG, "ssd_decode_step: args is NULL");
   if (a->struct_size != sizeof(ssd_decode_args))

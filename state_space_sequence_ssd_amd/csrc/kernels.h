@@ -38,6 +38,22 @@ struct DecodeParams {
 };
 hipError_t launch_decode_step(const DecodeParams &p, hipStream_t stream);
 
+struct MimoParams {
+  int bf16;
+  int batch, H, G, R, trapezoid;
+  const void *x; int64_t x_sb;
+  const void *B; int64_t B_sb;
+  const void *C; int64_t C_sb;
+  const void *dt; int64_t dt_sb;
+  const void *lam; int64_t lam_sb;
+  const float *dt_bias, *A, *D;
+  float *ssm_state;
+  void *prev_x, *prev_B;
+  void *y; int64_t y_sb;
+};
+size_t mimo_lds_bytes(int hpg, int R, bool trapezoid);
+hipError_t launch_decode_mimo(const MimoParams &p, hipStream_t stream);
+
 struct NormParams {
   int bf16;
   int batch, L, CH, gs, before;

@@ -235,3 +235,21 @@ def norm_inputs(batch: int, seqlen: int, channels: int, seed: int, bf16: bool = 
     return {"y": normal((batch, seqlen, channels), 1.0, seed, 21, bf16),
             "z": normal((batch, seqlen, channels), 1.0, seed, 22, bf16),
             "w": (1.0 + normal((channels,), 0.1, seed, 23, False)).astype(np.float32)}
+
+
+def mimo_decode_inputs(batch: int, nheads: int, ngroups: int, rank: int, seed: int, bf16: bool = True) -> dict:
+    """One MIMO decode token: x, previous x ~ N(0, 1) (batch, H, P, R); B, C,
+    previous B ~ N(0, 1/128) (batch, G, N, R); dt_raw ~ N(0, 1); lam ~ U(0, 1);
+    per-head params as for the scan workloads.  The fp32 state is drawn
+    separately (decode_state_host / decode_state_device)."""
+    H, G, P, N, R = nheads, ngroups, HEADDIM, DSTATE, rank
+    out = {"x": normal((batch, H, P, R), 1.0, seed, 51, bf16),
+           "B": normal((batch, G, N, R), 2.0 ** -3.5, seed, 52, bf16),
+           "C": normal((batch, G, N, R), 2.0 ** -3.5, seed, 53, bf16),
+           "dt": normal((batch, H), 1.0, seed, 54, bf16),
+           "prev_x": normal((batch, H, P, R), 1.0, seed, 55, bf16),
+           "prev_B": normal((batch, G, N, R), 2.0 ** -3.5, seed, 56, bf16)}
+    lam = _rng(seed, 57).uniform(0.0, 1.0, size=(batch, H)).astype(np.float32)
+    out["lam"] = bf16_round(lam) if bf16 else lam
+    out["dt_bias"], out["A"], out["D"] = head_params(H, seed)
+    return out

@@ -67,9 +67,20 @@ class SsdNormArgs(ctypes.Structure):
                 ("out", _vp), ("out_stride_batch", _i64), ("out_stride_token", _i64)]
 
 
+class SsdMimoDecodeArgs(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("dtype", _i32),
+                ("batch", _i32), ("nheads", _i32), ("headdim", _i32), ("dstate", _i32),
+                ("ngroups", _i32), ("rank", _i32), ("trapezoid", _i32),
+                ("x", _vp), ("x_stride_batch", _i64), ("B", _vp), ("B_stride_batch", _i64),
+                ("C", _vp), ("C_stride_batch", _i64), ("dt", _vp), ("dt_stride_batch", _i64),
+                ("lam", _vp), ("lam_stride_batch", _i64),
+                ("dt_bias", _vp), ("A", _vp), ("D", _vp), ("ssm_state", _vp),
+                ("prev_x", _vp), ("prev_B", _vp), ("y", _vp), ("y_stride_batch", _i64)]
+
+
 EXPORTS = ["ssd_conv1d_silu", "ssd_chunk_scan_workspace_size", "ssd_chunk_scan_fwd",
-           "ssd_chunk_scan_fwd_noalloc", "ssd_gated_rmsnorm", "ssd_decode_step", "ssd_last_error",
-           "ssd_version"]
+           "ssd_chunk_scan_fwd_noalloc", "ssd_gated_rmsnorm", "ssd_decode_step",
+           "ssd_decode_step_mimo", "ssd_last_error", "ssd_version"]
 NOALLOC_SCRATCH_BYTES = 96 * 1024 * 1024   # SSD_NOALLOC_SCRATCH_BYTES
 
 _lib = None
@@ -94,6 +105,8 @@ def load_library(path: str = LIB_PATH):
     lib.ssd_chunk_scan_fwd_noalloc.restype = ctypes.c_int
     lib.ssd_gated_rmsnorm.argtypes = [ctypes.POINTER(SsdNormArgs), _vp]
     lib.ssd_gated_rmsnorm.restype = ctypes.c_int
+    lib.ssd_decode_step_mimo.argtypes = [ctypes.POINTER(SsdMimoDecodeArgs), _vp]
+    lib.ssd_decode_step_mimo.restype = ctypes.c_int
     lib.ssd_decode_step.argtypes = [ctypes.POINTER(SsdDecodeArgs), _vp]
     lib.ssd_decode_step.restype = ctypes.c_int
     lib.ssd_last_error.argtypes = []
@@ -438,4 +451,65 @@ def ssd_decode_step(xBC: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, ssm_st
     a.ssm_state = _ptr(ssm_state)
     a.y, a.y_stride_batch = _ptr(y), y.stride(0)
     _check(lib.ssd_decode_step(ctypes.byref(a), _stream(stream)))
+    return y
+
+
+def ssd_decode_step_mimo(x: torch.Tensor, B: torch.Tensor, C: torch.Tensor, dt: torch.Tensor,
+                         A: torch.Tensor, ssm_state: torch.Tensor, dt_bias: Optional[torch.Tensor] = None,
+                         D: Optional[torch.Tensor] = None, trapezoid: bool = False,
+                         lam: Optional[torch.Tensor] = None, prev_x: Optional[torch.Tensor] = None,
+                         prev_B: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+                         stream=None) -> torch.Tensor:
+    """One MIMO decode token.  x (batch,H,P,R), B/C (batch,G,N,R), dt (and lam)
+    (batch,H); ssm_state (batch,H,P,N) fp32 updated in place, and with the
+    trapezoidal form prev_x / prev_B replaced by x / B.  Returns y (batch,H,P,R)."""
+    lib = load_library()
+    if x.dim() != 4 or B.dim() != 4 or C.dim() != 4 or dt.dim() != 2:
+        raise ValueError("x (batch,H,P,R), B/C (batch,G,N,R) and dt (batch,H) expected")
+    batch, H, P, R = x.shape
+    G, N = B.shape[1], B.shape[2]
+    _dtype_code(x)
+    _same_dtype(x, B=B, C=C, dt=dt, lam=lam, prev_x=prev_x, prev_B=prev_B, y=y)
+    _shape(B, "B", (batch, G, N, R))
+    _shape(C, "C", (batch, G, N, R))
+    _shape(dt, "dt", (batch, H))
+    _shape(lam, "lam", (batch, H))
+    _shape(y, "y", (batch, H, P, R))
+    _shape(prev_x, "prev_x", (batch, H, P, R))
+    _shape(prev_B, "prev_B", (batch, G, N, R))
+    for name, t in (("x", x), ("B", B), ("C", C), ("y", y)):
+        if t is not None and not t[0].is_contiguous():
+            raise ValueError(f"{name}: each batch row must be contiguous")
+    for name, t in (("dt", dt), ("lam", lam)):
+        if t is not None and t.stride(1) != 1:
+            raise ValueError(f"{name}: rows must be unit-stride")
+    for name, t in (("prev_x", prev_x), ("prev_B", prev_B)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if trapezoid and (prev_x is None or prev_B is None):
+        raise ValueError("the trapezoidal form needs prev_x and prev_B")
+    _f32(ssm_state, "ssm_state", shape=(batch, H, P, N))
+    _f32(A, "A", numel=H)
+    _f32(dt_bias, "dt_bias", numel=H)
+    _f32(D, "D", numel=H)
+    _on_gpu(x, B=B, C=C, dt=dt, lam=lam, A=A, ssm_state=ssm_state, dt_bias=dt_bias, D=D,
+            prev_x=prev_x, prev_B=prev_B, y=y)
+    if y is None:
+        y = torch.empty((batch, H, P, R), dtype=x.dtype, device=x.device)
+    a = SsdMimoDecodeArgs()
+    a.struct_size = ctypes.sizeof(SsdMimoDecodeArgs)
+    a.dtype = _dtype_code(x)
+    a.batch, a.nheads, a.headdim, a.dstate, a.ngroups, a.rank = batch, H, P, N, G, R
+    a.trapezoid = int(bool(trapezoid))
+    a.x, a.x_stride_batch = _ptr(x), x.stride(0)
+    a.B, a.B_stride_batch = _ptr(B), B.stride(0)
+    a.C, a.C_stride_batch = _ptr(C), C.stride(0)
+    a.dt, a.dt_stride_batch = _ptr(dt), dt.stride(0)
+    if lam is not None:
+        a.lam, a.lam_stride_batch = _ptr(lam), lam.stride(0)
+    a.dt_bias, a.A, a.D = _ptr(dt_bias), _ptr(A), _ptr(D)
+    a.ssm_state = _ptr(ssm_state)
+    a.prev_x, a.prev_B = _ptr(prev_x), _ptr(prev_B)
+    a.y, a.y_stride_batch = _ptr(y), y.stride(0)
+    _check(lib.ssd_decode_step_mimo(ctypes.byref(a), _stream(stream)))
     return y

@@ -33,7 +33,8 @@ def test_struct_layouts_match_header(tmp_path):
     """Every ctypes mirror field sits at the offset the C compiler gives it."""
     import subprocess
     structs = {"ssd_conv_args": ssd.SsdConvArgs, "ssd_scan_args": ssd.SsdScanArgs,
-               "ssd_decode_args": ssd.SsdDecodeArgs, "ssd_norm_args": ssd.SsdNormArgs}
+               "ssd_decode_args": ssd.SsdDecodeArgs, "ssd_norm_args": ssd.SsdNormArgs,
+               "ssd_mimo_decode_args": ssd.SsdMimoDecodeArgs}
     lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "ssd.h"', "int main(void) {"]
     for cname, py in structs.items():
         lines.append(f'printf("{cname} sizeof %zu\\n", sizeof({cname}));')
@@ -288,3 +289,39 @@ def test_norm_fp32_group_limit():
     lib = ssd.load_library()
     a = norm_args(dtype=ssd.SSD_DTYPE_F32, group_size=8192, channels=8192)
     assert lib.ssd_gated_rmsnorm(ctypes.byref(a), None) == 2
+
+
+def mimo_args(**kw):
+    a = ssd.SsdMimoDecodeArgs()
+    a.struct_size = ctypes.sizeof(ssd.SsdMimoDecodeArgs)
+    a.dtype = ssd.SSD_DTYPE_BF16
+    a.batch, a.nheads, a.headdim, a.dstate, a.ngroups, a.rank = 4, 16, 64, 128, 4, 4
+    a.x, a.x_stride_batch = FAKE, 16 * 64 * 4
+    a.B, a.B_stride_batch, a.C, a.C_stride_batch = FAKE, 4 * 128 * 4, FAKE, 4 * 128 * 4
+    a.dt, a.dt_stride_batch = FAKE, 16
+    a.A, a.ssm_state, a.y, a.y_stride_batch = FAKE, FAKE, FAKE, 16 * 64 * 4
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("struct_size", 0, 1), ("dtype", 9, 2), ("ngroups", 3, 1), ("headdim", 32, 2), ("rank", 3, 2),
+    ("rank", 16, 2), ("x", None, 1), ("ssm_state", FAKE + 4, 4), ("trapezoid", 1, 1),
+    ("x_stride_batch", 100, 1), ("B_stride_batch", 500, 1),
+])
+def test_mimo_argument_errors(field, value, code):
+    lib = ssd.load_library()
+    assert lib.ssd_decode_step_mimo(ctypes.byref(mimo_args(**{field: value})), None) == code
+    assert lib.ssd_last_error().decode()
+
+
+def test_mimo_lds_limit():
+    """A group's X, previous X and Y must fit one workgroup's LDS: 16 heads per
+    group at rank 8 with the trapezoidal term fit, 64 do not.  The accepted
+    case is stopped by a later check, so no kernel is launched."""
+    lib = ssd.load_library()
+    ok = mimo_args(rank=8, trapezoid=1, prev_x=FAKE, prev_B=FAKE, x_stride_batch=8)
+    assert lib.ssd_decode_step_mimo(ctypes.byref(ok), None) == 1
+    big = mimo_args(nheads=64, ngroups=1, rank=8, trapezoid=1, prev_x=FAKE, prev_B=FAKE)
+    assert lib.ssd_decode_step_mimo(ctypes.byref(big), None) == 2

@@ -1,0 +1,124 @@
+"""MIMO decode step (rank R, Euler or exponential-trapezoidal input term) on
+the GPU vs the fp64 oracle, through the C ABI.
+
+Bars: max|gpu - oracle| / max|oracle| <= 2e-2 (bf16 inputs, fp32 state and
+arithmetic) or 1e-4 (fp32), for y and for the updated state; the previous-
+input caches are copies of the inputs, compared bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from state_space_sequence_ssd_amd import inputs, ssd
+from tests.gpu_helpers import BF, DEV, rel, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+TOL = {True: 2e-2, False: 1e-4}
+
+
+def _run(d, st, H, G, bf16, trap, with_lam=True):
+    dt_ = BF if bf16 else torch.float32
+    state = to_dev(st)
+    px = to_dev(d["prev_x"], dt_) if trap else None
+    pb = to_dev(d["prev_B"], dt_) if trap else None
+    lam = to_dev(d["lam"], dt_) if (trap and with_lam) else None
+    y = ssd.ssd_decode_step_mimo(to_dev(d["x"], dt_), to_dev(d["B"], dt_), to_dev(d["C"], dt_), to_dev(d["dt"], dt_),
+                                 to_dev(d["A"]), state, dt_bias=to_dev(d["dt_bias"]), D=to_dev(d["D"]),
+                                 trapezoid=trap, lam=lam, prev_x=px, prev_B=pb)
+    torch.cuda.synchronize()
+    return y, state, px, pb
+
+
+@pytest.mark.parametrize("R", [1, 2, 4, 8])
+@pytest.mark.parametrize("trap", [False, True])
+@pytest.mark.parametrize("bf16", [True, False])
+def test_mimo_small(R, trap, bf16):
+    batch, H, G = 3, 16, 4
+    print(f"case mimo R={R} trapezoid={trap} bf16={bf16}", flush=True)
+    d = inputs.mimo_decode_inputs(batch, H, G, R, seed=10 * R + trap, bf16=bf16)
+    st = inputs.decode_state_host(inputs.DecodeWorkload("m", batch, H, G, 1), 7, R)
+    y, state, px, pb = _run(d, st, H, G, bf16, trap)
+    ry, rs, rpx, rpb = oracle.decode_step_mimo(d["x"], d["B"], d["C"], d["dt"], d["dt_bias"], d["A"], d["D"], st,
+                                               trapezoid=trap, lam=d["lam"], prev_x=d["prev_x"],
+                                               prev_B=d["prev_B"])
+    ey, es = rel(to_np(y), ry), rel(to_np(state), rs)
+    print(f"  y rel err {ey:.3e}  state rel err {es:.3e}", flush=True)
+    assert ey <= TOL[bf16] and es <= TOL[bf16]
+    if trap:
+        assert np.array_equal(to_np(px), rpx) and np.array_equal(to_np(pb), rpb)
+
+
+def test_mimo_default_lambda_and_group_of_16():
+    """lam NULL (the trapezoid rule) with 16 heads in one group (every wave of
+    the workgroup busy), rank 4, and bf16."""
+    d = inputs.mimo_decode_inputs(2, 16, 1, 4, seed=3)
+    st = inputs.decode_state_host(inputs.DecodeWorkload("m", 2, 16, 1, 1), 3, 0)
+    y, state, _, _ = _run(d, st, 16, 1, True, True, with_lam=False)
+    ry, rs, _, _ = oracle.decode_step_mimo(d["x"], d["B"], d["C"], d["dt"], d["dt_bias"], d["A"], d["D"], st,
+                                           trapezoid=True, lam=None, prev_x=d["prev_x"], prev_B=d["prev_B"])
+    assert rel(to_np(y), ry) <= 2e-2 and rel(to_np(state), rs) <= 2e-2
+
+
+def test_mimo_rank1_euler_matches_mamba2_decode():
+    """Rank 1 with the Euler form against the Mamba-2 decode kernel (no conv)
+    and the oracle: the same recurrence through two kernels."""
+    batch, H, G = 4, 16, 4
+    d = inputs.mimo_decode_inputs(batch, H, G, 1, seed=5)
+    st = inputs.decode_state_host(inputs.DecodeWorkload("m", batch, H, G, 1), 5, 1)
+    y, state, _, _ = _run(d, st, H, G, True, False)
+    xbc = torch.cat([to_dev(d["x"][..., 0].reshape(batch, -1), BF), to_dev(d["B"][..., 0].reshape(batch, -1), BF),
+                     to_dev(d["C"][..., 0].reshape(batch, -1), BF)], dim=1)
+    s2 = to_dev(st)
+    y2 = ssd.ssd_decode_step(xbc, to_dev(d["dt"], BF), to_dev(d["A"]), s2, H, G, dt_bias=to_dev(d["dt_bias"]),
+                             D=to_dev(d["D"]))
+    torch.cuda.synchronize()
+    assert rel(to_np(state), to_np(s2)) <= 1e-6
+    assert rel(to_np(y[..., 0]), to_np(y2)) <= 2e-2
+
+
+def test_mimo_trapezoid_chain():
+    """Six tokens in a row on the GPU, each step's previous-input caches
+    carried on the device, against the oracle's chain."""
+    batch, H, G, R = 2, 8, 2, 2
+    st = inputs.decode_state_host(inputs.DecodeWorkload("m", batch, H, G, 1), 9, 0)
+    state = to_dev(st)
+    d0 = inputs.mimo_decode_inputs(batch, H, G, R, seed=100)
+    px, pb = to_dev(d0["prev_x"], BF), to_dev(d0["prev_B"], BF)
+    rs, rpx, rpb = st.astype(np.float64), d0["prev_x"], d0["prev_B"]
+    for k in range(6):
+        d = inputs.mimo_decode_inputs(batch, H, G, R, seed=200 + k)
+        d["dt_bias"], d["A"], d["D"] = d0["dt_bias"], d0["A"], d0["D"]
+        y = ssd.ssd_decode_step_mimo(to_dev(d["x"], BF), to_dev(d["B"], BF), to_dev(d["C"], BF), to_dev(d["dt"], BF),
+                                     to_dev(d["A"]), state, dt_bias=to_dev(d["dt_bias"]), D=to_dev(d["D"]),
+                                     trapezoid=True, lam=to_dev(d["lam"], BF), prev_x=px, prev_B=pb)
+        ry, rs, rpx, rpb = oracle.decode_step_mimo(d["x"], d["B"], d["C"], d["dt"], d["dt_bias"], d["A"], d["D"],
+                                                   rs, trapezoid=True, lam=d["lam"], prev_x=rpx, prev_B=rpb)
+        torch.cuda.synchronize()
+        assert rel(to_np(y), ry) <= 2e-2, k
+    assert rel(to_np(state), rs) <= 2e-2
+
+
+def test_mimo_full_size_rank4_trapezoid():
+    """Batch 256, 128 heads, 8 groups (the decode workload's shape), rank 4
+    with the trapezoidal term: every row, first application on fresh states."""
+    print("case mimo full size R=4 trapezoid", flush=True)
+    w = inputs.decode_29_layers()
+    d = inputs.mimo_decode_inputs(w.batch, w.nheads, w.ngroups, 4, seed=11)
+    state = inputs.decode_state_device(w, 11, 0, DEV)
+    st0 = state.cpu().numpy()
+    px, pb = to_dev(d["prev_x"], BF), to_dev(d["prev_B"], BF)
+    y = ssd.ssd_decode_step_mimo(to_dev(d["x"], BF), to_dev(d["B"], BF), to_dev(d["C"], BF), to_dev(d["dt"], BF),
+                                 to_dev(d["A"]), state, dt_bias=to_dev(d["dt_bias"]), D=to_dev(d["D"]),
+                                 trapezoid=True, lam=to_dev(d["lam"], BF), prev_x=px, prev_B=pb)
+    torch.cuda.synchronize()
+    yg, sg = to_np(y), state.cpu().numpy()
+    del state
+    torch.cuda.empty_cache()
+    ry, rs, _, _ = oracle.decode_step_mimo(d["x"], d["B"], d["C"], d["dt"], d["dt_bias"], d["A"], d["D"], st0,
+                                           trapezoid=True, lam=d["lam"], prev_x=d["prev_x"], prev_B=d["prev_B"])
+    del st0
+    ey, es = rel(yg, ry), rel(sg, rs)
+    print(f"  y rel err {ey:.3e}  state rel err {es:.3e}", flush=True)
+    assert ey <= 2e-2 and es <= 2e-2
