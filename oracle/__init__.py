@@ -33,8 +33,13 @@ def _load(path: str = LIB):
         lib.oracle_decode_step.argtypes = [i, i, i, i, i, i, dp, dp, dp, dp, dp, dp, dp,
                                            dp, dp, dp]
         lib.oracle_gated_rmsnorm.argtypes = [i, i, i, i, ctypes.c_double, dp, dp, dp, dp]
+        lib.oracle_ssd_scan_bwd.argtypes = [i, i, i, i, i, i, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp,
+                                            dp, dp, dp, dp, dp, dp, dp, dp]
+        lib.oracle_ssd_scan_bwd.restype = ctypes.c_int
+        lib.oracle_decode_step_mimo.argtypes = [i, i, i, i, i, i, i, dp, dp, dp, dp, dp, dp, dp, dp,
+                                                dp, dp, dp, dp]
         for f in (lib.oracle_conv1d_silu, lib.oracle_ssd_scan, lib.oracle_decode_step,
-                  lib.oracle_gated_rmsnorm):
+                  lib.oracle_gated_rmsnorm, lib.oracle_decode_step_mimo):
             f.restype = ctypes.c_int
         if path != LIB:
             return lib
@@ -154,4 +159,66 @@ def gated_rmsnorm(y, z, w, group_size, norm_before_gate=False, eps=1e-5, lib=Non
                                   yp, zp, wp, out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
     if rc:
         raise ValueError("oracle_gated_rmsnorm: invalid argument")
+    return out
+
+
+def decode_step_mimo(x, B, C, dt_raw, dt_bias, A, D, ssm_state, trapezoid=False, lam=None,
+                     prev_x=None, prev_B=None, lib=None):
+    """MIMO decode step.  x (batch,H,P,R), B/C (batch,G,N,R), dt_raw (batch,H),
+    state (batch,H,P,N).  Returns (y (batch,H,P,R), new state, new prev_x,
+    new prev_B) as float64 copies (prev ones None without the trapezoid)."""
+    lib = lib or _load()
+    x_, xp = _d(x)
+    B_, Bp = _d(B)
+    C_, Cp = _d(C)
+    dt_, dtp = _d(dt_raw)
+    l_, lp = _d(lam)
+    db_, dbp = _d(dt_bias)
+    A_, Ap = _d(A)
+    D_, Dp = _d(D)
+    batch, H, P, R = x_.shape
+    G, N = B_.shape[1], B_.shape[2]
+    ss = np.array(ssm_state, dtype=np.float64, copy=True, order="C")
+    px = pb = None
+    pxp = pbp = None
+    if trapezoid:
+        px = np.array(prev_x, dtype=np.float64, copy=True, order="C")
+        pb = np.array(prev_B, dtype=np.float64, copy=True, order="C")
+        pxp = px.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+        pbp = pb.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+    y = np.zeros((batch, H, P, R), np.float64)
+    rc = lib.oracle_decode_step_mimo(batch, H, P, N, G, R, int(bool(trapezoid)), xp, Bp, Cp, dtp, lp, dbp,
+                                     Ap, Dp, ss.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), pxp, pbp,
+                                     y.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
+    if rc:
+        raise ValueError("oracle_decode_step_mimo: invalid argument")
+    return y, ss, px, pb
+
+
+def ssd_scan_bwd(x, dt_raw, dt_bias, A, B, C, D, dy, initial_state=None, d_final_state=None, lib=None):
+    """Gradients of the selective scan (batch rows, no seq_idx) for the loss
+    L = <dy, y> + <d_final_state, final_state>.  Returns a dict with dx,
+    ddt_raw, dB, dC, ddt_bias, dA, dD and dh0 (float64)."""
+    lib = lib or _load()
+    x_, xp = _d(x)
+    dt_, dtp = _d(dt_raw)
+    db_, dbp = _d(dt_bias)
+    A_, Ap = _d(A)
+    B_, Bp = _d(B)
+    C_, Cp = _d(C)
+    D_, Dp = _d(D)
+    h0_, h0p = _d(initial_state)
+    dy_, dyp = _d(dy)
+    df_, dfp = _d(d_final_state)
+    batch, L, H, P = x_.shape
+    G, N = B_.shape[2], B_.shape[3]
+    out = {"dx": np.zeros((batch, L, H, P)), "ddt_raw": np.zeros((batch, L, H)),
+           "dB": np.zeros((batch, L, G, N)), "dC": np.zeros((batch, L, G, N)),
+           "ddt_bias": np.zeros(H), "dA": np.zeros(H), "dD": np.zeros(H), "dh0": np.zeros((batch, H, P, N))}
+    ptr = {k: v.ctypes.data_as(ctypes.POINTER(ctypes.c_double)) for k, v in out.items()}
+    rc = lib.oracle_ssd_scan_bwd(batch, L, H, P, N, G, xp, dtp, dbp, Ap, Bp, Cp, Dp, h0p, dyp, dfp,
+                                 ptr["dx"], ptr["ddt_raw"], ptr["dB"], ptr["dC"], ptr["ddt_bias"], ptr["dA"],
+                                 ptr["dD"], ptr["dh0"])
+    if rc:
+        raise ValueError("oracle_ssd_scan_bwd: invalid argument")
     return out

@@ -317,3 +317,239 @@ int oracle_gated_rmsnorm(int T, int CH, int group_size, int norm_before_gate,
     }
     return 0;
 }
+
+/*
+ * MIMO decode step (Mamba-3's multi-input multi-output SSM, optionally with
+ * an exponential-trapezoidal input term), one token for every batch row.
+ *
+ * "Mamba-3: an inference-first state space model" lists the changes: a more
+ * general recurrence derived from an exponential-trapezoidal
+ * discretization, and MIMO in place of SISO, whose projection widens B and
+ * C to the representation the MIMO SSM needs and adds parallel work to each
+ * update at almost no extra decode cost.  The page gives no formulas; this
+ * is the plainest reading, which reduces to the Mamba-2 step at R = 1 with
+ * the Euler form:
+ *   per head h (group g = h / (H/G)), rank R, state S (P x N):
+ *     dt = softplus(dt_raw + dt_bias[h]),  a = exp(dt A[h])
+ *     Euler:        S <- a S + dt X B^T
+ *     trapezoidal:  S <- a S + (1 - lam) dt a Xp Bp^T + lam dt X B^T
+ *     Y = S C + D[h] X                      (P x R)
+ *   with X (P x R) the head's input, B, C (N x R) the group's, and Xp, Bp the
+ *   previous token's X and B (kept as decode state, then replaced by X, B).
+ *   lam in [0, 1] per (row, head); lam = 1/2 is the trapezoid rule, lam = 1
+ *   the Euler form.  The previous-input term is the rule's weight on the
+ *   left end of the step, carried through the step's decay.
+ * Layouts (row-major, contiguous): x, y, prev_x (batch, H, P, R);
+ * B, C, prev_B (batch, G, N, R); dt_raw, lam (batch, H); state
+ * (batch, H, P, N).  lam NULL = 1/2.  prev_x / prev_B are read and replaced
+ * only when trapezoid != 0.
+ */
+int oracle_decode_step_mimo(int batch, int H, int P, int N, int G, int R, int trapezoid,
+                            const double *x, const double *B, const double *C,
+                            const double *dt_raw, const double *lam,
+                            const double *dt_bias, const double *A, const double *D,
+                            double *ssm_state, double *prev_x, double *prev_B, double *y) {
+    if (batch < 1 || H < 1 || P < 1 || N < 1 || G < 1 || R < 1 || H % G != 0) return -1;
+    if (trapezoid && (!prev_x || !prev_B)) return -1;
+    const int heads_per_group = H / G;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int b = 0; b < batch; ++b) {
+        for (int h = 0; h < H; ++h) {
+            const int g = h / heads_per_group;
+            const double dt = softplus(dt_raw[(size_t)b * H + h] + (dt_bias ? dt_bias[h] : 0.0));
+            const double a = exp(dt * A[h]);
+            const double l = trapezoid ? (lam ? lam[(size_t)b * H + h] : 0.5) : 1.0;
+            const double *X = x + ((size_t)b * H + h) * P * R;
+            const double *Bm = B + ((size_t)b * G + g) * N * R;
+            const double *Cm = C + ((size_t)b * G + g) * N * R;
+            const double *Xp = trapezoid ? prev_x + ((size_t)b * H + h) * P * R : NULL;
+            const double *Bp = trapezoid ? prev_B + ((size_t)b * G + g) * N * R : NULL;
+            double *S = ssm_state + ((size_t)b * H + h) * P * N;
+            for (int p = 0; p < P; ++p) {
+                for (int n = 0; n < N; ++n) {
+                    double cur = 0.0, prev = 0.0;
+                    for (int r = 0; r < R; ++r) {
+                        cur += X[p * R + r] * Bm[n * R + r];
+                        if (trapezoid) prev += Xp[p * R + r] * Bp[n * R + r];
+                    }
+                    S[p * N + n] = a * S[p * N + n] + l * dt * cur + (1.0 - l) * dt * a * prev;
+                }
+                for (int r = 0; r < R; ++r) {
+                    double acc = 0.0;
+                    for (int n = 0; n < N; ++n) acc += S[p * N + n] * Cm[n * R + r];
+                    y[(((size_t)b * H + h) * P + p) * R + r] = acc + (D ? D[h] : 0.0) * X[p * R + r];
+                }
+            }
+        }
+    }
+    if (trapezoid) {
+        /* the new token's inputs become the previous ones (after every read) */
+        memcpy(prev_x, x, sizeof(double) * (size_t)batch * H * P * R);
+        memcpy(prev_B, B, sizeof(double) * (size_t)batch * G * N * R);
+    }
+    return 0;
+}
+
+/*
+ * Backward pass of the selective scan (reverse mode of the recurrence in
+ * oracle_ssd_scan), batch rows only.  The training workload of the same
+ * layer needs the gradients of every input ("Nemotron-H style Hybrid
+ * Mamba-Transformer 3B feasibility study": sec. 3.1, its table row on
+ * forward/backward verification, and the Phase 2 plan of sec. 7).
+ *
+ * Forward, per (row, head), g = h / (H/G):
+ *   dt_t = softplus(z_t), z_t = dt_raw[t] + dt_bias[h],  a_t = exp(dt_t A[h])
+ *   S_t  = a_t S_{t-1} + dt_t x_t B_t^T       (S_{-1} = initial_state or 0)
+ *   y_t  = S_t C_t + D[h] x_t
+ * Given dy (and d_final = dL/dS_{L-1}, or 0), with Gt = dL/dS_t accumulated
+ * from the last token backwards:
+ *   Gt  += dy_t C_t^T
+ *   dC_t += S_t^T dy_t                   dD += dy_t . x_t
+ *   dx_t  = D dy_t + dt_t Gt B_t          dB_t += dt_t Gt^T x_t
+ *   ddt_t = x_t^T Gt B_t + A a_t <Gt, S_{t-1}>
+ *   dA   += dt_t a_t <Gt, S_{t-1}>
+ *   dz_t  = ddt_t sigmoid(z_t)            (d/dz softplus = sigmoid)
+ *   ddt_raw_t = dz_t,  ddt_bias += dz_t
+ *   G_{t-1} = a_t Gt                      dh0 = G_{-1}
+ * dB and dC sum over the heads of a group.  The forward states are
+ * recomputed from checkpoints every 64 tokens (the same operations as the
+ * forward sweep, so S_t is bit-identical to oracle_ssd_scan's).
+ * Outputs (all overwritten): dx (batch,L,H,P), ddt_raw (batch,L,H),
+ * dB, dC (batch,L,G,N), ddt_bias, dA, dD (H), dh0 (batch,H,P,N) or NULL.
+ */
+int oracle_ssd_scan_bwd(int batch, int L, int H, int P, int N, int G,
+                        const double *x, const double *dt_raw,
+                        const double *dt_bias, const double *A,
+                        const double *B, const double *C, const double *D,
+                        const double *initial_state, const double *dy,
+                        const double *d_final,
+                        double *dx, double *ddt_raw, double *dB, double *dC,
+                        double *ddt_bias, double *dA, double *dD, double *dh0) {
+    if (batch < 1 || L < 0 || H < 1 || P < 1 || N < 1 || G < 1 || H % G != 0) return -1;
+    const int heads_per_group = H / G;
+    const int K = 64;                                   /* checkpoint interval */
+    const int nck = (L + K - 1) / K;
+    const size_t PN = (size_t)P * N;
+    memset(dB, 0, sizeof(double) * (size_t)batch * L * G * N);
+    memset(dC, 0, sizeof(double) * (size_t)batch * L * G * N);
+    /* per-(row, head) partial sums, reduced in a fixed order afterwards */
+    double *pdA = (double *)calloc((size_t)batch * H, sizeof(double));
+    double *pdD = (double *)calloc((size_t)batch * H, sizeof(double));
+    double *pdb = (double *)calloc((size_t)batch * H, sizeof(double));
+    /* per-(row, head) dB / dC contributions: (batch, H, L, N) */
+    double *hB = (double *)calloc((size_t)batch * H * L * N, sizeof(double));
+    double *hC = (double *)calloc((size_t)batch * H * L * N, sizeof(double));
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long long unit = 0; unit < (long long)batch * H; ++unit) {
+        const int b = (int)(unit / H), h = (int)(unit % H);
+        const int g = h / heads_per_group;
+        const double bias = dt_bias ? dt_bias[h] : 0.0;
+        const double dsk = D ? D[h] : 0.0;
+        double *ck = (double *)malloc(sizeof(double) * PN * (nck + 1));   /* S before each block */
+        double *blk = (double *)malloc(sizeof(double) * PN * (K + 1));    /* S_{t0-1} .. S_{t0+K-1} */
+        double *Gt = (double *)malloc(sizeof(double) * PN);
+        double *S = (double *)malloc(sizeof(double) * PN);
+        if (initial_state) memcpy(S, initial_state + ((size_t)b * H + h) * PN, sizeof(double) * PN);
+        else memset(S, 0, sizeof(double) * PN);
+        /* forward sweep: checkpoints */
+        for (int t = 0; t < L; ++t) {
+            if (t % K == 0) memcpy(ck + PN * (t / K), S, sizeof(double) * PN);
+            const size_t tok = (size_t)b * L + t;
+            const double dt = softplus(dt_raw[tok * H + h] + bias);
+            const double a = exp(dt * A[h]);
+            const double *xt = x + (tok * H + h) * P, *Bt = B + (tok * G + g) * N;
+            for (int p = 0; p < P; ++p)
+                for (int n = 0; n < N; ++n) S[p * N + n] = a * S[p * N + n] + dt * xt[p] * Bt[n];
+        }
+        if (d_final) memcpy(Gt, d_final + ((size_t)b * H + h) * PN, sizeof(double) * PN);
+        else memset(Gt, 0, sizeof(double) * PN);
+        double accA = 0.0, accD = 0.0, accb = 0.0;
+        for (int c = nck - 1; c >= 0; --c) {
+            const int t0 = c * K, t1 = (t0 + K < L) ? t0 + K : L;
+            /* recompute S_{t0-1} .. S_{t1-1} into blk[0 .. t1-t0] */
+            memcpy(blk, ck + PN * c, sizeof(double) * PN);
+            for (int t = t0; t < t1; ++t) {
+                const size_t tok = (size_t)b * L + t;
+                const double dt = softplus(dt_raw[tok * H + h] + bias);
+                const double a = exp(dt * A[h]);
+                const double *xt = x + (tok * H + h) * P, *Bt = B + (tok * G + g) * N;
+                const double *Sp = blk + PN * (t - t0);
+                double *Sn = blk + PN * (t - t0 + 1);
+                for (int p = 0; p < P; ++p)
+                    for (int n = 0; n < N; ++n) Sn[p * N + n] = a * Sp[p * N + n] + dt * xt[p] * Bt[n];
+            }
+            for (int t = t1 - 1; t >= t0; --t) {
+                const size_t tok = (size_t)b * L + t;
+                const double z = dt_raw[tok * H + h] + bias;
+                const double dt = softplus(z);
+                const double a = exp(dt * A[h]);
+                const double *xt = x + (tok * H + h) * P, *Bt = B + (tok * G + g) * N;
+                const double *Ct = C + (tok * G + g) * N, *dyt = dy + (tok * H + h) * P;
+                const double *St = blk + PN * (t - t0 + 1), *Sp = blk + PN * (t - t0);
+                double *dxt = dx + (tok * H + h) * P;
+                double *hBt = hB + (((size_t)b * H + h) * L + t) * N;
+                double *hCt = hC + (((size_t)b * H + h) * L + t) * N;
+                for (int p = 0; p < P; ++p)
+                    for (int n = 0; n < N; ++n) Gt[p * N + n] += dyt[p] * Ct[n];
+                for (int n = 0; n < N; ++n) {
+                    double s = 0.0;
+                    for (int p = 0; p < P; ++p) s += St[p * N + n] * dyt[p];
+                    hCt[n] = s;
+                }
+                double gs = 0.0, xgb = 0.0;
+                for (int p = 0; p < P; ++p) {
+                    accD += dyt[p] * xt[p];
+                    double gb = 0.0;
+                    for (int n = 0; n < N; ++n) {
+                        gb += Gt[p * N + n] * Bt[n];
+                        gs += Gt[p * N + n] * Sp[p * N + n];
+                    }
+                    dxt[p] = dsk * dyt[p] + dt * gb;
+                    xgb += xt[p] * gb;
+                }
+                for (int n = 0; n < N; ++n) {
+                    double s = 0.0;
+                    for (int p = 0; p < P; ++p) s += Gt[p * N + n] * xt[p];
+                    hBt[n] = dt * s;
+                }
+                const double ddt = xgb + A[h] * a * gs;
+                accA += dt * a * gs;
+                const double dz = ddt / (1.0 + exp(-z));
+                ddt_raw[tok * H + h] = dz;
+                accb += dz;
+                for (size_t e = 0; e < PN; ++e) Gt[e] *= a;
+            }
+        }
+        if (dh0) memcpy(dh0 + ((size_t)b * H + h) * PN, Gt, sizeof(double) * PN);
+        pdA[unit] = accA;
+        pdD[unit] = accD;
+        pdb[unit] = accb;
+        free(ck); free(blk); free(Gt); free(S);
+    }
+    for (int h = 0; h < H; ++h) {
+        double sa = 0.0, sd = 0.0, sb = 0.0;
+        for (int b = 0; b < batch; ++b) {
+            sa += pdA[(size_t)b * H + h];
+            sd += pdD[(size_t)b * H + h];
+            sb += pdb[(size_t)b * H + h];
+        }
+        dA[h] = sa;
+        if (dD) dD[h] = sd;
+        if (ddt_bias) ddt_bias[h] = sb;
+    }
+    /* dB, dC: sum over the heads of each group, in head order */
+#pragma omp parallel for schedule(static)
+    for (long long bt = 0; bt < (long long)batch * L; ++bt) {
+        const int b = (int)(bt / L), t = (int)(bt % L);
+        for (int h = 0; h < H; ++h) {
+            const int g = h / heads_per_group;
+            const double *sB = hB + (((size_t)b * H + h) * L + t) * N;
+            const double *sC = hC + (((size_t)b * H + h) * L + t) * N;
+            double *oB = dB + (((size_t)b * L + t) * G + g) * N;
+            double *oC = dC + (((size_t)b * L + t) * G + g) * N;
+            for (int n = 0; n < N; ++n) { oB[n] += sB[n]; oC[n] += sC[n]; }
+        }
+    }
+    free(pdA); free(pdD); free(pdb); free(hB); free(hC);
+    return 0;
+}

@@ -440,4 +440,215 @@ def pin_norm_scale_and_eps(lib):
     assert np.allclose(o, small * w / 100.0, rtol=1e-12, atol=0)
 
 
+# ---------------------------------------------------------------------------
+# MIMO decode step with the optional exponential-trapezoidal input term
+# ---------------------------------------------------------------------------
+def _mimo_rand(seed, batch, H, P, N, G, R):
+    r = np.random.default_rng(seed)
+    return {"x": r.standard_normal((batch, H, P, R)), "B": r.standard_normal((batch, G, N, R)) / np.sqrt(N),
+            "C": r.standard_normal((batch, G, N, R)) / np.sqrt(N), "dt": r.standard_normal((batch, H)),
+            "dt_bias": r.standard_normal(H) * 0.3 - 1.0, "A": -np.exp(r.uniform(0, np.log(16), H)),
+            "D": r.standard_normal(H), "S": r.standard_normal((batch, H, P, N)),
+            "px": r.standard_normal((batch, H, P, R)), "pB": r.standard_normal((batch, G, N, R)) / np.sqrt(N),
+            "lam": r.uniform(0, 1, (batch, H))}
+
+
+def _siso_decode(lib, x, B, C, dt, d, S):
+    """Mamba-2 decode oracle (no conv) on one-column inputs: x (b,H,P), B/C (b,G,N)."""
+    b, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    xbc = np.concatenate([x.reshape(b, H * P), B.reshape(b, G * N), C.reshape(b, G * N)], axis=1)
+    y, s, _ = oracle.decode_step(xbc, dt, d["dt_bias"], d["A"], d["D"], S, H, P, N, G, lib=lib)
+    return y, s
+
+
+def pin_mimo_rank1_is_mamba2_decode(lib):
+    """Rank 1 with the Euler form is the Mamba-2 decode step (its own oracle,
+    pinned separately)."""
+    d = _mimo_rand(97, 3, 4, 5, 6, 2, 1)
+    y, s, _, _ = oracle.decode_step_mimo(d["x"], d["B"], d["C"], d["dt"], d["dt_bias"], d["A"], d["D"], d["S"],
+                                         lib=lib)
+    ys, ss = _siso_decode(lib, d["x"][..., 0], d["B"][..., 0], d["C"][..., 0], d["dt"], d, d["S"])
+    assert rel_err(y[..., 0], ys) < 1e-13 and rel_err(s, ss) < 1e-14
+
+
+def pin_mimo_superposition_of_siso_steps(lib):
+    """A rank-R Euler step: the new state is the Mamba-2 step on column 0 plus
+    Mamba-2 steps of columns 1..R-1 from a zero state; output column r is
+    the Mamba-2 readout of the new state with C's column r (a step with
+    dt = 0: x enters nothing and nothing decays) plus D x_r."""
+    d = _mimo_rand(101, 2, 4, 3, 5, 2, 3)
+    y, s, _, _ = oracle.decode_step_mimo(d["x"], d["B"], d["C"], d["dt"], d["dt_bias"], d["A"], d["D"], d["S"],
+                                         lib=lib)
+    _, expect = _siso_decode(lib, d["x"][..., 0], d["B"][..., 0], d["C"][..., 0], d["dt"], d, d["S"])
+    for r in (1, 2):
+        _, part = _siso_decode(lib, d["x"][..., r], d["B"][..., r], d["C"][..., r], d["dt"], d,
+                               np.zeros_like(d["S"]))
+        expect = expect + part
+    assert rel_err(s, expect) < 1e-13
+    frozen = np.full_like(d["dt"], -np.inf)
+    for r in range(3):
+        yr, s_same = _siso_decode(lib, np.zeros_like(d["x"][..., r]), d["B"][..., r], d["C"][..., r], frozen,
+                                  d, s)
+        assert np.array_equal(s_same, s)
+        assert rel_err(y[..., r], yr + d["D"][None, :, None] * d["x"][..., r]) < 1e-13
+
+
+def pin_mimo_column_permutation(lib):
+    """Permuting the R columns of X, B and C together permutes Y's columns and
+    leaves the state as it was (also with the trapezoidal term)."""
+    d = _mimo_rand(103, 2, 4, 3, 5, 4, 4)
+    perm = np.array([2, 0, 3, 1])
+    for trap in (False, True):
+        kw = dict(trapezoid=trap, lam=d["lam"], prev_x=d["px"], prev_B=d["pB"]) if trap else {}
+        y, s, px, pb = oracle.decode_step_mimo(d["x"], d["B"], d["C"], d["dt"], d["dt_bias"], d["A"], d["D"],
+                                               d["S"], lib=lib, **kw)
+        kwp = dict(trapezoid=trap, lam=d["lam"], prev_x=d["px"][..., perm], prev_B=d["pB"][..., perm]) \
+            if trap else {}
+        yp, sp, _, _ = oracle.decode_step_mimo(d["x"][..., perm], d["B"][..., perm], d["C"][..., perm], d["dt"],
+                                               d["dt_bias"], d["A"], d["D"], d["S"], lib=lib, **kwp)
+        assert rel_err(yp, y[..., perm]) < 1e-13 and rel_err(sp, s) < 1e-13
+        if trap:
+            assert np.array_equal(px, d["x"]) and np.array_equal(pb, d["B"]), "prev inputs replaced"
+
+
+def pin_trapezoid_limits(lib):
+    """lam = 1 is the Euler form whatever the previous inputs are; lam = 0
+    keeps only the previous inputs, decayed over the step."""
+    d = _mimo_rand(107, 2, 2, 3, 4, 1, 2)
+    ye, se, _, _ = oracle.decode_step_mimo(d["x"], d["B"], d["C"], d["dt"], d["dt_bias"], d["A"], d["D"], d["S"],
+                                           lib=lib)
+    y1, s1, _, _ = oracle.decode_step_mimo(d["x"], d["B"], d["C"], d["dt"], d["dt_bias"], d["A"], d["D"], d["S"],
+                                           trapezoid=True, lam=np.ones_like(d["lam"]), prev_x=d["px"],
+                                           prev_B=d["pB"], lib=lib)
+    assert np.array_equal(s1, se) and np.array_equal(y1, ye)
+    _, s0, _, _ = oracle.decode_step_mimo(d["x"], d["B"], d["C"], d["dt"], d["dt_bias"], d["A"], d["D"], d["S"],
+                                          trapezoid=True, lam=np.zeros_like(d["lam"]), prev_x=d["px"],
+                                          prev_B=d["pB"], lib=lib)
+    dt = softplus(d["dt"] + d["dt_bias"][None, :])
+    a = np.exp(dt * d["A"][None, :])
+    for b in range(2):
+        for h in range(2):
+            expect = a[b, h] * d["S"][b, h] + dt[b, h] * a[b, h] * d["px"][b, h] @ d["pB"][b, 0].T
+            assert rel_err(s0[b, h], expect) < 1e-13
+
+
+def pin_trapezoid_second_order(lib):
+    """Scalar system h' = A h + x(t), x(t) = sin(w t), h(0) = h0, stepped
+    with decode steps of size dt: against the exact solution at T, the
+    trapezoidal rule (lam = 1/2) converges at second order in dt and the
+    Euler form at first order (error ratios near 4 and 2 when dt halves)."""
+    A, w, h0, T = -1.3, 2.0, 0.7, 2.0
+
+    def exact(t):
+        # h(t) = e^{At} h0 + int_0^t e^{A(t-s)} sin(w s) ds
+        integral = (np.exp(A * t) * w + (-A) * np.sin(w * t) - w * np.cos(w * t)) / (A * A + w * w)
+        return np.exp(A * t) * h0 + integral
+
+    def run(n, trap):
+        dt = T / n
+        z = np.log(np.expm1(dt))            # softplus(z) = dt
+        S = np.full((1, 1, 1, 1), h0)
+        px, pb = np.zeros((1, 1, 1, 1)), np.ones((1, 1, 1, 1))
+        for k in range(1, n + 1):
+            xk = np.full((1, 1, 1, 1), np.sin(w * k * dt))
+            if k == 1:
+                px = np.zeros((1, 1, 1, 1))            # x(0) = sin(0) = 0
+            kw = dict(trapezoid=True, lam=np.full((1, 1), 0.5), prev_x=px, prev_B=pb) if trap else {}
+            _, S, px2, pb2 = oracle.decode_step_mimo(xk, np.ones((1, 1, 1, 1)), np.ones((1, 1, 1, 1)),
+                                                     np.full((1, 1), z), np.zeros(1), np.array([A]), None, S,
+                                                     lib=lib, **kw)
+            if trap:
+                px, pb = px2, pb2
+        return abs(S[0, 0, 0, 0] - exact(T))
+
+    et = [run(n, True) for n in (40, 80, 160)]
+    ee = [run(n, False) for n in (40, 80, 160)]
+    for e1, e2 in zip(et, et[1:]):
+        assert 3.6 < e1 / e2 < 4.4, ("trapezoid order", et)
+    for e1, e2 in zip(ee, ee[1:]):
+        assert 1.8 < e1 / e2 < 2.2, ("Euler order", ee)
+    assert et[-1] < ee[-1] / 20
+
+
+# ---------------------------------------------------------------------------
+# backward pass: against finite differences of the forward oracle
+# ---------------------------------------------------------------------------
+_BWD_INPUTS = ("x", "dt", "dt_bias", "A", "B", "C", "D", "h0")
+_BWD_GRAD = {"x": "dx", "dt": "ddt_raw", "dt_bias": "ddt_bias", "A": "dA", "B": "dB", "C": "dC", "D": "dD",
+             "h0": "dh0"}
+
+
+def _bwd_problem(seed, batch, L, H, P, N, G):
+    r = np.random.default_rng(seed)
+    d = {"x": r.standard_normal((batch, L, H, P)), "dt": r.standard_normal((batch, L, H)),
+         "dt_bias": r.standard_normal(H) * 0.5 - 1.0, "A": -np.exp(r.uniform(0, np.log(4), H)),
+         "B": r.standard_normal((batch, L, G, N)) / np.sqrt(N), "C": r.standard_normal((batch, L, G, N)) / np.sqrt(N),
+         "D": r.standard_normal(H), "h0": r.standard_normal((batch, H, P, N)) * 0.5}
+    w = {"dy": r.standard_normal((batch, L, H, P)), "df": r.standard_normal((batch, H, P, N))}
+    return d, w
+
+
+def _loss(lib, d, w):
+    y, fs = oracle.ssd_scan(d["x"], d["dt"], d["dt_bias"], d["A"], d["B"], d["C"], d["D"],
+                            initial_state=d["h0"], want_final_state=True, lib=lib)
+    return float(np.sum(w["dy"] * y) + np.sum(w["df"] * fs))
+
+
+def _grads(lib, d, w):
+    return oracle.ssd_scan_bwd(d["x"], d["dt"], d["dt_bias"], d["A"], d["B"], d["C"], d["D"], w["dy"],
+                               initial_state=d["h0"], d_final_state=w["df"], lib=lib)
+
+
+def pin_backward_finite_differences(lib):
+    """Every gradient entry against a central difference of the forward
+    oracle's loss <dy, y> + <df, final_state> (step 1e-6, fp64)."""
+    d, w = _bwd_problem(109, 2, 7, 4, 3, 5, 2)
+    g = _grads(lib, d, w)
+    eps = 1e-6
+    for k in _BWD_INPUTS:
+        fd = np.zeros_like(d[k])
+        flat = d[k].reshape(-1)
+        for idx in range(flat.size):
+            old = flat[idx]
+            flat[idx] = old + eps
+            lp = _loss(lib, d, w)
+            flat[idx] = old - eps
+            lm = _loss(lib, d, w)
+            flat[idx] = old
+            fd.reshape(-1)[idx] = (lp - lm) / (2 * eps)
+        err = np.max(np.abs(g[_BWD_GRAD[k]] - fd)) / max(np.max(np.abs(fd)), 1e-30)
+        assert err < 1e-6, ("finite difference", k, err)
+
+
+def pin_backward_directional_across_checkpoints(lib):
+    """Sequences longer than the oracle's 64-token checkpoint interval: the
+    gradient's inner product with a random direction of every input at once
+    equals the loss's central difference along it."""
+    d, w = _bwd_problem(113, 2, 150, 2, 3, 4, 1)
+    g = _grads(lib, d, w)
+    r = np.random.default_rng(127)
+    v = {k: r.standard_normal(np.shape(d[k])) for k in _BWD_INPUTS}
+    eps = 1e-6
+    dp = {k: d[k] + eps * v[k] for k in _BWD_INPUTS}
+    dm = {k: d[k] - eps * v[k] for k in _BWD_INPUTS}
+    fd = (_loss(lib, dp, w) - _loss(lib, dm, w)) / (2 * eps)
+    an = sum(float(np.sum(g[_BWD_GRAD[k]] * v[k])) for k in _BWD_INPUTS)
+    assert abs(an - fd) < 1e-6 * max(1.0, abs(fd)), ("directional derivative", an, fd)
+
+
+def pin_backward_linear_parts(lib):
+    """y is linear in x and in h0: the gradients for x and h0 do not change
+    when x or h0 change, and with dy = 0, df = 0 every gradient is zero."""
+    d, w = _bwd_problem(131, 1, 20, 2, 3, 4, 1)
+    g1 = _grads(lib, d, w)
+    d2 = dict(d)
+    d2["x"] = d["x"] * -2.5 + 1.0
+    d2["h0"] = d["h0"] * 3.0
+    g2 = _grads(lib, d2, w)
+    assert rel_err(g2["dx"], g1["dx"]) < 1e-13 and rel_err(g2["dh0"], g1["dh0"]) < 1e-13
+    z = _grads(lib, d, {"dy": np.zeros_like(w["dy"]), "df": np.zeros_like(w["df"])})
+    assert all(np.all(v == 0) for v in z.values())
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -15,16 +15,16 @@ from oracle.build import SRC, build
 from tests.oracle_pins import ALL_PINS
 
 MUTANTS = {
-    "no_decay": ("S[p * N + n] = a * S[p * N + n] + dt * xt[p] * Bt[n];",
-                 "S[p * N + n] = S[p * N + n] + dt * xt[p] * Bt[n];"),
-    "no_dt_input_scale": ("S[p * N + n] = a * S[p * N + n] + dt * xt[p] * Bt[n];",
-                          "S[p * N + n] = a * S[p * N + n] + xt[p] * Bt[n];"),
+    "no_decay": ("S[p * N + n] = a * S[p * N + n] + dt * xt[p] * Bt[n];\n                    acc += S[p * N + n] * Ct[n];",
+                 "S[p * N + n] = S[p * N + n] + dt * xt[p] * Bt[n];\n                    acc += S[p * N + n] * Ct[n];"),
+    "no_dt_input_scale": ("S[p * N + n] = a * S[p * N + n] + dt * xt[p] * Bt[n];\n                    acc += S[p * N + n] * Ct[n];",
+                          "S[p * N + n] = a * S[p * N + n] + xt[p] * Bt[n];\n                    acc += S[p * N + n] * Ct[n];"),
     "no_skip_D": ("yt[p] = acc + d_skip * xt[p];", "yt[p] = acc;"),
     "softplus_is_exp": ("return log1p(exp(z));", "return exp(z);"),
     "softplus_large_drops_z": ("if (z > 30.0) return z + log1p(exp(-z));",
                                "if (z > 30.0) return log1p(exp(-z));"),
-    "decay_sign": ("const double a = exp(dt * A[h]);\n            const double *xt",
-                   "const double a = exp(-dt * A[h]);\n            const double *xt"),
+    "decay_sign": ("const double a = exp(dt * A[h]);\n            const double *xt = x + (tok * H + h) * P;",
+                   "const double a = exp(-dt * A[h]);\n            const double *xt = x + (tok * H + h) * P;"),
     "B_C_swapped": ("const double *Bt = B + (tok * G + g) * N;\n            const double *Ct = C + (tok * G + g) * N;",
                     "const double *Bt = C + (tok * G + g) * N;\n            const double *Ct = B + (tok * G + g) * N;"),
     "group_map_modulo": ("const int g = h / heads_per_group;\n        const size_t row_off",
@@ -32,7 +32,8 @@ MUTANTS = {
     "output_before_update": ("S[p * N + n] = a * S[p * N + n] + dt * xt[p] * Bt[n];\n                    acc += S[p * N + n] * Ct[n];",
                              "acc += S[p * N + n] * Ct[n];\n                    S[p * N + n] = a * S[p * N + n] + dt * xt[p] * Bt[n];"),
     "initial_state_ignored": ("if (initial_state)\n            memcpy(S,", "if (0)\n            memcpy(S,"),
-    "dt_bias_ignored": ("const double bias = dt_bias ? dt_bias[h] : 0.0;", "const double bias = 0.0;"),
+    "dt_bias_ignored": ("const double bias = dt_bias ? dt_bias[h] : 0.0;\n        const double d_skip",
+                        "const double bias = 0.0;\n        const double d_skip"),
     "conv_taps_reversed": ("u += w[(size_t)c * K + k] * v;", "u += w[(size_t)c * K + (K - 1 - k)] * v;"),
     "conv_no_silu": ("os[(size_t)t * CH + c] = silu(u);", "os[(size_t)t * CH + c] = u;"),
     "conv_crosses_sequences": ("if (tau >= start[s]) v = xs[(size_t)tau * CH + c];\n                    else if (st) v = st[(size_t)(tau - start[s] + K - 1) * CH + c];\n                    else v = 0.0;\n                    u +=",
@@ -52,6 +53,20 @@ MUTANTS = {
                                  "ss += v * v;"),
     "norm_gate_sigmoid_only": ("if (z && norm_before_gate) o *= silu(z[base + c]);",
                                "if (z && norm_before_gate) o *= silu(z[base + c]) / z[base + c];"),
+    "mimo_prev_term_not_decayed": ("(1.0 - l) * dt * a * prev;", "(1.0 - l) * dt * prev;"),
+    "mimo_lambda_swapped": ("a * S[p * N + n] + l * dt * cur + (1.0 - l) * dt * a * prev;",
+                            "a * S[p * N + n] + (1.0 - l) * dt * cur + l * dt * a * prev;"),
+    "mimo_prev_not_replaced": ("memcpy(prev_x, x, sizeof(double) * (size_t)batch * H * P * R);", "(void)0;"),
+    "mimo_rank_truncated": ("for (int r = 0; r < R; ++r) {\n                        cur +=",
+                            "for (int r = 0; r < 1; ++r) {\n                        cur +="),
+    "mimo_output_column_zero": ("acc += S[p * N + n] * Cm[n * R + r];", "acc += S[p * N + n] * Cm[n * R];"),
+    "bwd_no_decay_term": ("const double ddt = xgb + A[h] * a * gs;", "const double ddt = xgb;"),
+    "bwd_no_sigmoid": ("const double dz = ddt / (1.0 + exp(-z));", "const double dz = ddt;"),
+    "bwd_decay_uses_new_state": ("gs += Gt[p * N + n] * Sp[p * N + n];", "gs += Gt[p * N + n] * St[p * N + n];"),
+    "bwd_dB_without_dt": ("hBt[n] = dt * s;", "hBt[n] = s;"),
+    "bwd_adjoint_not_decayed": ("for (size_t e = 0; e < PN; ++e) Gt[e] *= a;", "(void)0;"),
+    "bwd_dC_from_adjoint": ("for (int p = 0; p < P; ++p) s += St[p * N + n] * dyt[p];\n                    hCt[n] = s;",
+                            "for (int p = 0; p < P; ++p) s += Gt[p * N + n] * dyt[p];\n                    hCt[n] = s;"),
     "decode_no_D": ("y[((size_t)b * H + h) * P + p] = acc + (D ? D[h] : 0.0) * xv[h * P + p];",
                     "y[((size_t)b * H + h) * P + p] = acc;"),
 }
