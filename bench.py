@@ -627,6 +627,59 @@ class MimoRun:
         return out
 
 
+class BwdRun:
+    """The scan's backward pass at the headline shape (bf16 inputs, fp32
+    arithmetic): gradients of x, dt, B, C, the per-head parameters and the
+    initial state from dy and a final-state gradient."""
+
+    def __init__(self, w):
+        import torch
+        from state_space_sequence_ssd_amd import inputs, ssd
+        dev = torch.device("cuda:0")
+        self.w = w
+        d = inputs.make_scan_inputs(inputs.ScanWorkload(w.name, w.batch, w.seqlen, w.nheads, w.ngroups, bf16=True,
+                                                        conv=False, final_state=True), seed=1)
+        bf = torch.bfloat16
+        self.t = {k: torch.from_numpy(d[k]).to(dev, bf) for k in ("x", "dt", "B", "C")}
+        self.t.update({k: torch.from_numpy(d[k]).to(dev) for k in ("A", "D", "dt_bias")})
+        self.t["dy"] = torch.from_numpy(inputs.normal((w.batch, w.seqlen, w.nheads, w.headdim), 1.0, 1, 61,
+                                                      True)).to(dev, bf)
+        self.t["df"] = torch.from_numpy(inputs.normal((w.batch, w.nheads, w.headdim, w.dstate), 0.1, 1, 62,
+                                                      False)).to(dev)
+        t = self.t
+        self.ws = None
+        g = ssd.ssd_chunk_scan_bwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["dy"], dt_bias=t["dt_bias"],
+                                   D=t["D"], d_final_state=t["df"], want_d_initial_state=True)
+        del g
+
+    def timed(self, steps, warmup, stream):
+        import numpy as np
+        import torch
+        from state_space_sequence_ssd_amd import ssd
+        t, w = self.t, self.w
+
+        def step():
+            return ssd.ssd_chunk_scan_bwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["dy"], dt_bias=t["dt_bias"],
+                                          D=t["D"], d_final_state=t["df"], want_d_initial_state=True)
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for e in evs:
+            e[0].record(stream)
+            step()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        T, H, G, P, N = w.batch * w.seqlen, w.nheads, w.ngroups, w.headdim, w.dstate
+        nbytes = T * (2 * (2 * H * P) + 2 * (2 * G * N) + 2 * H) * 2 + 2 * w.batch * H * P * N * 4
+        return {"avg_ms": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+                "algorithmic_bytes": nbytes, "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "note": "launch-inclusive time of the three backward launches (chunk states, reverse chunks, "
+                        "fixed-order reductions); fp32 arithmetic"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -638,6 +691,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
     ap.add_argument("--no-norm", action="store_true", help="skip the gated RMSNorm measurement")
     ap.add_argument("--no-mimo", action="store_true", help="skip the MIMO decode measurement")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the scan backward measurement")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other synthetic configs (profiler runs: same kernel names)")
     ap.add_argument("--only", choices=["nemotron_h_8b", "decode", "tiny_fp32", "nemotron3_nano", "packed_3b"],
@@ -688,6 +742,7 @@ def main():
 
     nrun = NormRun(run.w, run.y) if run is not None and not args.no_norm else None
     mimo_run = MimoRun() if want("decode") and not args.no_decode and not args.no_mimo else None
+    brun = BwdRun(run.w) if run is not None and not args.no_bwd else None
     progress("inputs resident")
 
     # ---------------- decode: batch 256 through 29 layers ----------------
@@ -725,6 +780,9 @@ def main():
     total_ms, conv_ms, scan_ms, wall = run.timed(args.steps, args.warmup)
     progress(f"headline timed: {total_ms / args.steps:.4f} ms per step")
     norm = nrun.timed(args.steps, args.warmup, stream) if nrun is not None else None
+    bwd = brun.timed(args.steps, min(args.warmup, 3), stream) if brun is not None else None
+    if bwd is not None:
+        progress(f"backward timed: {bwd['avg_ms']} ms")
     ms_per_step = total_ms / args.steps
     tokens = w.batch * w.seqlen
     value = tokens / (ms_per_step / 1e3)
@@ -785,6 +843,7 @@ def main():
         "kernels": kernels,
         "decode": decode,
         "gated_rmsnorm": norm,
+        "scan_backward": bwd,
         "configs": configs,
         "host": host_info(),
     }

@@ -268,6 +268,52 @@ typedef struct ssd_decode_args {
 int ssd_decode_step(const ssd_decode_args *args, void *stream);
 
 /* ------------------------------------------------------------------------
+ * ssd_chunk_scan_bwd -- backward pass of the scan: the gradients of every
+ * input for a loss L with dL/dy = dy (and dL/dfinal_state = d_final_state).
+ *
+ * Passage: the training workload of the layer needs its backward pass
+ * ("Nemotron-H style Hybrid Mamba-Transformer 3B feasibility study", sec. 3.1,
+ * forward/backward verification of the layer; sec. 7, Phase 2).
+ *
+ * Forward (as ssd_chunk_scan_fwd, batch rows only): dt_t = softplus(z_t),
+ * z_t = dt[t] + dt_bias, a_t = exp(dt_t A), S_t = a_t S_{t-1} + dt_t x_t B_t^T,
+ * y_t = S_t C_t + D x_t, S_{-1} = initial_state (or 0).  Outputs:
+ *   dx (batch, seqlen, nheads, headdim), ddt = dL/d(dt raw) (batch, seqlen,
+ *   nheads), dB, dC (batch, seqlen, ngroups, dstate): the dtype of x;
+ *   d_dt_bias, dA, dD (nheads) fp32; d_initial_state (batch, nheads, headdim,
+ *   dstate) fp32 or NULL.  Every output is overwritten.
+ * Inputs x, dt, B, C, dy are contiguous in the layouts above (dy like x).
+ * Arithmetic is fp32 (bf16 inputs widened), in chunks of 32 tokens.
+ *
+ * The workspace (ssd_chunk_scan_bwd_workspace_size bytes, 256-byte aligned)
+ * holds the state entering every chunk and per-head partial sums: about
+ * batch x nheads x (seqlen / 32 x 32 KiB + seqlen x 1 KiB).
+ *
+ * Supported: headdim 64, dstate 128, dtype F32 or BF16, batch rows (no
+ * seq_idx); x, B, C, dy, dt and the states 16-byte aligned.
+ * ---------------------------------------------------------------------- */
+typedef struct ssd_scan_bwd_args {
+  uint32_t struct_size;          /* sizeof(ssd_scan_bwd_args) */
+  int32_t dtype;                 /* ssd_dtype of x, dt, B, C, dy and of dx, ddt, dB, dC */
+  int32_t batch, seqlen, nheads, headdim, dstate, ngroups;
+  const void *x, *dt, *B, *C, *dy;
+  const float *dt_bias;          /* (nheads) or NULL */
+  const float *A;                /* (nheads), required */
+  const float *D;                /* (nheads) or NULL */
+  const float *initial_state;    /* (batch, nheads, headdim, dstate) or NULL */
+  const float *d_final_state;    /* (batch, nheads, headdim, dstate) or NULL (= 0) */
+  void *dx, *ddt, *dB, *dC;
+  float *d_dt_bias;              /* (nheads) or NULL (not written) */
+  float *dA;                     /* (nheads), required */
+  float *dD;                     /* (nheads) or NULL (not written) */
+  float *d_initial_state;        /* (batch, nheads, headdim, dstate) or NULL */
+} ssd_scan_bwd_args;
+
+size_t ssd_chunk_scan_bwd_workspace_size(const ssd_scan_bwd_args *args);
+
+int ssd_chunk_scan_bwd(const ssd_scan_bwd_args *args, void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
  * ssd_gated_rmsnorm -- the gated RMSNorm that follows the scan in the
  * Mamba-2 mixer.
  *

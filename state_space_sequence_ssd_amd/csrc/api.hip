@@ -259,6 +259,62 @@ int ssd_chunk_scan_fwd_noalloc(const ssd_scan_args *a, void *stream) {
   return ok();
 }
 
+static int check_bwd(const ssd_scan_bwd_args *a) {
+  if (!a) return fail(SSD_ERR_INVALID_ARG, "ssd_chunk_scan_bwd: args is NULL");
+  if (a->struct_size != sizeof(ssd_scan_bwd_args))
+    return fail(SSD_ERR_INVALID_ARG, "ssd_chunk_scan_bwd: struct_size %u != %zu", a->struct_size,
+                sizeof(ssd_scan_bwd_args));
+  if (a->dtype != SSD_DTYPE_F32 && a->dtype != SSD_DTYPE_BF16)
+    return fail(SSD_ERR_UNSUPPORTED, "ssd_chunk_scan_bwd: dtype %d not supported", a->dtype);
+  if (a->batch < 1 || a->seqlen < 0 || a->nheads < 1 || a->ngroups < 1)
+    return fail(SSD_ERR_INVALID_ARG, "ssd_chunk_scan_bwd: non-positive dims");
+  if (a->nheads % a->ngroups != 0)
+    return fail(SSD_ERR_INVALID_ARG, "ssd_chunk_scan_bwd: nheads %d not a multiple of ngroups %d", a->nheads,
+                a->ngroups);
+  if (a->headdim != ssd::kHeadDim || a->dstate != ssd::kDState)
+    return fail(SSD_ERR_UNSUPPORTED, "ssd_chunk_scan_bwd: built for headdim 64, dstate 128 (got %d, %d)", a->headdim,
+                a->dstate);
+  if (!a->A || !a->dA) return fail(SSD_ERR_INVALID_ARG, "ssd_chunk_scan_bwd: A and dA are required");
+  if (a->seqlen > 0 && (!a->x || !a->dt || !a->B || !a->C || !a->dy || !a->dx || !a->ddt || !a->dB || !a->dC))
+    return fail(SSD_ERR_INVALID_ARG, "ssd_chunk_scan_bwd: x, dt, B, C, dy, dx, ddt, dB and dC are required");
+  const void *al[] = {a->x, a->B, a->C, a->dy, a->dx, a->dB, a->dC, a->initial_state, a->d_final_state,
+                      a->d_initial_state};
+  for (const void *q : al)
+    if (q && !aligned16(q)) return fail(SSD_ERR_MISALIGNED, "ssd_chunk_scan_bwd: tensors must be 16-byte aligned");
+  return SSD_OK;
+}
+
+size_t ssd_chunk_scan_bwd_workspace_size(const ssd_scan_bwd_args *a) {
+  if (check_bwd(a) != SSD_OK) return (size_t)-1;
+  return ssd::bwd_layout(a->batch, a->seqlen, a->nheads, a->ngroups).bytes;
+}
+
+int ssd_chunk_scan_bwd(const ssd_scan_bwd_args *a, void *workspace, size_t ws_bytes, void *stream) {
+  const int rc = check_bwd(a);
+  if (rc != SSD_OK) return rc;
+  const ssd::BwdLayout w = ssd::bwd_layout(a->batch, a->seqlen, a->nheads, a->ngroups);
+  if (ws_bytes < w.bytes || !workspace)
+    return fail(SSD_ERR_WORKSPACE_TOO_SMALL, "ssd_chunk_scan_bwd: workspace needs %zu bytes, got %zu", w.bytes,
+                ws_bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(SSD_ERR_MISALIGNED, "ssd_chunk_scan_bwd: workspace must be 256-byte aligned");
+  char *ws = reinterpret_cast<char *>(workspace);
+  ssd::BwdParams p{};
+  p.bf16 = a->dtype == SSD_DTYPE_BF16;
+  p.batch = a->batch; p.L = a->seqlen; p.H = a->nheads; p.G = a->ngroups; p.nchunks = w.nchunks;
+  p.x = a->x; p.dt = a->dt; p.B = a->B; p.C = a->C; p.dy = a->dy;
+  p.dt_bias = a->dt_bias; p.A = a->A; p.D = a->D; p.init = a->initial_state; p.dfinal = a->d_final_state;
+  p.dx = a->dx; p.ddt = a->ddt; p.dB = a->dB; p.dC = a->dC;
+  p.ddt_bias = a->d_dt_bias; p.dA = a->dA; p.dD = a->dD; p.dinit = a->d_initial_state;
+  p.ws_states = reinterpret_cast<float *>(ws + w.states_off);
+  p.ws_dB = reinterpret_cast<float *>(ws + w.dB_off);
+  p.ws_dC = reinterpret_cast<float *>(ws + w.dC_off);
+  p.ws_scalars = reinterpret_cast<float *>(ws + w.scalars_off);
+  const hipError_t e = ssd::launch_chunk_scan_bwd(p, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SSD_ERR_HIP, "ssd_chunk_scan_bwd: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int ssd_gated_rmsnorm(const ssd_norm_args *a, void *stream) {
   if (!a) return fail(SSD_ERR_INVALID_ARG, "ssd_gated_rmsnorm: args is NULL");
   if (a->struct_size != sizeof(ssd_norm_args))

@@ -54,6 +54,23 @@ struct MimoParams {
 size_t mimo_lds_bytes(int hpg, int R, bool trapezoid);
 hipError_t launch_decode_mimo(const MimoParams &p, hipStream_t stream);
 
+struct BwdParams {
+  int bf16;
+  int batch, L, H, G, nchunks;
+  const void *x, *dt, *B, *C, *dy;      // contiguous (batch, L, H, P) / (batch, L, H) / (batch, L, G, N)
+  const float *dt_bias, *A, *D, *init, *dfinal;
+  void *dx, *ddt, *dB, *dC;
+  float *ddt_bias, *dA, *dD, *dinit;
+  float *ws_states, *ws_dB, *ws_dC, *ws_scalars;
+};
+struct BwdLayout {
+  int nchunks;
+  size_t states_off, dB_off, dC_off, scalars_off, bytes;
+};
+BwdLayout bwd_layout(int batch, int L, int H, int G);
+size_t bwd_lds_bytes();
+hipError_t launch_chunk_scan_bwd(const BwdParams &p, hipStream_t stream);
+
 struct NormParams {
   int bf16;
   int batch, L, CH, gs, before;

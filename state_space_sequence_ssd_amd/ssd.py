@@ -78,9 +78,19 @@ class SsdMimoDecodeArgs(ctypes.Structure):
                 ("prev_x", _vp), ("prev_B", _vp), ("y", _vp), ("y_stride_batch", _i64)]
 
 
+class SsdScanBwdArgs(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("dtype", _i32),
+                ("batch", _i32), ("seqlen", _i32), ("nheads", _i32), ("headdim", _i32),
+                ("dstate", _i32), ("ngroups", _i32),
+                ("x", _vp), ("dt", _vp), ("B", _vp), ("C", _vp), ("dy", _vp),
+                ("dt_bias", _vp), ("A", _vp), ("D", _vp), ("initial_state", _vp), ("d_final_state", _vp),
+                ("dx", _vp), ("ddt", _vp), ("dB", _vp), ("dC", _vp),
+                ("d_dt_bias", _vp), ("dA", _vp), ("dD", _vp), ("d_initial_state", _vp)]
+
+
 EXPORTS = ["ssd_conv1d_silu", "ssd_chunk_scan_workspace_size", "ssd_chunk_scan_fwd",
-           "ssd_chunk_scan_fwd_noalloc", "ssd_gated_rmsnorm", "ssd_decode_step",
-           "ssd_decode_step_mimo", "ssd_last_error", "ssd_version"]
+           "ssd_chunk_scan_fwd_noalloc", "ssd_chunk_scan_bwd_workspace_size", "ssd_chunk_scan_bwd",
+           "ssd_gated_rmsnorm", "ssd_decode_step", "ssd_decode_step_mimo", "ssd_last_error", "ssd_version"]
 NOALLOC_SCRATCH_BYTES = 96 * 1024 * 1024   # SSD_NOALLOC_SCRATCH_BYTES
 
 _lib = None
@@ -105,6 +115,10 @@ def load_library(path: str = LIB_PATH):
     lib.ssd_chunk_scan_fwd_noalloc.restype = ctypes.c_int
     lib.ssd_gated_rmsnorm.argtypes = [ctypes.POINTER(SsdNormArgs), _vp]
     lib.ssd_gated_rmsnorm.restype = ctypes.c_int
+    lib.ssd_chunk_scan_bwd_workspace_size.argtypes = [ctypes.POINTER(SsdScanBwdArgs)]
+    lib.ssd_chunk_scan_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.ssd_chunk_scan_bwd.argtypes = [ctypes.POINTER(SsdScanBwdArgs), _vp, ctypes.c_size_t, _vp]
+    lib.ssd_chunk_scan_bwd.restype = ctypes.c_int
     lib.ssd_decode_step_mimo.argtypes = [ctypes.POINTER(SsdMimoDecodeArgs), _vp]
     lib.ssd_decode_step_mimo.restype = ctypes.c_int
     lib.ssd_decode_step.argtypes = [ctypes.POINTER(SsdDecodeArgs), _vp]
@@ -513,3 +527,59 @@ def ssd_decode_step_mimo(x: torch.Tensor, B: torch.Tensor, C: torch.Tensor, dt: 
     a.y, a.y_stride_batch = _ptr(y), y.stride(0)
     _check(lib.ssd_decode_step_mimo(ctypes.byref(a), _stream(stream)))
     return y
+
+
+def ssd_chunk_scan_bwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+                       dy: torch.Tensor, dt_bias: Optional[torch.Tensor] = None,
+                       D: Optional[torch.Tensor] = None, initial_state: Optional[torch.Tensor] = None,
+                       d_final_state: Optional[torch.Tensor] = None, want_d_initial_state: bool = False,
+                       workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Backward of ssd_chunk_scan_fwd (batch rows).  Contiguous x, dy
+    (batch,L,H,P), dt (batch,L,H), B, C (batch,L,G,N).  Returns a dict of
+    dx, ddt (w.r.t. dt raw), dB, dC (x's dtype), d_dt_bias, dA, dD (fp32) and
+    d_initial_state (fp32, if asked)."""
+    lib = load_library()
+    if x.dim() != 4 or B.dim() != 4 or C.dim() != 4 or dt.dim() != 3:
+        raise ValueError("x (batch,L,H,P), B/C (batch,L,G,N) and dt (batch,L,H) expected")
+    batch, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    _dtype_code(x)
+    _same_dtype(x, dt=dt, B=B, C=C, dy=dy)
+    _shape(B, "B", (batch, L, G, N))
+    _shape(C, "C", (batch, L, G, N))
+    _shape(dt, "dt", (batch, L, H))
+    _shape(dy, "dy", (batch, L, H, P))
+    for name, t in (("x", x), ("dt", dt), ("B", B), ("C", C), ("dy", dy)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    _f32(A, "A", numel=H)
+    _f32(dt_bias, "dt_bias", numel=H)
+    _f32(D, "D", numel=H)
+    _f32(initial_state, "initial_state", shape=(batch, H, P, N))
+    _f32(d_final_state, "d_final_state", shape=(batch, H, P, N))
+    _on_gpu(x, dt=dt, A=A, B=B, C=C, dy=dy, dt_bias=dt_bias, D=D, initial_state=initial_state,
+            d_final_state=d_final_state, workspace=workspace)
+    dev = x.device
+    out = {"dx": torch.empty_like(x), "ddt": torch.empty_like(dt), "dB": torch.empty_like(B),
+           "dC": torch.empty_like(C), "d_dt_bias": torch.empty(H, device=dev),
+           "dA": torch.empty(H, device=dev), "dD": torch.empty(H, device=dev),
+           "d_initial_state": torch.empty((batch, H, P, N), device=dev) if want_d_initial_state else None}
+    a = SsdScanBwdArgs()
+    a.struct_size = ctypes.sizeof(SsdScanBwdArgs)
+    a.dtype = _dtype_code(x)
+    a.batch, a.seqlen, a.nheads, a.headdim, a.dstate, a.ngroups = batch, L, H, P, N, G
+    a.x, a.dt, a.B, a.C, a.dy = _ptr(x), _ptr(dt), _ptr(B), _ptr(C), _ptr(dy)
+    a.dt_bias, a.A, a.D = _ptr(dt_bias), _ptr(A), _ptr(D)
+    a.initial_state, a.d_final_state = _ptr(initial_state), _ptr(d_final_state)
+    a.dx, a.ddt, a.dB, a.dC = _ptr(out["dx"]), _ptr(out["ddt"]), _ptr(out["dB"]), _ptr(out["dC"])
+    a.d_dt_bias, a.dA, a.dD = _ptr(out["d_dt_bias"]), _ptr(out["dA"]), _ptr(out["dD"])
+    a.d_initial_state = _ptr(out["d_initial_state"])
+    need = lib.ssd_chunk_scan_bwd_workspace_size(ctypes.byref(a))
+    if need == ctypes.c_size_t(-1).value:
+        raise SsdError(1, lib.ssd_last_error().decode())
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if workspace.dtype != torch.uint8 or workspace.numel() < need:
+        raise ValueError(f"workspace must be a uint8 tensor of at least {need} bytes")
+    _check(lib.ssd_chunk_scan_bwd(ctypes.byref(a), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out

@@ -34,7 +34,7 @@ def test_struct_layouts_match_header(tmp_path):
     import subprocess
     structs = {"ssd_conv_args": ssd.SsdConvArgs, "ssd_scan_args": ssd.SsdScanArgs,
                "ssd_decode_args": ssd.SsdDecodeArgs, "ssd_norm_args": ssd.SsdNormArgs,
-               "ssd_mimo_decode_args": ssd.SsdMimoDecodeArgs}
+               "ssd_mimo_decode_args": ssd.SsdMimoDecodeArgs, "ssd_scan_bwd_args": ssd.SsdScanBwdArgs}
     lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "ssd.h"', "int main(void) {"]
     for cname, py in structs.items():
         lines.append(f'printf("{cname} sizeof %zu\\n", sizeof({cname}));')
@@ -325,3 +325,38 @@ def test_mimo_lds_limit():
     assert lib.ssd_decode_step_mimo(ctypes.byref(ok), None) == 1
     big = mimo_args(nheads=64, ngroups=1, rank=8, trapezoid=1, prev_x=FAKE, prev_B=FAKE)
     assert lib.ssd_decode_step_mimo(ctypes.byref(big), None) == 2
+
+
+def bwd_args(**kw):
+    a = ssd.SsdScanBwdArgs()
+    a.struct_size = ctypes.sizeof(ssd.SsdScanBwdArgs)
+    a.dtype = ssd.SSD_DTYPE_BF16
+    a.batch, a.seqlen, a.nheads, a.headdim, a.dstate, a.ngroups = 4, 4096, 128, 64, 128, 8
+    for f in ("x", "dt", "B", "C", "dy", "dx", "ddt", "dB", "dC", "A", "dA"):
+        setattr(a, f, FAKE)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("struct_size", 4, 1), ("dtype", 4, 2), ("ngroups", 3, 1), ("dstate", 64, 2), ("dA", None, 1),
+    ("dy", None, 1), ("dB", FAKE + 8, 4), ("initial_state", FAKE + 4, 4),
+])
+def test_bwd_argument_errors(field, value, code):
+    lib = ssd.load_library()
+    assert lib.ssd_chunk_scan_bwd(ctypes.byref(bwd_args(**{field: value})), FAKE, 1 << 40, None) == code
+
+
+def test_bwd_workspace_layout():
+    """The backward workspace: the state entering every 32-token chunk of every
+    (row, head), per-head dB and dC partials, per-(row, head) scalars, each
+    block 256-byte aligned; a smaller workspace is refused."""
+    lib = ssd.load_library()
+    a = bwd_args(batch=2, seqlen=100, nheads=8, ngroups=2)
+    n = lib.ssd_chunk_scan_bwd_workspace_size(ctypes.byref(a))
+    up = lambda v: -(-v // 256) * 256
+    expect = up(2 * 8 * 4 * 64 * 128 * 4) + 2 * up(2 * 100 * 8 * 128 * 4) + up(2 * 8 * 3 * 4)
+    assert n == expect
+    assert lib.ssd_chunk_scan_bwd(ctypes.byref(a), FAKE, n - 1, None) == 3
+    assert lib.ssd_chunk_scan_bwd(ctypes.byref(a), FAKE + 16, n, None) == 4

@@ -1,0 +1,89 @@
+"""Backward pass of the scan on the GPU vs the fp64 oracle's backward, through
+the C ABI (the oracle's backward is itself pinned by finite differences of the
+forward oracle).
+
+Bars, per gradient tensor: max|gpu - oracle| / max|oracle| <= 1e-4 for fp32
+inputs (fp32 arithmetic), <= 2e-2 for bf16 inputs (bf16 storage of dx, ddt,
+dB, dC; fp32 arithmetic).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from state_space_sequence_ssd_amd import inputs, ssd
+from tests.gpu_helpers import BF, DEV, rel, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+NAMES = [("dx", "dx"), ("ddt", "ddt_raw"), ("dB", "dB"), ("dC", "dC"), ("d_dt_bias", "ddt_bias"), ("dA", "dA"),
+         ("dD", "dD"), ("d_initial_state", "dh0")]
+
+
+def _case(batch, L, H, G, bf16, seed, init=True, dfinal=True, dt_inf_heads=()):
+    w = inputs.ScanWorkload("bwd", batch, L, H, G, bf16=bf16, conv=False, final_state=True,
+                            init_std=0.3 if init else 0.0)
+    d = inputs.make_scan_inputs(w, seed=seed)
+    d["dy"] = inputs.normal((batch, L, H, 64), 1.0, seed, 61, bf16)
+    d["dfinal"] = inputs.normal((batch, H, 64, 128), 0.1, seed, 62, False) if dfinal else None
+    for h in dt_inf_heads:
+        d["dt"][:, :, h] = -np.inf
+    return w, d
+
+
+def _check(w, d, tol):
+    dtp = BF if w.bf16 else torch.float32
+    g = ssd.ssd_chunk_scan_bwd(to_dev(d["x"], dtp), to_dev(d["dt"], dtp), to_dev(d["A"]), to_dev(d["B"], dtp),
+                               to_dev(d["C"], dtp), to_dev(d["dy"], dtp), dt_bias=to_dev(d["dt_bias"]),
+                               D=to_dev(d["D"]),
+                               initial_state=to_dev(d["initial_state"]) if "initial_state" in d else None,
+                               d_final_state=None if d["dfinal"] is None else to_dev(d["dfinal"]),
+                               want_d_initial_state=True)
+    torch.cuda.synchronize()
+    r = oracle.ssd_scan_bwd(d["x"], d["dt"], d["dt_bias"], d["A"], d["B"], d["C"], d["D"], d["dy"],
+                            initial_state=d.get("initial_state"), d_final_state=d["dfinal"])
+    errs = {}
+    for k, rk in NAMES:
+        errs[k] = rel(to_np(g[k]), r[rk])
+    print("  " + "  ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+    for k, v in errs.items():
+        assert np.isfinite(v) and v <= tol, (k, v)
+
+
+@pytest.mark.parametrize("batch,L,H,G,bf16,init,dfinal", [
+    (2, 100, 8, 2, False, True, True),      # three chunks and a ragged tail
+    (1, 33, 4, 4, False, False, False),
+    (3, 1, 4, 1, False, True, True),
+    (2, 64, 16, 4, True, True, True),
+    (1, 257, 8, 8, True, False, True),
+])
+def test_bwd_small(batch, L, H, G, bf16, init, dfinal):
+    print(f"case bwd batch={batch} L={L} H={H} G={G} bf16={bf16} init={init} dfinal={dfinal}", flush=True)
+    w, d = _case(batch, L, H, G, bf16, seed=L + H, init=init, dfinal=dfinal)
+    _check(w, d, 2e-2 if bf16 else 1e-4)
+
+
+def test_bwd_dt_zero_heads():
+    """dt_raw = -inf on two heads (dt = 0, sigmoid(-inf) = 0): their ddt_raw is
+    zero and the rest of the gradients still match."""
+    w, d = _case(2, 70, 8, 2, False, seed=5, dt_inf_heads=(1, 6))
+    _check(w, d, 1e-4)
+
+
+def test_bwd_repeat_runs_bitwise_identical():
+    w, d = _case(2, 90, 8, 2, True, seed=9)
+    args = (to_dev(d["x"], BF), to_dev(d["dt"], BF), to_dev(d["A"]), to_dev(d["B"], BF), to_dev(d["C"], BF),
+            to_dev(d["dy"], BF))
+    g1 = ssd.ssd_chunk_scan_bwd(*args, dt_bias=to_dev(d["dt_bias"]), D=to_dev(d["D"]))
+    g2 = ssd.ssd_chunk_scan_bwd(*args, dt_bias=to_dev(d["dt_bias"]), D=to_dev(d["D"]))
+    torch.cuda.synchronize()
+    for k in ("dx", "ddt", "dB", "dC", "d_dt_bias", "dA", "dD"):
+        assert torch.equal(g1[k], g2[k]), k
+
+
+def test_bwd_full_nemotron_h_8b():
+    """The Nemotron-H 8B scan shape (batch 4 x 4096, 128 heads, 8 groups, bf16):
+    every element of every gradient."""
+    print("case bwd nemotron_h_8b shape (every element)", flush=True)
+    w, d = _case(4, 4096, 128, 8, True, seed=1, init=False, dfinal=True)
+    _check(w, d, 2e-2)
