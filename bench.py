@@ -39,7 +39,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 PROFILES = os.path.join(ROOT, "profiles")
-SCAN_SOURCES = ["chunk_scan.hip", "chunk_scan_bf16.hip", "scan_items.h", "common.h", "kernels.h"]
+SCAN_SOURCES = ["chunk_scan.hip", "chunk_scan_bf16.hip", "quad_scan_f32.hip", "scan_items.h", "common.h", "kernels.h"]
 CONV_SOURCES = ["conv1d_silu.hip", "common.h", "kernels.h"]
 DECODE_SOURCES = ["decode_step.hip", "common.h", "kernels.h"]
 NORM_SOURCES = ["gated_rmsnorm.hip", "common.h", "kernels.h"]
@@ -212,6 +212,43 @@ class ScanRun:
         scan = [e[1].elapsed_time(e[2]) for e in evs]
         return t0.elapsed_time(t1), conv, scan, wall
 
+    def graph_ms(self, steps, replays=3):
+        """GPU time per step with `steps` steps captured in one HIP graph and
+        replayed, so no host work sits between the kernels.  Every replay's y
+        and final states must equal the eager step's bit for bit (the kernels
+        sum in a fixed order); the outputs are cleared by eager work between
+        replays.  Returns the median over `replays` replays."""
+        import numpy as np
+        import torch
+        self.step()
+        torch.cuda.synchronize()
+        y0, fs0 = self.y.clone(), self.fs.clone()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(steps):
+                self.step()
+        times = []
+        for _ in range(replays):
+            self.y.zero_()
+            self.fs.zero_()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b) / steps)
+            if not (torch.equal(self.y, y0) and torch.equal(self.fs, fs0)):
+                raise RuntimeError(f"{self.w.name}: graph replay differs from the eager step")
+        del g
+        return float(np.median(times))
+
     def launch_inclusive_ms(self, steps):
         """Host wall clock per back-to-back call of the whole step."""
         import torch
@@ -247,6 +284,9 @@ def config_result(run, steps, warmup):
         step_ms += conv_ms
     out["layer_tokens_per_s"] = round(tokens / (step_ms * 1e-3), 1)
     out["step_launch_inclusive_ms"] = round(run.launch_inclusive_ms(steps), 5)
+    gms = run.graph_ms(steps)
+    out["step_graph_ms"] = round(gms, 5)
+    out["layer_tokens_per_s_graph"] = round(tokens / (gms * 1e-3), 1)
     out["traffic_per_kernel"] = read_traffic_all(w.name)
     return out
 
@@ -779,6 +819,7 @@ def main():
     H, G, P, N = w.nheads, w.ngroups, w.headdim, w.dstate
     total_ms, conv_ms, scan_ms, wall = run.timed(args.steps, args.warmup)
     progress(f"headline timed: {total_ms / args.steps:.4f} ms per step")
+    graph_step_ms = run.graph_ms(args.steps)
     norm = nrun.timed(args.steps, args.warmup, stream) if nrun is not None else None
     bwd = brun.timed(args.steps, min(args.warmup, 3), stream) if brun is not None else None
     if bwd is not None:
@@ -837,6 +878,7 @@ def main():
                    "step": "conv1d(4)+SiLU then chunked SSD scan with final states",
                    "parallelism": "single GPU"},
         "wall_s_timed": round(wall, 4),
+        "ms_per_step_graph": round(graph_step_ms, 5),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "cpu_baseline_single_core": cpu1,

@@ -160,6 +160,33 @@ int scratch_address(void **out) {
 
 }  // namespace
 
+namespace ssd {
+hipError_t set_max_dynamic_lds(const void *fn, size_t bytes) {
+  static std::mutex mu;
+  static constexpr int kSlots = 64;
+  static struct {
+    int dev;
+    const void *fn;
+    size_t bytes;
+  } done[kSlots];
+  static int n = 0;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < n; ++i)
+    if (done[i].dev == dev && done[i].fn == fn && done[i].bytes >= bytes) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e != hipSuccess) return e;
+  int slot = -1;
+  for (int i = 0; i < n; ++i)
+    if (done[i].dev == dev && done[i].fn == fn) slot = i;
+  if (slot < 0 && n < kSlots) slot = n++;
+  if (slot >= 0) done[slot] = {dev, fn, bytes};
+  return hipSuccess;
+}
+}  // namespace ssd
+
 extern "C" {
 
 const char *ssd_last_error(void) { return g_err; }

@@ -485,6 +485,15 @@ ScanPlan make_scan_plan(const ScanParams &p, int seg_chunks) {
   ScanPlan plan{};
   plan.packed = p.seq_idx != nullptr;
   plan.rows = plan.packed ? p.num_seqs : p.batch;
+  if (!p.bf16 && !plan.packed && p.L <= kQuadMaxL) {
+    // short fp32 batch rows: one quadratic-form launch (the model's chunk and
+    // seg_chunks do not change its result), no workspace
+    plan.quad = 1;
+    plan.seg_len = std::max(p.L, 1);
+    plan.nseg = 1;
+    plan.items = p.batch;
+    return plan;
+  }
   const int chunks_max = std::max(1, (p.L + kChunk - 1) / kChunk);
   // Automatic segments are whole tiles of the kernel that runs them: 128
   // tokens for bf16, the fp32 kernel's 64-token sub-chunks for fp32 (its
@@ -535,6 +544,7 @@ ScanPlan make_scan_plan(const ScanParams &p, int seg_chunks) {
 
 hipError_t launch_chunk_scan(const ScanParams &p, const ScanPlan &plan, void *workspace,
                              hipStream_t stream) {
+  if (plan.quad) return launch_quad_scan_f32(p, stream);
   char *ws = reinterpret_cast<char *>(workspace);
   if (plan.packed) {
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p.seq_idx, p.L, plan, ws);

@@ -118,15 +118,22 @@ __global__ __launch_bounds__(kT) void bwd_states_kernel(BwdParams p) {
 // -------------------------------------------------------------------------
 // 2. the chunks in reverse
 // -------------------------------------------------------------------------
+// Rows are padded by one float (129 and 65 floats), so lanes that walk down
+// a column of one of these tiles hit different LDS banks.
+constexpr int kNP = kN + 1, kPP = kP + 1;
+__device__ __forceinline__ int gi(int q, int n) { return q * kNP + n; }   // G, S0: [p][n]
+__device__ __forceinline__ int bi(int j, int n) { return j * kNP + n; }   // B, C: [token][n]
+__device__ __forceinline__ int xi(int j, int q) { return j * kPP + q; }   // X, DY, GB, S0C: [token][p]
+
 struct BwdSmem {
-  float G[kPN];       // adjoint dL/dS leaving the chunk (G1), then entering (G0)
-  float S0[kPN];      // state entering the chunk
-  float X[kQ * kP], DY[kQ * kP], B[kQ * kN], C[kQ * kN];
+  float G[kP * kNP];   // adjoint dL/dS leaving the chunk (G1), then entering (G0)
+  float S0[kP * kNP];  // state entering the chunk
+  float X[kQ * kPP], DY[kQ * kPP], B[kQ * kNP], C[kQ * kNP];
   float CB[kQ * kQ], DYX[kQ * kQ];                 // C_i . B_j, dy_i . x_j
   float Lm[kQ * kQ];                               // e^{cs_i - cs_j} for j <= i, else 0
-  float GB[kQ * kP];                               // (G1 B_j)[p]
+  float GB[kQ * kPP];                              // (G1 B_j)[p]
   float XG[kQ * kN];                               // (G1^T x_j)[n]
-  float S0C[kQ * kP];                              // (S0 C_i)[p]
+  float S0C[kQ * kPP];                             // (S0 C_i)[p]
   float dt[kQ], cs[kQ], z[kQ], ei[kQ], fj[kQ], dcs[kQ], ddt[kQ], xgb[kQ], red[kT / 64];
 };
 
@@ -139,25 +146,25 @@ __global__ __launch_bounds__(kT) void bwd_chunks_kernel(BwdParams p) {
   const float Ah = p.A[h], Dh = p.D ? p.D[h] : 0.f;
   const float *states = p.ws_states + ((int64_t)b * p.H + h) * p.nchunks * kPN;
   for (int e = tid; e < kPN; e += kT)
-    s.G[e] = p.dfinal ? p.dfinal[((int64_t)b * p.H + h) * kPN + e] : 0.f;
+    s.G[gi(e / kN, e % kN)] = p.dfinal ? p.dfinal[((int64_t)b * p.H + h) * kPN + e] : 0.f;
   float accA = 0.f, accD = 0.f, accBias = 0.f;
   __syncthreads();
 
   for (int c = p.nchunks - 1; c >= 0; --c) {
     const int t0 = c * kQ, nv = min(kQ, p.L - t0);
     // operands of the chunk (rows past the end are zero; their dt is 0)
-    for (int e = tid; e < kPN; e += kT) s.S0[e] = states[(int64_t)c * kPN + e];
+    for (int e = tid; e < kPN; e += kT) s.S0[gi(e / kN, e % kN)] = states[(int64_t)c * kPN + e];
     for (int e = tid; e < kQ * kP; e += kT) {
       const int j = e / kP, q = e % kP;
       const int64_t o = (((int64_t)b * p.L + t0 + j) * p.H + h) * kP + q;
-      s.X[e] = j < nv ? ld<T>(p.x, o) : 0.f;
-      s.DY[e] = j < nv ? ld<T>(p.dy, o) : 0.f;
+      s.X[xi(j, q)] = j < nv ? ld<T>(p.x, o) : 0.f;
+      s.DY[xi(j, q)] = j < nv ? ld<T>(p.dy, o) : 0.f;
     }
     for (int e = tid; e < kQ * kN; e += kT) {
       const int j = e / kN, q = e % kN;
       const int64_t o = (((int64_t)b * p.L + t0 + j) * p.G + g) * kN + q;
-      s.B[e] = j < nv ? ld<T>(p.B, o) : 0.f;
-      s.C[e] = j < nv ? ld<T>(p.C, o) : 0.f;
+      s.B[bi(j, q)] = j < nv ? ld<T>(p.B, o) : 0.f;
+      s.C[bi(j, q)] = j < nv ? ld<T>(p.C, o) : 0.f;
     }
     chunk_dt<T>(p, b, h, t0, nv, s.dt, s.cs, s.z);
     __syncthreads();
@@ -174,8 +181,8 @@ __global__ __launch_bounds__(kT) void bwd_chunks_kernel(BwdParams p) {
     for (int e = tid; e < kQ * kQ; e += kT) {
       const int i = e / kQ, j = e % kQ;
       float cb = 0.f, dx = 0.f;
-      for (int n = 0; n < kN; ++n) cb = fmaf(s.C[i * kN + n], s.B[j * kN + n], cb);
-      for (int q = 0; q < kP; ++q) dx = fmaf(s.DY[i * kP + q], s.X[j * kP + q], dx);
+      for (int n = 0; n < kN; ++n) cb = fmaf(s.C[bi(i, n)], s.B[bi(j, n)], cb);
+      for (int q = 0; q < kP; ++q) dx = fmaf(s.DY[xi(i, q)], s.X[xi(j, q)], dx);
       s.CB[e] = cb;
       s.DYX[e] = dx;
     }
@@ -183,20 +190,20 @@ __global__ __launch_bounds__(kT) void bwd_chunks_kernel(BwdParams p) {
       const int j = e / kP, q = e % kP;
       float gb = 0.f, sc = 0.f;
       for (int n = 0; n < kN; ++n) {
-        gb = fmaf(s.G[q * kN + n], s.B[j * kN + n], gb);
-        sc = fmaf(s.S0[q * kN + n], s.C[j * kN + n], sc);
+        gb = fmaf(s.G[gi(q, n)], s.B[bi(j, n)], gb);
+        sc = fmaf(s.S0[gi(q, n)], s.C[bi(j, n)], sc);
       }
-      s.GB[e] = gb;
-      s.S0C[e] = sc;
+      s.GB[xi(j, q)] = gb;
+      s.S0C[xi(j, q)] = sc;
     }
     for (int e = tid; e < kQ * kN; e += kT) {
       const int j = e / kN, n = e % kN;
       float xg = 0.f;
-      for (int q = 0; q < kP; ++q) xg = fmaf(s.X[j * kP + q], s.G[q * kN + n], xg);
+      for (int q = 0; q < kP; ++q) xg = fmaf(s.X[xi(j, q)], s.G[gi(q, n)], xg);
       s.XG[e] = xg;
     }
     float gs = 0.f;  // <G1, S0>
-    for (int e = tid; e < kPN; e += kT) gs = fmaf(s.G[e], s.S0[e], gs);
+    for (int e = tid; e < kPN; e += kT) gs = fmaf(s.G[gi(e / kN, e % kN)], s.S0[gi(e / kN, e % kN)], gs);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) gs += __shfl_xor(gs, off, 64);
     if ((tid & 63) == 0) s.red[tid >> 6] = gs;
@@ -209,7 +216,7 @@ __global__ __launch_bounds__(kT) void bwd_chunks_kernel(BwdParams p) {
       const int j = tid;
       const float fj = s.fj[j];
       float xgb = 0.f;  // x_j . (G1 B_j)
-      for (int q = 0; q < kP; ++q) xgb = fmaf(s.X[j * kP + q], s.GB[j * kP + q], xgb);
+      for (int q = 0; q < kP; ++q) xgb = fmaf(s.X[xi(j, q)], s.GB[xi(j, q)], xgb);
       s.xgb[j] = xgb;
       float dexp = fj * xgb;  // explicit: f_j x_j . G1 B_j + sum_{i>=j} L_ij CB_ij dyX_ij
       float col = 0.f;        // sum_{i>=j} W_ij
@@ -222,7 +229,7 @@ __global__ __launch_bounds__(kT) void bwd_chunks_kernel(BwdParams p) {
       for (int k = 0; k <= j; ++k)
         row = fmaf(s.Lm[j * kQ + k] * s.CB[j * kQ + k] * s.DYX[j * kQ + k], s.dt[k], row);
       float ey = 0.f;         // dy_j . (S0 C_j)
-      for (int q = 0; q < kP; ++q) ey = fmaf(s.DY[j * kP + q], s.S0C[j * kP + q], ey);
+      for (int q = 0; q < kP; ++q) ey = fmaf(s.DY[xi(j, q)], s.S0C[xi(j, q)], ey);
       float dcs = s.ei[j] * ey + row - col - fj * s.dt[j] * xgb;
       s.ddt[j] = dexp;
       s.dcs[j] = dcs;
@@ -245,18 +252,18 @@ __global__ __launch_bounds__(kT) void bwd_chunks_kernel(BwdParams p) {
       const int j = e / kP, q = e % kP;
       if (j >= nv) continue;
       float acc = 0.f;
-      for (int i = j; i < kQ; ++i) acc = fmaf(s.Lm[i * kQ + j] * s.CB[i * kQ + j], s.DY[i * kP + q], acc);
-      const float v = fmaf(Dh, s.DY[e], s.dt[j] * fmaf(s.fj[j], s.GB[e], acc));
+      for (int i = j; i < kQ; ++i) acc = fmaf(s.Lm[i * kQ + j] * s.CB[i * kQ + j], s.DY[xi(i, q)], acc);
+      const float v = fmaf(Dh, s.DY[xi(j, q)], s.dt[j] * fmaf(s.fj[j], s.GB[xi(j, q)], acc));
       reinterpret_cast<T *>(p.dx)[(((int64_t)b * p.L + t0 + j) * p.H + h) * kP + q] = from_f32<T>(v);
     }
     for (int e = tid; e < kQ * kN; e += kT) {
       const int j = e / kN, n = e % kN;
       if (j >= nv) continue;
       float ab = 0.f, ac = 0.f;
-      for (int i = j; i < kQ; ++i) ab = fmaf(s.Lm[i * kQ + j] * s.DYX[i * kQ + j], s.C[i * kN + n], ab);
-      for (int k = 0; k <= j; ++k) ac = fmaf(s.Lm[j * kQ + k] * s.dt[k] * s.DYX[j * kQ + k], s.B[k * kN + n], ac);
+      for (int i = j; i < kQ; ++i) ab = fmaf(s.Lm[i * kQ + j] * s.DYX[i * kQ + j], s.C[bi(i, n)], ab);
+      for (int k = 0; k <= j; ++k) ac = fmaf(s.Lm[j * kQ + k] * s.dt[k] * s.DYX[j * kQ + k], s.B[bi(k, n)], ac);
       float dcv = 0.f;  // e_j (S0^T dy_j)[n]
-      for (int q = 0; q < kP; ++q) dcv = fmaf(s.S0[q * kN + n], s.DY[j * kP + q], dcv);
+      for (int q = 0; q < kP; ++q) dcv = fmaf(s.S0[gi(q, n)], s.DY[xi(j, q)], dcv);
       const int64_t o = (((int64_t)b * p.L + t0 + j) * p.H + h) * kN + n;   // per-head partials
       p.ws_dB[o] = s.dt[j] * fmaf(s.fj[j], s.XG[e], ab);
       p.ws_dC[o] = fmaf(s.ei[j], dcv, ac);
@@ -283,14 +290,14 @@ __global__ __launch_bounds__(kT) void bwd_chunks_kernel(BwdParams p) {
     // G0 = sum_i e_i dy_i C_i^T + e^{cs_Q} G1, in place (every read of G1 is done)
     for (int e = tid; e < kPN; e += kT) {
       const int q = e / kN, n = e % kN;
-      float acc = eQ * s.G[e];
-      for (int i = 0; i < kQ; ++i) acc = fmaf(s.ei[i] * s.DY[i * kP + q], s.C[i * kN + n], acc);
-      s.G[e] = acc;
+      float acc = eQ * s.G[gi(q, n)];
+      for (int i = 0; i < kQ; ++i) acc = fmaf(s.ei[i] * s.DY[xi(i, q)], s.C[bi(i, n)], acc);
+      s.G[gi(q, n)] = acc;
     }
     __syncthreads();
   }
   if (p.dinit)
-    for (int e = tid; e < kPN; e += kT) p.dinit[((int64_t)b * p.H + h) * kPN + e] = s.G[e];
+    for (int e = tid; e < kPN; e += kT) p.dinit[((int64_t)b * p.H + h) * kPN + e] = s.G[gi(e / kN, e % kN)];
   if (tid == 0) {
     p.ws_scalars[((int64_t)b * p.H + h) * 3 + 0] = accA;
     p.ws_scalars[((int64_t)b * p.H + h) * 3 + 1] = accD;
@@ -341,8 +348,7 @@ hipError_t launch_t(const BwdParams &p, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t lds = sizeof(BwdSmem);
-  e = hipFuncSetAttribute(reinterpret_cast<const void *>(bwd_chunks_kernel<T>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  e = set_max_dynamic_lds(reinterpret_cast<const void *>(bwd_chunks_kernel<T>), lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_chunks_kernel<T>, dim3(units), dim3(kT), lds, stream, p);
   e = hipGetLastError();

@@ -171,16 +171,14 @@ hipError_t launch_r(const MimoParams &p, hipStream_t s) {
   if (p.trapezoid) {
     auto fn = decode_mimo_kernel<T, R, true>;
     if (lds > 65536) {
-      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      const hipError_t e = set_max_dynamic_lds(reinterpret_cast<const void *>(fn), lds);
       if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(fn, grid, block, lds, s, p);
   } else {
     auto fn = decode_mimo_kernel<T, R, false>;
     if (lds > 65536) {
-      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      const hipError_t e = set_max_dynamic_lds(reinterpret_cast<const void *>(fn), lds);
       if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(fn, grid, block, lds, s, p);

@@ -141,7 +141,7 @@ hipError_t launch_decode_step(const DecodeParams &p, hipStream_t stream) {
   const void *fn = p.bf16 ? reinterpret_cast<const void *>(decode_step_kernel<bf16_t>)
                          : reinterpret_cast<const void *>(decode_step_kernel<float>);
   if (lds > 65536) {
-    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const hipError_t e = set_max_dynamic_lds(fn, lds);
     if (e != hipSuccess) return e;
   }
   if (p.bf16) hipLaunchKernelGGL(decode_step_kernel<bf16_t>, grid, block, lds, stream, p);

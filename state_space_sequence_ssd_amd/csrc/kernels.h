@@ -8,6 +8,11 @@
 
 namespace ssd {
 
+// hipFuncSetAttribute(MaxDynamicSharedMemorySize) once per (device, kernel)
+// and size, not on every launch: a launch stays a plain stream operation
+// (nothing else on the host), which also keeps it capturable in a graph.
+hipError_t set_max_dynamic_lds(const void *fn, size_t bytes);
+
 constexpr int kHeadDim = 64;     // P
 constexpr int kDState = 128;     // N
 constexpr int kChunk = 128;      // Q
@@ -91,6 +96,7 @@ struct ScanPlan {
   int nseg;             // batch mode: segments per row
   int items;            // batch mode: exact count; packed: upper bound
   int segmented;        // segments may need an entry state from the pre-pass
+  int quad;             // fp32 short batch rows: one quadratic-form launch, no workspace
   size_t ws_plan_off, ws_local_off, ws_entry_off, ws_decay_off, ws_bytes;
 };
 
@@ -106,6 +112,11 @@ struct ScanParams {
   const float *init; float *final_state;
   void *y; int64_t y_sb, y_st;
 };
+
+// fp32 batch-row sequences up to this length run as one masked quadratic form
+// (quad_scan_f32.hip) instead of the chunked kernels.
+constexpr int kQuadMaxL = 1024;
+hipError_t launch_quad_scan_f32(const ScanParams &p, hipStream_t stream);
 
 // Host arithmetic only.
 ScanPlan make_scan_plan(const ScanParams &p, int seg_chunks);

@@ -185,19 +185,23 @@ def test_automatic_segments_follow_the_kernel_tile():
     sub-chunks and bf16 inputs at 128-token tiles; an explicit seg_chunks
     counts 128-token tiles for both.  The workspace holds a local and an
     entry state (64 x 128 fp32) per (segment, head) plus the decays, each
-    block 256-byte aligned."""
+    block 256-byte aligned.  fp32 batch rows of at most 1024 tokens run as
+    one quadratic form and need no workspace at all."""
     lib = ssd.load_library()
     state = 64 * 128 * 4
 
-    def need(**kw):
+    def need(seqlen, **kw):
         return lib.ssd_chunk_scan_workspace_size(
-            ctypes.byref(scan_args(batch=1, seqlen=512, nheads=8, ngroups=1, **kw)))
+            ctypes.byref(scan_args(batch=1, seqlen=seqlen, nheads=8, ngroups=1, **kw)))
 
     def expected(nseg):
         return 2 * nseg * 8 * state + (-(-nseg * 8 * 4 // 256)) * 256
-    assert need(dtype=ssd.SSD_DTYPE_F32) == expected(8)   # 64-token segments
-    assert need() == expected(4)                          # bf16: 128-token segments
-    assert need(dtype=ssd.SSD_DTYPE_F32, seg_chunks=2) == expected(2)
+    assert need(2048, dtype=ssd.SSD_DTYPE_F32) == expected(32)   # 64-token segments
+    assert need(512) == expected(4)                              # bf16: 128-token segments
+    assert need(2048, dtype=ssd.SSD_DTYPE_F32, seg_chunks=2) == expected(8)
+    for L in (1, 512, 1024):
+        assert need(L, dtype=ssd.SSD_DTYPE_F32) == 0 and need(L, dtype=ssd.SSD_DTYPE_F32, seg_chunks=1) == 0
+    assert need(1025, dtype=ssd.SSD_DTYPE_F32) > 0
 
 
 def test_decode_heads_per_group_limit():

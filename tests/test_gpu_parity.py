@@ -39,9 +39,16 @@ SMALL = [
     # sequences with no token (first, middle, last): their final state is their initial one
     (W("bf16_packed_empty_h8_g2_init", 1, 0, 8, 2, init=0.3, lens=[0, 5, 0, 130, 1, 0]), 0),
     (W("bf16_packed_empty_conv_seg1_h8_g2", 1, 0, 8, 2, conv=True, lens=[0, 200, 0, 3]), 1),
+    # fp32 batch rows up to 1024 tokens: the one-launch quadratic form
     (inputs.tiny_fp32(), 0),
     (W("fp32_conv_b2_l200_h8_g2_init", 2, 200, 8, 2, bf16=False, conv=True, init=0.3), 0),
     (W("fp32_seg1_b1_l300_h4_g1_init", 1, 300, 4, 1, bf16=False, init=0.3), 1),
+    (W("fp32_b1_l1_h4_g1_init", 1, 1, 4, 1, bf16=False, init=0.3), 0),
+    (W("fp32_b3_l1000_h4_g2_init", 3, 1000, 4, 2, bf16=False, init=0.3), 0),
+    (W("fp32_b1_l1024_h8_g1", 1, 1024, 8, 1, bf16=False), 0),
+    # longer fp32 rows and packed streams: the chunked fp32 kernel
+    (W("fp32_b1_l1100_h4_g1_init", 1, 1100, 4, 1, bf16=False, init=0.3), 0),
+    (W("fp32_seg2_b2_l1500_h4_g2", 2, 1500, 4, 2, bf16=False), 2),
     (W("fp32_packed_h4_g2_init", 1, 0, 4, 2, bf16=False, init=0.3, lens=[130, 1, 7, 128]), 0),
 ]
 

@@ -74,7 +74,7 @@ def test_noalloc_two_calls_in_a_row():
 def test_noalloc_fp32_and_no_workspace_needed():
     """The fp32 kernel's segmented path, and a call that needs no workspace
     (enough (row, head) pairs): the library array is not even looked up."""
-    w = inputs.ScanWorkload("fp32_seg_b1_l900_h4_g1_init", 1, 900, 4, 1, bf16=False, conv=False,
+    w = inputs.ScanWorkload("fp32_seg_b1_l1500_h4_g1_init", 1, 1500, 4, 1, bf16=False, conv=False,
                             final_state=True, init_std=0.3)
     d, y, fs, _ = _both(w, seed=5)
     _check_oracle(d, w, y, fs)
