@@ -48,6 +48,9 @@ class SsdScanArgs(ctypes.Structure):
                 ("y", _vp), ("y_stride_batch", _i64), ("y_stride_token", _i64)]
 
 
+_SCAN_ARGS_SIZE = ctypes.sizeof(SsdScanArgs)
+
+
 class SsdDecodeArgs(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("dtype", _i32),
                 ("batch", _i32), ("nheads", _i32), ("headdim", _i32), ("dstate", _i32),
@@ -182,7 +185,7 @@ def _same_dtype(ref: torch.Tensor, **tensors):
 
 
 def _shape(t: Optional[torch.Tensor], name: str, shape: tuple):
-    if t is not None and tuple(t.shape) != tuple(shape):
+    if t is not None and t.shape != shape:
         raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
 
 
@@ -256,11 +259,14 @@ def ssd_conv1d_silu(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.
 
 def _scan_args(x, dt, A, B, C, dt_bias, D, seq_idx, num_seqs, initial_state, final_state, y,
                chunk_size, seg_chunks) -> SsdScanArgs:
+    # Per-call host cost matters for short sequences (the kernel then runs
+    # for tens of microseconds): every tensor's metadata is read once and the
+    # struct is built in one constructor call.
     if x.dim() != 4 or B.dim() != 4 or C.dim() != 4 or dt.dim() != 3:
         raise ValueError("x (batch,L,H,P), B/C (batch,L,G,N) and dt (batch,L,H) expected")
     batch, L, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
-    _dtype_code(x)
+    code = _dtype_code(x)
     _same_dtype(x, dt=dt, B=B, C=C, y=y)
     _shape(B, "B", (batch, L, G, N))
     _shape(C, "C", (batch, L, G, N))
@@ -275,31 +281,20 @@ def _scan_args(x, dt, A, B, C, dt_bias, D, seq_idx, num_seqs, initial_state, fin
     _f32(final_state, "final_state", shape=(rows, H, P, N))
     _on_gpu(x, dt=dt, A=A, B=B, C=C, y=y, dt_bias=dt_bias, D=D, seq_idx=seq_idx,
             initial_state=initial_state, final_state=final_state)
+    xs, bs, cs, ds = x.stride(), B.stride(), C.stride(), dt.stride()
+    ys = y.stride() if y is not None else (0, 0, P, 1)
     if L > 0:
-        for t, name, inner in ((x, "x", P), (y, "y", P), (B, "B", N), (C, "C", N)):
-            if t is not None and (t.stride(3) != 1 or t.stride(2) != inner):
+        for st, name, inner in ((xs, "x", P), (ys, "y", P), (bs, "B", N), (cs, "C", N)):
+            if st[3] != 1 or st[2] != inner:
                 raise ValueError(f"{name}: the last two dims must be packed (strides ({inner}, 1))")
-        if dt.stride(2) != 1:
+        if ds[2] != 1:
             raise ValueError("dt: head dim must be unit-stride")
-    a = SsdScanArgs()
-    a.struct_size = ctypes.sizeof(SsdScanArgs)
-    a.dtype = _dtype_code(x)
-    a.batch, a.seqlen, a.nheads, a.headdim = batch, L, H, P
-    a.dstate, a.ngroups, a.chunk_size, a.seg_chunks = N, G, chunk_size, seg_chunks
-    a.x, a.x_stride_batch, a.x_stride_token = _ptr(x), x.stride(0), x.stride(1)
-    a.B, a.B_stride_batch, a.B_stride_token = _ptr(B), B.stride(0), B.stride(1)
-    a.C, a.C_stride_batch, a.C_stride_token = _ptr(C), C.stride(0), C.stride(1)
-    a.dt, a.dt_stride_batch, a.dt_stride_token = _ptr(dt), dt.stride(0), dt.stride(1)
-    a.dt_bias = _ptr(_f32(dt_bias, "dt_bias"))
-    a.A = _ptr(_f32(A, "A"))
-    a.D = _ptr(_f32(D, "D"))
-    a.seq_idx = _ptr(seq_idx)
-    a.num_seqs = int(num_seqs or 0)
-    a.initial_state = _ptr(_f32(initial_state, "initial_state"))
-    a.final_state = _ptr(_f32(final_state, "final_state"))
-    if y is not None:
-        a.y, a.y_stride_batch, a.y_stride_token = _ptr(y), y.stride(0), y.stride(1)
-    return a
+    return SsdScanArgs(_SCAN_ARGS_SIZE, code, batch, L, H, P, N, G, chunk_size, seg_chunks,
+                       x.data_ptr(), xs[0], xs[1], B.data_ptr(), bs[0], bs[1],
+                       C.data_ptr(), cs[0], cs[1], dt.data_ptr(), ds[0], ds[1],
+                       _ptr(dt_bias), A.data_ptr(), _ptr(D), _ptr(seq_idx), int(num_seqs or 0),
+                       _ptr(initial_state), _ptr(final_state),
+                       _ptr(y), ys[0], ys[1])
 
 
 def ssd_chunk_scan_workspace_size(x, dt, A, B, C, seq_idx=None, num_seqs=None, chunk_size=128,
@@ -331,11 +326,13 @@ def ssd_chunk_scan_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: to
         y = torch.empty(x.shape, dtype=x.dtype, device=x.device)
     a = _scan_args(x, dt, A, B, C, dt_bias, D, seq_idx, num_seqs, initial_state, final_state, y,
                    chunk_size, seg_chunks)
-    need = lib.ssd_chunk_scan_workspace_size(ctypes.byref(a))
-    if need == ctypes.c_size_t(-1).value:
-        raise SsdError(1, lib.ssd_last_error().decode())
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if workspace is None:
+        # (a caller workspace is checked by the library: too small is an error)
+        need = lib.ssd_chunk_scan_workspace_size(ctypes.byref(a))
+        if need == ctypes.c_size_t(-1).value:
+            raise SsdError(1, lib.ssd_last_error().decode())
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.ssd_chunk_scan_fwd(ctypes.byref(a), _ptr(workspace), ws_bytes, _stream(stream)))
     return y
