@@ -122,10 +122,30 @@ def scan_flops(w):
     return T * (G * (Q + 1) * N + H * (Q + 1) * P + 4 * H * P * N)
 
 
-def conv_algorithmic_bytes(w):
+def conv_algorithmic_bytes(w, channels=None):
+    """The conv over `channels` (all by default): input read and output written
+    once, the fp32 taps, seq_idx when packed."""
     es = 2 if w.bf16 else 4
-    return (w.batch * w.seqlen * w.conv_dim * 2 * es + w.conv_dim * 4 * 4
+    ch = w.conv_dim if channels is None else channels
+    return (w.batch * w.seqlen * ch * 2 * es + ch * 4 * 4
             + (w.batch * w.seqlen * 4 if w.packed_lengths is not None else 0))
+
+
+def fused_scan_algorithmic_bytes(w):
+    """The scan kernel with the x channels' conv inside: the scan's bytes (raw x
+    has post-conv x's size) plus those channels' taps and bias."""
+    return scan_algorithmic_bytes(w) + w.nheads * w.headdim * (4 + 1) * 4
+
+
+def step_algorithmic_bytes(w):
+    """The whole conv + scan step at its minimum: xBC read once, y written
+    once, dt, states and parameters; no intermediate."""
+    T = w.batch * w.seqlen
+    H, P = w.nheads, w.headdim
+    es = 2 if w.bf16 else 4
+    state = w.num_seqs * H * P * w.dstate * 4
+    return (T * (w.conv_dim + H * P + H) * es + state + (state if w.init_std > 0 else 0)
+            + w.conv_dim * 5 * 4 + 3 * H * 4 + (T * 4 if w.packed_lengths is not None else 0))
 
 
 def decode_algorithmic_bytes(dw):
@@ -140,8 +160,11 @@ def decode_algorithmic_bytes(dw):
 
 
 class ScanRun:
-    """Device tensors of one prefill config and its step (conv if the workload
-    has one, then the scan with final states), launched through the C ABI."""
+    """Device tensors of one prefill config and its step, launched through the
+    C ABI: the fused conv + scan (ssd_conv_scan_fwd) when the workload has a
+    conv, else the scan; both with final states.  The unfused pair (conv then
+    scan) and the fused call's first kernel alone (the B|C conv) are timed
+    beside it."""
 
     def __init__(self, w, seed):
         import torch
@@ -175,30 +198,57 @@ class ScanRun:
         wsb = ssd.ssd_chunk_scan_workspace_size(self.x, self.dt, self.A, self.B, self.C, seq_idx=self.seq,
                                                 num_seqs=self.nseq)
         self.ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+        if w.conv:
+            fwb = ssd.ssd_conv_scan_workspace_size(self.xbc, self.conv_w, self.dt, self.A, H, G,
+                                                   seq_idx=self.seq, num_seqs=self.nseq)
+            self.fws = torch.empty(max(fwb, 1), dtype=torch.uint8, device=dev)
+            # the fused call's B|C conv on its own (same kernel, same launch)
+            self.bc_in = self.xbc[..., H * P:]
+            self.bc_w = self.conv_w[H * P:]
+            self.bc_out = torch.empty((Bt, L, 2 * G * N), dtype=dtp, device=dev)
         self.stream = torch.cuda.current_stream()
 
+    def scan_call(self):
+        self.ssd.ssd_chunk_scan_fwd(self.x, self.dt, self.A, self.B, self.C, dt_bias=self.dt_bias, D=self.D,
+                                    seq_idx=self.seq, num_seqs=self.nseq, initial_state=self.init,
+                                    final_state=self.fs, y=self.y, workspace=self.ws)
+
     def step(self, ev=None):
-        ssd, w = self.ssd, self.w
+        """The timed step: fused conv + scan (conv workloads) or the scan."""
         if ev is not None:
             ev[0].record(self.stream)
-        if w.conv:
-            ssd.ssd_conv1d_silu(self.xbc, self.conv_w, seq_idx=self.seq, num_seqs=self.nseq, out=self.conv_out)
+        if self.w.conv:
+            H, G = self.w.nheads, self.w.ngroups
+            self.ssd.ssd_conv_scan_fwd(self.xbc, self.conv_w, self.dt, self.A, H, G, dt_bias=self.dt_bias,
+                                       D=self.D, seq_idx=self.seq, num_seqs=self.nseq, initial_state=self.init,
+                                       final_state=self.fs, y=self.y, workspace=self.fws)
+        else:
+            self.scan_call()
         if ev is not None:
             ev[1].record(self.stream)
-        ssd.ssd_chunk_scan_fwd(self.x, self.dt, self.A, self.B, self.C, dt_bias=self.dt_bias, D=self.D,
-                               seq_idx=self.seq, num_seqs=self.nseq, initial_state=self.init,
-                               final_state=self.fs, y=self.y, workspace=self.ws)
-        if ev is not None:
-            ev[2].record(self.stream)
+
+    def step_unfused(self, ev):
+        """Reference: the conv kernel over every channel, then the scan."""
+        ev[0].record(self.stream)
+        self.ssd.ssd_conv1d_silu(self.xbc, self.conv_w, seq_idx=self.seq, num_seqs=self.nseq, out=self.conv_out)
+        ev[1].record(self.stream)
+        self.scan_call()
+        ev[2].record(self.stream)
+
+    def step_conv_bc(self, ev):
+        """The fused call's first kernel alone: the conv of the B|C channels."""
+        ev[0].record(self.stream)
+        self.ssd.ssd_conv1d_silu(self.bc_in, self.bc_w, seq_idx=self.seq, num_seqs=self.nseq, out=self.bc_out)
+        ev[1].record(self.stream)
 
     def timed(self, steps, warmup):
-        """W untimed steps, then K steps bracketed by events per kernel and
-        around the whole region.  Returns (total_ms, conv_ms list, scan_ms list, wall_s)."""
+        """W untimed steps, then K steps, each bracketed by events, and events
+        around the whole region.  Returns (total_ms, step_ms list, wall_s)."""
         import torch
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         wall0 = time.perf_counter()
@@ -208,9 +258,30 @@ class ScanRun:
         t1.record(self.stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - wall0
-        conv = [e[0].elapsed_time(e[1]) for e in evs]
-        scan = [e[1].elapsed_time(e[2]) for e in evs]
-        return t0.elapsed_time(t1), conv, scan, wall
+        return t0.elapsed_time(t1), [e[0].elapsed_time(e[1]) for e in evs], wall
+
+    def timed_parts(self, steps, warmup):
+        """Conv workloads: per-kernel event times of the unfused pair (conv,
+        scan) and of the fused call's B|C conv alone, each over K steps after
+        W warm-ups.  Returns {"conv": [...], "scan": [...], "conv_bc": [...]}."""
+        import torch
+        out = {"conv": [], "scan": [], "conv_bc": []}
+        for k in range(warmup + steps):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            self.step_unfused(ev)
+            if k >= warmup:
+                out["conv"].append(ev)
+        for k in range(warmup + steps):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            self.step_conv_bc(ev)
+            if k >= warmup:
+                out["conv_bc"].append(ev)
+        torch.cuda.synchronize()
+        evs = out["conv"]
+        out["conv"] = [e[0].elapsed_time(e[1]) for e in evs]
+        out["scan"] = [e[1].elapsed_time(e[2]) for e in evs]
+        out["conv_bc"] = [e[0].elapsed_time(e[1]) for e in out["conv_bc"]]
+        return out
 
     def graph_ms(self, steps, replays=3):
         """GPU time per step with `steps` steps captured in one HIP graph and
@@ -260,29 +331,48 @@ class ScanRun:
         return (time.perf_counter() - t0) * 1e3 / steps
 
 
+def rate(nbytes, ms):
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return round(gbs, 1), round(gbs / HBM_PEAK_GBS, 4)
+
+
 def config_result(run, steps, warmup):
-    """One synthetic config, event-timed per kernel on the launch stream; rates
-    against the HBM roofline."""
+    """One synthetic config, event-timed on the launch stream; rates against
+    the HBM roofline.  Conv workloads time the fused step; its scan kernel is
+    the step minus the fused call's B|C conv (that launch timed alone), and
+    the unfused pair is reported beside it."""
     import numpy as np
     w = run.w
-    _, conv, scan, _ = run.timed(steps, warmup)
-    scan_ms = float(np.mean(scan))
+    _, step_list, _ = run.timed(steps, warmup)
+    step_ms = float(np.mean(step_list))
     tokens = w.batch * w.seqlen
-    sb = scan_algorithmic_bytes(w)
-    out = {"tokens": tokens, "io_dtype": "bf16" if w.bf16 else "f32",
-           "scan_avg_ms": round(scan_ms, 5), "scan_algorithmic_bytes": sb,
-           "scan_gbs": round(sb / (scan_ms * 1e-3) / 1e9, 1),
-           "scan_hbm_frac": round(sb / (scan_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-           "scan_tokens_per_s": round(tokens / (scan_ms * 1e-3), 1)}
-    step_ms = scan_ms
+    out = {"tokens": tokens, "io_dtype": "bf16" if w.bf16 else "f32", "step_avg_ms": round(step_ms, 5),
+           "layer_tokens_per_s": round(tokens / (step_ms * 1e-3), 1)}
     if w.conv:
-        conv_ms = float(np.mean(conv))
-        cb = conv_algorithmic_bytes(w)
-        out.update({"conv_avg_ms": round(conv_ms, 5), "conv_algorithmic_bytes": cb,
-                    "conv_gbs": round(cb / (conv_ms * 1e-3) / 1e9, 1),
-                    "conv_hbm_frac": round(cb / (conv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
-        step_ms += conv_ms
-    out["layer_tokens_per_s"] = round(tokens / (step_ms * 1e-3), 1)
+        parts = run.timed_parts(steps, warmup)
+        bc_ms = float(np.mean(parts["conv_bc"]))
+        scan_ms = step_ms - bc_ms
+        sb = fused_scan_algorithmic_bytes(w)
+        cbb = conv_algorithmic_bytes(w, 2 * w.ngroups * w.dstate)
+        stb = step_algorithmic_bytes(w)
+        u_conv, u_scan = float(np.mean(parts["conv"])), float(np.mean(parts["scan"]))
+        out.update({
+            "step": "fused conv + scan (ssd_conv_scan_fwd): B|C conv kernel, then the scan with the x conv inside",
+            "step_algorithmic_bytes": stb, "step_gbs": rate(stb, step_ms)[0], "step_hbm_frac": rate(stb, step_ms)[1],
+            "conv_bc_avg_ms": round(bc_ms, 5), "conv_bc_algorithmic_bytes": cbb,
+            "conv_bc_hbm_frac": rate(cbb, bc_ms)[1],
+            "scan_timing": "fused step minus the B|C conv launched alone (HIP events)",
+            "unfused": {"conv_avg_ms": round(u_conv, 5), "scan_avg_ms": round(u_scan, 5),
+                        "step_ms": round(u_conv + u_scan, 5),
+                        "layer_tokens_per_s": round(tokens / ((u_conv + u_scan) * 1e-3), 1),
+                        "conv_hbm_frac": rate(conv_algorithmic_bytes(w), u_conv)[1],
+                        "scan_hbm_frac": rate(scan_algorithmic_bytes(w), u_scan)[1]}})
+    else:
+        scan_ms = step_ms
+        sb = scan_algorithmic_bytes(w)
+    out.update({"scan_avg_ms": round(scan_ms, 5), "scan_algorithmic_bytes": sb,
+                "scan_gbs": rate(sb, scan_ms)[0], "scan_hbm_frac": rate(sb, scan_ms)[1],
+                "scan_tokens_per_s": round(tokens / (scan_ms * 1e-3), 1)})
     out["step_launch_inclusive_ms"] = round(run.launch_inclusive_ms(steps), 5)
     gms = run.graph_ms(steps)
     out["step_graph_ms"] = round(gms, 5)
@@ -817,9 +907,10 @@ def main():
     # ---------------- headline: prefill step at the Nemotron-H 8B layer shape ----------------
     w = run.w
     H, G, P, N = w.nheads, w.ngroups, w.headdim, w.dstate
-    total_ms, conv_ms, scan_ms, wall = run.timed(args.steps, args.warmup)
+    total_ms, step_list, wall = run.timed(args.steps, args.warmup)
     progress(f"headline timed: {total_ms / args.steps:.4f} ms per step")
     graph_step_ms = run.graph_ms(args.steps)
+    parts = run.timed_parts(args.steps, args.warmup)
     norm = nrun.timed(args.steps, args.warmup, stream) if nrun is not None else None
     bwd = brun.timed(args.steps, min(args.warmup, 3), stream) if brun is not None else None
     if bwd is not None:
@@ -828,29 +919,42 @@ def main():
     tokens = w.batch * w.seqlen
     value = tokens / (ms_per_step / 1e3)
 
-    conv_avg, scan_avg = float(np.mean(conv_ms)), float(np.mean(scan_ms))
-    scan_bytes = scan_algorithmic_bytes(w)
-    conv_bytes = conv_algorithmic_bytes(w)
+    step_avg = float(np.mean(step_list))
+    bc_avg = float(np.mean(parts["conv_bc"]))
+    scan_avg = step_avg - bc_avg
+    scan_bytes = fused_scan_algorithmic_bytes(w)
+    bc_bytes = conv_algorithmic_bytes(w, 2 * G * N)
+    u_conv, u_scan = float(np.mean(parts["conv"])), float(np.mean(parts["scan"]))
+
+    def kern(avg, nbytes, **extra):
+        d = {"avg_ms": avg, "algorithmic_bytes": nbytes, "gbs": nbytes / (avg * 1e-3) / 1e9,
+             "hbm_frac": nbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        d.update(extra)
+        return d
+
     kernels = {
-        "ssd_chunk_scan_fwd": {
-            "avg_ms": scan_avg, "median_ms": float(np.median(scan_ms)),
-            "algorithmic_bytes": scan_bytes, "gbs": scan_bytes / (scan_avg * 1e-3) / 1e9,
-            "hbm_frac": scan_bytes / (scan_avg * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "useful_tflops": scan_flops(w) / (scan_avg * 1e-3) / 1e12,
-            "tokens_per_s": tokens / (scan_avg * 1e-3),
-            "traffic": read_traffic("chunk_scan_nemotron_h_8b", SCAN_SOURCES)},
-        "ssd_conv1d_silu": {
-            "avg_ms": conv_avg, "median_ms": float(np.median(conv_ms)),
-            "algorithmic_bytes": conv_bytes, "gbs": conv_bytes / (conv_avg * 1e-3) / 1e9,
-            "hbm_frac": conv_bytes / (conv_avg * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "traffic": read_traffic("conv1d_silu_nemotron_h_8b", CONV_SOURCES)},
+        "chunk_scan_bf16 (x conv fused)": kern(
+            scan_avg, scan_bytes, useful_tflops=scan_flops(w) / (scan_avg * 1e-3) / 1e12,
+            tokens_per_s=tokens / (scan_avg * 1e-3),
+            timing="fused step minus the B|C conv launched alone (HIP events)",
+            traffic=read_traffic("chunk_scan_fused_nemotron_h_8b", SCAN_SOURCES)),
+        "conv1d_silu (B|C channels)": kern(bc_avg, bc_bytes,
+                                           traffic=read_traffic("conv1d_silu_bc_nemotron_h_8b", CONV_SOURCES)),
     }
     dom_name = max(kernels, key=lambda k: kernels[k]["avg_ms"])
     dom = kernels[dom_name]
     roofline = {"kernel": dom_name, "bound": "hbm", "achieved": round(dom["gbs"], 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom["gbs"] / HBM_PEAK_GBS, 4),
                 "traffic": dom["traffic"]}
-
+    stb = step_algorithmic_bytes(w)
+    step_summary = {"algorithmic_bytes": stb, "gbs": round(stb / (ms_per_step * 1e-3) / 1e9, 1),
+                    "hbm_frac": round(stb / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    unfused = {
+        "ssd_conv1d_silu": kern(u_conv, conv_algorithmic_bytes(w),
+                                traffic=read_traffic("conv1d_silu_nemotron_h_8b", CONV_SOURCES)),
+        "ssd_chunk_scan_fwd": kern(u_scan, scan_algorithmic_bytes(w),
+                                   traffic=read_traffic("chunk_scan_nemotron_h_8b", SCAN_SOURCES)),
+        "step_ms": u_conv + u_scan, "layer_tokens_per_s": tokens / ((u_conv + u_scan) * 1e-3)}
 
     cpu = cpu1 = None
     if cpu_on:
@@ -875,11 +979,14 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seqlen, "nheads": H,
                    "headdim": P, "dstate": N, "ngroups": G, "chunk": w.chunk,
-                   "step": "conv1d(4)+SiLU then chunked SSD scan with final states",
+                   "step": "conv1d(4)+SiLU and the chunked SSD scan with final states, fused "
+                           "(ssd_conv_scan_fwd)",
                    "parallelism": "single GPU"},
         "wall_s_timed": round(wall, 4),
         "ms_per_step_graph": round(graph_step_ms, 5),
         "roofline": roofline,
+        "step_bytes": step_summary,
+        "unfused_reference": unfused,
         "cpu_baseline": cpu,
         "cpu_baseline_single_core": cpu1,
         "kernels": kernels,

@@ -199,6 +199,72 @@ int ssd_chunk_scan_fwd(const ssd_scan_args *args, void *workspace,
                        size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * ssd_conv_scan_fwd -- the conv1d(4) + SiLU and the chunked scan of one
+ * Mamba-2 mixer in one call: the short convolution fused into the scan's
+ * prologue.
+ *
+ * Passages: Conv1D and the SSM merged into one operator to save kernel
+ * launches and memory round trips ("Nemotron-Mamba3 architecture" article,
+ * sec. 4.3, deployment notes on operator fusion); the conv and the scan
+ * themselves as for ssd_conv1d_silu and ssd_chunk_scan_fwd above.
+ *
+ * The result is exactly that of ssd_conv1d_silu on xBC followed by
+ * ssd_chunk_scan_fwd on the x | B | C column views of its output (and, for
+ * bf16, bit for bit: the fused kernel repeats the conv's fp32 arithmetic in
+ * the same order and rounds to bf16 where the conv would have stored it).
+ * The post-conv x is never written to memory: the bf16 scan computes it
+ * while loading its x tiles; the B and C channels (shared by the heads of a
+ * group) are convolved once into the workspace.  fp32 runs the two steps
+ * through the workspace.
+ *
+ *   xBC (batch, seqlen, conv_dim), conv_dim = nheads*headdim + 2*ngroups*dstate:
+ *       the raw conv input, columns x | B | C (the in_proj output's slice);
+ *       16-byte aligned, strides multiples of 8 elements.
+ *   conv_weight (conv_dim, conv_width) fp32, required; conv_bias (conv_dim)
+ *       fp32 or NULL.  conv_width must be 4.
+ *   conv_state_in / conv_state_out (rows, conv_width-1, conv_dim) or NULL:
+ *       as for ssd_conv1d_silu (conv_state_out is written after every read
+ *       of conv_state_in, so the two may be the same buffer).
+ *   dt, dt_bias, A, D, seq_idx, num_seqs, initial_state, final_state, y,
+ *   chunk_size, seg_chunks: as for ssd_chunk_scan_fwd.
+ *
+ * The workspace (ssd_conv_scan_workspace_size() bytes, 256-byte aligned,
+ * contents on entry irrelevant) holds the conv output of the B and C
+ * channels (bf16; all channels for fp32) and the scan's own workspace.
+ * Errors: as for the two calls it replaces (SSD_ERR_INVALID_ARG,
+ * SSD_ERR_UNSUPPORTED, SSD_ERR_MISALIGNED, SSD_ERR_WORKSPACE_TOO_SMALL,
+ * SSD_ERR_HIP), reported before any kernel is launched except SSD_ERR_HIP.
+ * ---------------------------------------------------------------------- */
+typedef struct ssd_conv_scan_args {
+  uint32_t struct_size;          /* sizeof(ssd_conv_scan_args) */
+  int32_t dtype;                 /* ssd_dtype of xBC, dt, y, conv states */
+  int32_t batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size;
+  int32_t seg_chunks;            /* 0 = automatic */
+  int32_t conv_width;            /* 4 */
+  const void *xBC; int64_t xBC_stride_batch, xBC_stride_token;
+  const float *conv_weight;      /* (conv_dim, conv_width), required */
+  const float *conv_bias;        /* (conv_dim) or NULL */
+  const void *dt; int64_t dt_stride_batch, dt_stride_token;
+  const float *dt_bias;          /* (nheads) or NULL */
+  const float *A;                /* (nheads), required */
+  const float *D;                /* (nheads) or NULL */
+  const int32_t *seq_idx;        /* (seqlen) or NULL */
+  int32_t num_seqs;
+  const void *conv_state_in;     /* (rows, conv_width-1, conv_dim) or NULL */
+  void *conv_state_out;          /* (rows, conv_width-1, conv_dim) or NULL */
+  const float *initial_state;    /* (rows, nheads, headdim, dstate) or NULL */
+  float *final_state;            /* (rows, nheads, headdim, dstate) or NULL */
+  void *y;        int64_t y_stride_batch, y_stride_token;
+} ssd_conv_scan_args;
+
+/* Workspace bytes ssd_conv_scan_fwd needs (host arithmetic; (size_t)-1 if
+ * args are invalid). */
+size_t ssd_conv_scan_workspace_size(const ssd_conv_scan_args *args);
+
+int ssd_conv_scan_fwd(const ssd_conv_scan_args *args, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
  * ssd_chunk_scan_fwd_noalloc -- ssd_chunk_scan_fwd without a caller
  * workspace, for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc).

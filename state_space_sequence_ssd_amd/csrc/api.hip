@@ -233,6 +233,7 @@ int ssd_conv1d_silu(const ssd_conv_args *a, void *stream) {
   p.w = a->weight; p.bias = a->bias;
   p.seq_idx = a->seq_idx; p.num_seqs = a->num_seqs;
   p.state_in = a->conv_state_in; p.state_out = a->conv_state_out;
+  p.s_st = a->channels;
   const int drc = debug_check_seq_idx("ssd_conv1d_silu", a->seq_idx, a->seqlen, a->num_seqs, stream);
   if (drc != SSD_OK) return drc;
   const hipError_t e = ssd::launch_conv1d_silu(p, reinterpret_cast<hipStream_t>(stream));
@@ -283,6 +284,160 @@ int ssd_chunk_scan_fwd_noalloc(const ssd_scan_args *a, void *stream) {
   if (drc != SSD_OK) return drc;
   const hipError_t e = ssd::launch_chunk_scan(p, plan, ws, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SSD_ERR_HIP, "ssd_chunk_scan_fwd_noalloc: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// conv + scan in one call
+// ---------------------------------------------------------------------------
+namespace {
+struct ConvScanPlan {
+  ssd::ScanParams sp;
+  ssd::ScanPlan plan;
+  ssd::ConvParams conv;  // the conv launch (B|C channels for bf16, all for fp32)
+  size_t conv_bytes, scan_off, total;
+};
+
+constexpr size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+int plan_conv_scan(const ssd_conv_scan_args *a, ConvScanPlan &cp) {
+  if (!a) return fail(SSD_ERR_INVALID_ARG, "ssd_conv_scan_fwd: args is NULL");
+  if (a->struct_size != sizeof(ssd_conv_scan_args))
+    return fail(SSD_ERR_INVALID_ARG, "ssd_conv_scan_fwd: struct_size %u != %zu", a->struct_size,
+                sizeof(ssd_conv_scan_args));
+  if (a->dtype != SSD_DTYPE_F32 && a->dtype != SSD_DTYPE_BF16)
+    return fail(SSD_ERR_UNSUPPORTED, "ssd_conv_scan_fwd: dtype %d not supported", a->dtype);
+  if (a->conv_width != ssd::kConvWidth)
+    return fail(SSD_ERR_UNSUPPORTED, "ssd_conv_scan_fwd: built for conv width 4 (got %d)", a->conv_width);
+  if (!a->conv_weight) return fail(SSD_ERR_INVALID_ARG, "ssd_conv_scan_fwd: conv_weight is NULL");
+  if (a->seqlen > 0 && !a->xBC) return fail(SSD_ERR_INVALID_ARG, "ssd_conv_scan_fwd: xBC is required");
+  if (!aligned16(a->conv_weight) || (a->conv_state_in && !aligned16(a->conv_state_in)) ||
+      (a->conv_state_out && !aligned16(a->conv_state_out)))
+    return fail(SSD_ERR_MISALIGNED, "ssd_conv_scan_fwd: conv_weight and conv states must be 16-byte aligned");
+  // the scan's own checks, on the views it will read: x at column 0 of xBC,
+  // B and C at the conv output's layout (any 256-aligned base stands in for
+  // the workspace here)
+  const bool bf16 = a->dtype == SSD_DTYPE_BF16;
+  const int es = dtype_size(a->dtype);
+  if (a->nheads < 1 || a->ngroups < 1 || a->headdim < 1 || a->dstate < 1 || a->batch < 1 || a->seqlen < 0)
+    return fail(SSD_ERR_INVALID_ARG, "ssd_conv_scan_fwd: non-positive dims");
+  const int64_t HP = (int64_t)a->nheads * a->headdim, GN = (int64_t)a->ngroups * a->dstate;
+  const int64_t conv_dim = HP + 2 * GN;
+  if (a->seqlen > 0) {
+    if (!vec_ok(a->xBC, a->xBC_stride_batch, a->xBC_stride_token, es))
+      return fail(SSD_ERR_MISALIGNED,
+                  "ssd_conv_scan_fwd: xBC needs a 16-byte aligned base and strides multiples of %d elements", 16 / es);
+    if (a->xBC_stride_token < conv_dim)
+      return fail(SSD_ERR_INVALID_ARG, "ssd_conv_scan_fwd: xBC token stride %lld below conv_dim %lld",
+                  (long long)a->xBC_stride_token, (long long)conv_dim);
+  }
+  const int64_t out_ch = bf16 ? 2 * GN : conv_dim;  // channels of the conv output in the workspace
+  const int64_t L = a->seqlen;
+  static const char kDummy[16] __attribute__((aligned(256))) = {};
+  ssd_scan_args s{};
+  s.struct_size = sizeof(ssd_scan_args);
+  s.dtype = a->dtype;
+  s.batch = a->batch; s.seqlen = a->seqlen; s.nheads = a->nheads; s.headdim = a->headdim;
+  s.dstate = a->dstate; s.ngroups = a->ngroups; s.chunk_size = a->chunk_size; s.seg_chunks = a->seg_chunks;
+  if (bf16) {
+    s.x = a->xBC; s.x_stride_batch = a->xBC_stride_batch; s.x_stride_token = a->xBC_stride_token;
+  } else {
+    s.x = kDummy; s.x_stride_batch = L * out_ch; s.x_stride_token = out_ch;
+  }
+  s.B = kDummy; s.B_stride_batch = L * out_ch; s.B_stride_token = out_ch;
+  s.C = kDummy; s.C_stride_batch = L * out_ch; s.C_stride_token = out_ch;
+  s.dt = a->dt; s.dt_stride_batch = a->dt_stride_batch; s.dt_stride_token = a->dt_stride_token;
+  s.dt_bias = a->dt_bias; s.A = a->A; s.D = a->D;
+  s.seq_idx = a->seq_idx; s.num_seqs = a->num_seqs;
+  s.initial_state = a->initial_state; s.final_state = a->final_state;
+  s.y = a->y; s.y_stride_batch = a->y_stride_batch; s.y_stride_token = a->y_stride_token;
+  if (a->seqlen == 0) { s.x = s.B = s.C = nullptr; }
+  int rc = check_scan(&s, cp.sp);
+  if (rc != SSD_OK) return rc;  // (its messages name ssd_chunk_scan_fwd: the scan half of this call)
+  cp.plan = ssd::make_scan_plan(cp.sp, a->seg_chunks);
+  cp.conv_bytes = align256((size_t)a->batch * (size_t)L * (size_t)out_ch * (size_t)es);
+  cp.scan_off = cp.conv_bytes;
+  cp.total = cp.conv_bytes + cp.plan.ws_bytes;
+
+  ssd::ConvParams &c = cp.conv;
+  c = ssd::ConvParams{};
+  c.bf16 = bf16;
+  c.batch = a->batch; c.L = a->seqlen; c.CH = (int)out_ch;
+  const int64_t ch0 = bf16 ? HP : 0;  // first channel the conv launch covers
+  c.x = a->xBC ? static_cast<const char *>(a->xBC) + ch0 * es : nullptr;
+  c.x_sb = a->xBC_stride_batch; c.x_st = a->xBC_stride_token;
+  c.o_sb = L * out_ch; c.o_st = out_ch;
+  c.w = a->conv_weight + ch0 * ssd::kConvWidth;
+  c.bias = a->conv_bias ? a->conv_bias + ch0 : nullptr;
+  c.seq_idx = a->seq_idx; c.num_seqs = a->num_seqs;
+  c.state_in = a->conv_state_in ? static_cast<const char *>(a->conv_state_in) + ch0 * es : nullptr;
+  c.state_out = nullptr;
+  c.s_st = conv_dim;
+  if (bf16) {
+    cp.sp.xconv = 1;
+    cp.sp.conv_w = a->conv_weight;
+    cp.sp.conv_b = a->conv_bias;
+    cp.sp.conv_state = a->conv_state_in;
+    cp.sp.conv_ch = conv_dim;
+  }
+  return SSD_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t ssd_conv_scan_workspace_size(const ssd_conv_scan_args *a) {
+  ConvScanPlan cp;
+  if (plan_conv_scan(a, cp) != SSD_OK) return (size_t)-1;
+  return cp.total;
+}
+
+int ssd_conv_scan_fwd(const ssd_conv_scan_args *a, void *workspace, size_t ws_bytes, void *stream) {
+  ConvScanPlan cp;
+  const int rc = plan_conv_scan(a, cp);
+  if (rc != SSD_OK) return rc;
+  if (ws_bytes < cp.total || (cp.total > 0 && !workspace))
+    return fail(SSD_ERR_WORKSPACE_TOO_SMALL, "ssd_conv_scan_fwd: workspace needs %zu bytes, got %zu", cp.total,
+                ws_bytes);
+  if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return fail(SSD_ERR_MISALIGNED, "ssd_conv_scan_fwd: workspace must be 256-byte aligned");
+  const int drc = debug_check_seq_idx("ssd_conv_scan_fwd", a->seq_idx, a->seqlen, a->num_seqs, stream);
+  if (drc != SSD_OK) return drc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char *ws = static_cast<char *>(workspace);
+  const int es = dtype_size(a->dtype);
+  const int64_t HP = (int64_t)a->nheads * a->headdim, GN = (int64_t)a->ngroups * a->dstate;
+  ssd::ConvParams c = cp.conv;
+  ssd::ScanParams sp = cp.sp;
+  if (a->seqlen > 0) {
+    c.out = ws;
+    hipError_t e = ssd::launch_conv1d_silu(c, st);
+    if (e != hipSuccess) return fail(SSD_ERR_HIP, "ssd_conv_scan_fwd (conv): %s", hipGetErrorString(e));
+    if (sp.xconv) {
+      sp.B = ws;                 // conv output: B | C channels
+      sp.C = ws + GN * es;
+    } else {
+      sp.x = ws;                 // conv output: x | B | C channels
+      sp.B = ws + HP * es;
+      sp.C = ws + (HP + GN) * es;
+    }
+  }
+  hipError_t e = ssd::launch_chunk_scan(sp, cp.plan, ws + cp.scan_off, st);
+  if (e != hipSuccess) return fail(SSD_ERR_HIP, "ssd_conv_scan_fwd (scan): %s", hipGetErrorString(e));
+  if (a->conv_state_out) {
+    // after every read of conv_state_in (the two may be one buffer)
+    ssd::ConvParams x = ssd::ConvParams{};
+    x.bf16 = c.bf16;
+    x.batch = a->batch; x.L = a->seqlen; x.CH = (int)(HP + 2 * GN);
+    x.x = a->xBC; x.x_sb = a->xBC_stride_batch; x.x_st = a->xBC_stride_token;
+    x.seq_idx = a->seq_idx; x.num_seqs = a->num_seqs;
+    x.state_in = a->conv_state_in; x.state_out = a->conv_state_out;
+    x.s_st = HP + 2 * GN;
+    e = ssd::launch_conv_state_out(x, st);
+    if (e != hipSuccess) return fail(SSD_ERR_HIP, "ssd_conv_scan_fwd (conv state): %s", hipGetErrorString(e));
+  }
   return ok();
 }
 

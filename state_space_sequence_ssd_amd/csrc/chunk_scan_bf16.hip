@@ -309,7 +309,7 @@ __device__ __forceinline__ bf16x8 trd(const lds_u8 *tile, uint32_t lo, uint32_t 
   return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
 }
 
-template <bool kFull, int W>
+template <bool kFull, bool kConv, int W>
 __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &plan, char *ws, const Item &it,
                                          int item, int h, int g, const Lds &sm) {
   using Cf = Cfg<kFull, W>;
@@ -378,9 +378,98 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
                                        (lds_void *)(sm.X + (32 * W + 8 * i) * 128), 16, 0, 0);
     }
   };
+  // kConv: the x tile is conv1d(4) + SiLU of the raw conv input.  The raw
+  // rows land in the tile by the same direct loads as post-conv rows would
+  // (issue_x); once a wave's own loads have landed it convolves its 32 rows
+  // in place, with the conv kernel's arithmetic (fp32 taps in the same order,
+  // the same SiLU, bf16 round to nearest even), so the tile ends up holding
+  // exactly what a separate conv pass would have written.  Lane roles:
+  // channels 2 cp, 2 cp + 1 (cp = lane % 32) of rows 16 rg .. 16 rg + 15 (rg =
+  // lane / 32) of the wave's rows.  All of a wave's LDS reads precede its
+  // writes, so in place is safe within the wave; the 3 rows before the wave's
+  // first (another wave's, or before the chunk) come from global memory into
+  // registers: the input, or before the sequence the conv state (or zero).
+  // Rows past the segment end repeat its last token, as the direct loads do.
+  uint32_t halo[kConv ? kConvWidth - 1 : 1];
+  auto conv_halo_load = [&](int ln, int c0, int nv) {
+    const int cp = ln & 31;
+    const int first = it.seq0 - c0;  // chunk row of the sequence's first token (<= 0)
+    const char *xc = reinterpret_cast<const char *>(xg + (int64_t)c0 * p.x_st) + 4 * cp;
+    // one row past the sequence's conv state rows: row first - d sits d rows before it
+    const char *st = p.conv_state
+                         ? reinterpret_cast<const char *>(p.conv_state) +
+                               (((int64_t)it.row * (kConvWidth - 1) + (kConvWidth - 1)) * p.conv_ch +
+                                h * kHeadDim + 2 * cp) * 2
+                         : nullptr;
+#pragma unroll
+    for (int k = 0; k < kConvWidth - 1; ++k) {
+      const int r = min(32 * W - (kConvWidth - 1) + k, nv - 1);  // chunk row (negative: before the chunk)
+      const bool before = r < first;
+      const char *src = (before && st) ? st - (int64_t)(first - r) * p.conv_ch * 2
+                                       : xc + max(r, first) * (int)xst * 2;
+      const uint32_t v = *reinterpret_cast<const uint32_t *>(src);
+      halo[k] = (before && !st) ? 0u : v;
+    }
+  };
+  // the two channels' taps and biases: loaded ahead of the wait for the
+  // tile, so the conv does not wait for them
+  float cwt[kConv ? 2 : 1][4], cbias[kConv ? 2 : 1];
+  auto conv_taps_load = [&](int ln) {
+    const int ch = h * kHeadDim + 2 * (ln & 31);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float4 wv = *reinterpret_cast<const float4 *>(p.conv_w + (int64_t)(ch + i) * kConvWidth);
+      cwt[i][0] = wv.x; cwt[i][1] = wv.y; cwt[i][2] = wv.z; cwt[i][3] = wv.w;
+      cbias[i] = p.conv_b ? p.conv_b[ch + i] : 0.f;
+    }
+  };
+  // rows r0 + j0 .. r0 + j0 + 7 of this lane's group from raw[0..10] = rows
+  // r0 + j0 - 3 .. r0 + j0 + 7
+  auto conv_rows8 = [&](int ln, int j0, const uint32_t *raw) {
+    const int cp = ln & 31, r0 = 32 * W + 16 * (ln >> 5);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float u[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        auto v = [&](int k) { return i ? hi_bf16(raw[k]) : lo_bf16(raw[k]); };
+        float a = cbias[i];
+        a = fmaf(cwt[i][0], v(j), a);
+        a = fmaf(cwt[i][1], v(j + 1), a);
+        a = fmaf(cwt[i][2], v(j + 2), a);
+        a = fmaf(cwt[i][3], v(j + 3), a);
+        u[i] = silu_f32(a);
+      }
+      lds_st<uint32_t>(sm.X + off128(r0 + j0 + j, 2 * cp), pack2_bf16(u[0], u[1]));
+    }
+  };
+  // In two halves, each reading all it needs before writing: the group's
+  // rows 8..15 first (reads rows 5..15), then rows 0..7 (reads rows 0..7,
+  // untouched so far, and the 3 rows before the group, taken at the start:
+  // group 1's are group 0's rows 13..15, which the first half overwrites).
+  auto conv_in_place = [&](int ln) {
+    const int cp = ln & 31, rg = ln >> 5;
+    const int r0 = 32 * W + 16 * rg;
+    uint32_t pre[kConvWidth - 1];
+#pragma unroll
+    for (int k = 0; k < kConvWidth - 1; ++k) {
+      const uint32_t l = lds_ld<uint32_t>(sm.X + off128(max(r0 - (kConvWidth - 1) + k, 32 * W), 2 * cp));
+      pre[k] = rg ? l : halo[k];
+    }
+    uint32_t raw[8 + kConvWidth - 1];
+#pragma unroll
+    for (int k = 0; k < 8 + kConvWidth - 1; ++k) raw[k] = lds_ld<uint32_t>(sm.X + off128(r0 + 5 + k, 2 * cp));
+    conv_rows8(ln, 8, raw);
+#pragma unroll
+    for (int k = 0; k < kConvWidth - 1; ++k) raw[k] = pre[k];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) raw[kConvWidth - 1 + k] = lds_ld<uint32_t>(sm.X + off128(r0 + k, 2 * cp));
+    conv_rows8(ln, 0, raw);
+  };
   auto issue_tiles = [&](int ln, int c0, int nv) {
     issue_b(ln, c0, nv, 32 * W, std::integral_constant<int, 8>{});
     issue_x(ln, c0, nv);
+    if (kConv) conv_halo_load(ln, c0, nv);
   };
   // C rows i of this wave's i-block: this lane's 8 k-steps of the MFMA operand
   u32x4 cf[8];
@@ -446,7 +535,9 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
     }
     if (kFull) write_state_lds(ln);
     issue_tiles(ln, it.tok0, nv0);  // last, for the same reason as in the loop
+    if (kConv) conv_taps_load(ln);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
+    if (kConv) conv_in_place(ln);
     __syncthreads();
   }
 
@@ -699,9 +790,16 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
         if (rr + 8 * k < nv) *reinterpret_cast<u32x4 *>(yc + yo0 + k * ystep) = v;
       }
     }
+    // kConv: the next tile's halo rows and the taps, issued once y is out of
+    // the registers; the wait below is for the y stores too, which covers them
+    if (kConv && has_next) {
+      conv_halo_load(L.lane, c1, nvn);
+      conv_taps_load(L.lane);
+    }
     // after this wave's y read-back: the arrays overlay its staging rows
     if (W == kDtWave && has_next) nd.store(sm.cs, sm.dt, sm.w, sm.v, sm.misc);
     __builtin_amdgcn_s_waitcnt(0);       // this wave's direct loads of the next chunk have landed
+    if (kConv && has_next) conv_in_place(L.lane);  // (this chunk's reads of the tile ended at barrier A)
     __syncthreads();                     // B: ... and every wave's
   }
 
@@ -724,7 +822,7 @@ __device__ __forceinline__ void run_wave(const ScanParams &p, const ScanPlan &pl
   }
 }
 
-template <bool kFull>
+template <bool kFull, bool kConv>
 __global__ __launch_bounds__(kThr, 2) void chunk_scan_bf16_kernel(ScanParams p, ScanPlan plan, char *ws) {
   __shared__ __attribute__((aligned(16))) Smem smem;
   lds_f32 *small = (lds_f32 *)((lds_u8 *)smem.Y + kSmallOff);
@@ -736,10 +834,10 @@ __global__ __launch_bounds__(kThr, 2) void chunk_scan_bf16_kernel(ScanParams p, 
   if (!get_item(p, plan, ws, item, it)) return;
   if (!kFull && it.last) return;  // the pre-pass only needs segments that have a successor
   switch (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) {
-    case 0: run_wave<kFull, 0>(p, plan, ws, it, item, h, g, sm); break;
-    case 1: run_wave<kFull, 1>(p, plan, ws, it, item, h, g, sm); break;
-    case 2: run_wave<kFull, 2>(p, plan, ws, it, item, h, g, sm); break;
-    default: run_wave<kFull, 3>(p, plan, ws, it, item, h, g, sm); break;
+    case 0: run_wave<kFull, kConv, 0>(p, plan, ws, it, item, h, g, sm); break;
+    case 1: run_wave<kFull, kConv, 1>(p, plan, ws, it, item, h, g, sm); break;
+    case 2: run_wave<kFull, kConv, 2>(p, plan, ws, it, item, h, g, sm); break;
+    default: run_wave<kFull, kConv, 3>(p, plan, ws, it, item, h, g, sm); break;
   }
 }
 
@@ -747,8 +845,13 @@ __global__ __launch_bounds__(kThr, 2) void chunk_scan_bf16_kernel(ScanParams p, 
 
 hipError_t launch_chunk_scan_bf16(const ScanParams &p, const ScanPlan &plan, char *ws, unsigned nblk, bool full,
                                   hipStream_t stream) {
-  if (full) hipLaunchKernelGGL(chunk_scan_bf16_kernel<true>, dim3(nblk), dim3(kThr), 0, stream, p, plan, ws);
-  else hipLaunchKernelGGL(chunk_scan_bf16_kernel<false>, dim3(nblk), dim3(kThr), 0, stream, p, plan, ws);
+  if (p.xconv) {
+    if (full) hipLaunchKernelGGL((chunk_scan_bf16_kernel<true, true>), dim3(nblk), dim3(kThr), 0, stream, p, plan, ws);
+    else hipLaunchKernelGGL((chunk_scan_bf16_kernel<false, true>), dim3(nblk), dim3(kThr), 0, stream, p, plan, ws);
+  } else {
+    if (full) hipLaunchKernelGGL((chunk_scan_bf16_kernel<true, false>), dim3(nblk), dim3(kThr), 0, stream, p, plan, ws);
+    else hipLaunchKernelGGL((chunk_scan_bf16_kernel<false, false>), dim3(nblk), dim3(kThr), 0, stream, p, plan, ws);
+  }
   return hipGetLastError();
 }
 

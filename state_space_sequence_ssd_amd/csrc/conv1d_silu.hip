@@ -107,7 +107,7 @@ __global__ __launch_bounds__(kThreads) void conv1d_silu_kernel(ConvParams p) {
         Vec8<T>::load(x + (int64_t)(t0 - k) * p.x_st, v);
       } else if (sin) {
         // v(t0 - k) = state row (t0 - k) - start + 3 with start = t0 - d
-        Vec8<T>::load(sin + ((int64_t)cur * (kConvWidth - 1) + (3 - k + d)) * p.CH + c0, v);
+        Vec8<T>::load(sin + ((int64_t)cur * (kConvWidth - 1) + (3 - k + d)) * p.s_st + c0, v);
       } else {
         zero8<T>(v);
       }
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(kThreads) void conv1d_silu_kernel(ConvParams p) {
         cur = sq;
 #pragma unroll
         for (int r = 0; r < 3; ++r) {
-          if (sin) Vec8<T>::load(sin + ((int64_t)cur * (kConvWidth - 1) + r) * p.CH + c0, win[r]);
+          if (sin) Vec8<T>::load(sin + ((int64_t)cur * (kConvWidth - 1) + r) * p.s_st + c0, win[r]);
           else zero8<T>(win[r]);
         }
       }
@@ -189,14 +189,14 @@ __global__ __launch_bounds__(kThreads) void conv_state_out_kernel(ConvParams p, 
     x += (int64_t)s * p.x_sb;
   }
   const T *sin = reinterpret_cast<const T *>(p.state_in);
-  T *so = reinterpret_cast<T *>(p.state_out) + (int64_t)s * (kConvWidth - 1) * p.CH + c0;
+  T *so = reinterpret_cast<T *>(p.state_out) + (int64_t)s * (kConvWidth - 1) * p.s_st + c0;
   for (int r = 0; r < kConvWidth - 1; ++r) {
     const int tau = end - (kConvWidth - 1) + r;
     float v[kVec];
     if (tau >= start) Vec8<T>::load(x + (int64_t)tau * p.x_st, v);
-    else if (sin) Vec8<T>::load(sin + ((int64_t)s * (kConvWidth - 1) + (tau - start + kConvWidth - 1)) * p.CH + c0, v);
+    else if (sin) Vec8<T>::load(sin + ((int64_t)s * (kConvWidth - 1) + (tau - start + kConvWidth - 1)) * p.s_st + c0, v);
     else zero8<T>(v);
-    Vec8<T>::store(so + (int64_t)r * p.CH, v);
+    Vec8<T>::store(so + (int64_t)r * p.s_st, v);
   }
 }
 
@@ -213,15 +213,18 @@ hipError_t launch_conv1d_silu(const ConvParams &p, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (p.state_out) {
-    const int rows = p.seq_idx ? p.num_seqs : p.batch;
-    const int64_t n = (int64_t)rows * nvec;
-    dim3 grid((unsigned)((n + kThreads - 1) / kThreads)), block(kThreads);
-    if (p.bf16) hipLaunchKernelGGL(conv_state_out_kernel<bf16_t>, grid, block, 0, stream, p, rows);
-    else hipLaunchKernelGGL(conv_state_out_kernel<float>, grid, block, 0, stream, p, rows);
-    return hipGetLastError();
-  }
-  return hipSuccess;
+  return p.state_out ? launch_conv_state_out(p, stream) : hipSuccess;
+}
+
+hipError_t launch_conv_state_out(const ConvParams &p, hipStream_t stream) {
+  const int nvec = p.CH / kVec;
+  const int rows = p.seq_idx ? p.num_seqs : p.batch;
+  const int64_t n = (int64_t)rows * nvec;
+  if (n == 0) return hipSuccess;
+  dim3 grid((unsigned)((n + kThreads - 1) / kThreads)), block(kThreads);
+  if (p.bf16) hipLaunchKernelGGL(conv_state_out_kernel<bf16_t>, grid, block, 0, stream, p, rows);
+  else hipLaunchKernelGGL(conv_state_out_kernel<float>, grid, block, 0, stream, p, rows);
+  return hipGetLastError();
 }
 
 }  // namespace ssd

@@ -28,8 +28,11 @@ struct ConvParams {
   const float *w, *bias;
   const int32_t *seq_idx; int num_seqs;
   const void *state_in; void *state_out;
+  int64_t s_st;  // elements per conv-state row (the state's full channel count)
 };
 hipError_t launch_conv1d_silu(const ConvParams &p, hipStream_t stream);
+// the conv-state export alone (state_out from the last inputs of each sequence)
+hipError_t launch_conv_state_out(const ConvParams &p, hipStream_t stream);
 
 struct DecodeParams {
   int bf16;
@@ -111,6 +114,14 @@ struct ScanParams {
   const int32_t *seq_idx; int num_seqs;
   const float *init; float *final_state;
   void *y; int64_t y_sb, y_st;
+  // bf16 chunk kernel only: x is the raw conv input of the x channels (head h
+  // at columns h * headdim), and the kernel applies conv1d(4) + SiLU to it on
+  // the way into its x tile.  conv_w / conv_b: the conv's taps and bias with
+  // the x channels first (row h * headdim + p); conv_state: (rows, 3, conv_ch)
+  // inputs before each sequence (x channels at column 0), or null (zeros).
+  int xconv;
+  const float *conv_w, *conv_b;
+  const void *conv_state; int64_t conv_ch;
 };
 
 // fp32 batch-row sequences up to this length run as one masked quadratic form

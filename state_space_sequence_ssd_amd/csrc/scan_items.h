@@ -13,6 +13,7 @@ constexpr int kPN = kHeadDim * kDState;
 // ---------------------------------------------------------------------------
 struct Item {
   int row, k, tok0, tok1, first, last, item;
+  int seq0;      // first token of the item's sequence
   int64_t boff;  // batch row used for strides (0 in packed mode)
 };
 
@@ -45,6 +46,7 @@ __device__ __forceinline__ bool get_item(const ScanParams &p, const ScanPlan &pl
     it.first = it.k == 0;
     it.last = it.k == plan.nseg - 1;
     it.boff = it.row;
+    it.seq0 = 0;
     return true;
   }
   const PlanView v = plan_view(plan, ws);
@@ -57,6 +59,7 @@ __device__ __forceinline__ bool get_item(const ScanParams &p, const ScanPlan &pl
   it.first = it.k == 0;
   it.last = it.k == v.seq_nseg[it.row] - 1;
   it.boff = 0;
+  it.seq0 = start;
   return true;
 }
 

@@ -51,6 +51,20 @@ class SsdScanArgs(ctypes.Structure):
 _SCAN_ARGS_SIZE = ctypes.sizeof(SsdScanArgs)
 
 
+class SsdConvScanArgs(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("dtype", _i32),
+                ("batch", _i32), ("seqlen", _i32), ("nheads", _i32), ("headdim", _i32),
+                ("dstate", _i32), ("ngroups", _i32), ("chunk_size", _i32), ("seg_chunks", _i32),
+                ("conv_width", _i32),
+                ("xBC", _vp), ("xBC_stride_batch", _i64), ("xBC_stride_token", _i64),
+                ("conv_weight", _vp), ("conv_bias", _vp),
+                ("dt", _vp), ("dt_stride_batch", _i64), ("dt_stride_token", _i64),
+                ("dt_bias", _vp), ("A", _vp), ("D", _vp), ("seq_idx", _vp), ("num_seqs", _i32),
+                ("conv_state_in", _vp), ("conv_state_out", _vp),
+                ("initial_state", _vp), ("final_state", _vp),
+                ("y", _vp), ("y_stride_batch", _i64), ("y_stride_token", _i64)]
+
+
 class SsdDecodeArgs(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("dtype", _i32),
                 ("batch", _i32), ("nheads", _i32), ("headdim", _i32), ("dstate", _i32),
@@ -92,7 +106,7 @@ class SsdScanBwdArgs(ctypes.Structure):
 
 
 EXPORTS = ["ssd_conv1d_silu", "ssd_chunk_scan_workspace_size", "ssd_chunk_scan_fwd",
-           "ssd_chunk_scan_fwd_noalloc", "ssd_chunk_scan_bwd_workspace_size", "ssd_chunk_scan_bwd",
+           "ssd_chunk_scan_fwd_noalloc", "ssd_conv_scan_workspace_size", "ssd_conv_scan_fwd", "ssd_chunk_scan_bwd_workspace_size", "ssd_chunk_scan_bwd",
            "ssd_gated_rmsnorm", "ssd_decode_step", "ssd_decode_step_mimo", "ssd_last_error", "ssd_version"]
 NOALLOC_SCRATCH_BYTES = 96 * 1024 * 1024   # SSD_NOALLOC_SCRATCH_BYTES
 
@@ -116,6 +130,10 @@ def load_library(path: str = LIB_PATH):
     lib.ssd_chunk_scan_fwd.restype = ctypes.c_int
     lib.ssd_chunk_scan_fwd_noalloc.argtypes = [ctypes.POINTER(SsdScanArgs), _vp]
     lib.ssd_chunk_scan_fwd_noalloc.restype = ctypes.c_int
+    lib.ssd_conv_scan_workspace_size.argtypes = [ctypes.POINTER(SsdConvScanArgs)]
+    lib.ssd_conv_scan_workspace_size.restype = ctypes.c_size_t
+    lib.ssd_conv_scan_fwd.argtypes = [ctypes.POINTER(SsdConvScanArgs), _vp, ctypes.c_size_t, _vp]
+    lib.ssd_conv_scan_fwd.restype = ctypes.c_int
     lib.ssd_gated_rmsnorm.argtypes = [ctypes.POINTER(SsdNormArgs), _vp]
     lib.ssd_gated_rmsnorm.restype = ctypes.c_int
     lib.ssd_chunk_scan_bwd_workspace_size.argtypes = [ctypes.POINTER(SsdScanBwdArgs)]
@@ -354,6 +372,96 @@ def ssd_chunk_scan_fwd_noalloc(x: torch.Tensor, dt: torch.Tensor, A: torch.Tenso
     a = _scan_args(x, dt, A, B, C, dt_bias, D, seq_idx, num_seqs, initial_state, final_state, y,
                    chunk_size, seg_chunks)
     _check(lib.ssd_chunk_scan_fwd_noalloc(ctypes.byref(a), _stream(stream)))
+    return y
+
+
+def _conv_scan_args(xBC, conv_weight, dt, A, nheads, ngroups, headdim, dstate, conv_bias, dt_bias, D,
+                    seq_idx, num_seqs, conv_state_in, conv_state_out, initial_state, final_state, y,
+                    chunk_size, seg_chunks) -> SsdConvScanArgs:
+    if xBC.dim() != 3 or dt.dim() != 3:
+        raise ValueError("xBC (batch, L, conv_dim) and dt (batch, L, nheads) expected")
+    batch, L, CH = xBC.shape
+    H, G, P, N = int(nheads), int(ngroups), int(headdim), int(dstate)
+    if CH != H * P + 2 * G * N:
+        raise ValueError(f"xBC has {CH} channels; nheads*headdim + 2*ngroups*dstate = {H * P + 2 * G * N}")
+    code = _dtype_code(xBC)
+    _same_dtype(xBC, dt=dt, y=y, conv_state_in=conv_state_in, conv_state_out=conv_state_out)
+    if conv_weight.dim() != 2 or conv_weight.shape[0] != CH:
+        raise ValueError(f"conv_weight must be (conv_dim={CH}, width)")
+    K = conv_weight.shape[1]
+    _f32(conv_weight, "conv_weight")
+    _f32(conv_bias, "conv_bias", numel=CH)
+    _shape(dt, "dt", (batch, L, H))
+    _shape(y, "y", (batch, L, H, P))
+    _f32(A, "A", numel=H)
+    _f32(dt_bias, "dt_bias", numel=H)
+    _f32(D, "D", numel=H)
+    _seq_idx(seq_idx, L, num_seqs)
+    rows = int(num_seqs) if seq_idx is not None else batch
+    for name, t in (("conv_state_in", conv_state_in), ("conv_state_out", conv_state_out)):
+        _shape(t, name, (rows, K - 1, CH))
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    _f32(initial_state, "initial_state", shape=(rows, H, P, N))
+    _f32(final_state, "final_state", shape=(rows, H, P, N))
+    _on_gpu(xBC, conv_weight=conv_weight, conv_bias=conv_bias, dt=dt, A=A, y=y, dt_bias=dt_bias, D=D,
+            seq_idx=seq_idx, conv_state_in=conv_state_in, conv_state_out=conv_state_out,
+            initial_state=initial_state, final_state=final_state)
+    xs, ds = xBC.stride(), dt.stride()
+    ys = y.stride() if y is not None else (0, 0, P, 1)
+    if L > 0:
+        if xs[2] != 1:
+            raise ValueError("xBC must have unit channel stride")
+        if ys[3] != 1 or ys[2] != P:
+            raise ValueError(f"y: the last two dims must be packed (strides ({P}, 1))")
+        if ds[2] != 1:
+            raise ValueError("dt: head dim must be unit-stride")
+    return SsdConvScanArgs(ctypes.sizeof(SsdConvScanArgs), code, batch, L, H, P, N, G, chunk_size, seg_chunks, K,
+                           xBC.data_ptr(), xs[0], xs[1], conv_weight.data_ptr(), _ptr(conv_bias),
+                           dt.data_ptr(), ds[0], ds[1], _ptr(dt_bias), A.data_ptr(), _ptr(D),
+                           _ptr(seq_idx), int(num_seqs or 0), _ptr(conv_state_in), _ptr(conv_state_out),
+                           _ptr(initial_state), _ptr(final_state), _ptr(y), ys[0], ys[1])
+
+
+def ssd_conv_scan_workspace_size(xBC, conv_weight, dt, A, nheads, ngroups, headdim=64, dstate=128,
+                                 seq_idx=None, num_seqs=None, chunk_size=128, seg_chunks=0) -> int:
+    lib = load_library()
+    y = torch.empty((xBC.shape[0], xBC.shape[1], nheads, headdim), dtype=xBC.dtype, device=xBC.device)
+    a = _conv_scan_args(xBC, conv_weight, dt, A, nheads, ngroups, headdim, dstate, None, None, None,
+                        seq_idx, num_seqs, None, None, None, None, y, chunk_size, seg_chunks)
+    n = lib.ssd_conv_scan_workspace_size(ctypes.byref(a))
+    if n == ctypes.c_size_t(-1).value:
+        raise SsdError(1, lib.ssd_last_error().decode())
+    return int(n)
+
+
+def ssd_conv_scan_fwd(xBC: torch.Tensor, conv_weight: torch.Tensor, dt: torch.Tensor, A: torch.Tensor,
+                      nheads: int, ngroups: int, headdim: int = 64, dstate: int = 128,
+                      conv_bias: Optional[torch.Tensor] = None, dt_bias: Optional[torch.Tensor] = None,
+                      D: Optional[torch.Tensor] = None, seq_idx: Optional[torch.Tensor] = None,
+                      num_seqs: Optional[int] = None, conv_state_in: Optional[torch.Tensor] = None,
+                      conv_state_out: Optional[torch.Tensor] = None,
+                      initial_state: Optional[torch.Tensor] = None,
+                      final_state: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+                      chunk_size: int = 128, seg_chunks: int = 0,
+                      workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """conv1d(4) + SiLU of xBC (batch, L, nheads*headdim + 2*ngroups*dstate; columns
+    x | B | C) and the chunked scan of its output, in one call (the x channels'
+    conv runs inside the bf16 scan kernel).  Returns y (batch, L, nheads, headdim)."""
+    lib = load_library()
+    if y is None:
+        y = torch.empty((xBC.shape[0], xBC.shape[1], nheads, headdim), dtype=xBC.dtype, device=xBC.device)
+    a = _conv_scan_args(xBC, conv_weight, dt, A, nheads, ngroups, headdim, dstate, conv_bias, dt_bias, D,
+                        seq_idx, num_seqs, conv_state_in, conv_state_out, initial_state, final_state, y,
+                        chunk_size, seg_chunks)
+    if workspace is None:
+        need = lib.ssd_conv_scan_workspace_size(ctypes.byref(a))
+        if need == ctypes.c_size_t(-1).value:
+            raise SsdError(1, lib.ssd_last_error().decode())
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=xBC.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.ssd_conv_scan_fwd(ctypes.byref(a), _ptr(workspace), ws_bytes, _stream(stream)))
     return y
 
 

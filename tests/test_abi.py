@@ -34,7 +34,8 @@ def test_struct_layouts_match_header(tmp_path):
     import subprocess
     structs = {"ssd_conv_args": ssd.SsdConvArgs, "ssd_scan_args": ssd.SsdScanArgs,
                "ssd_decode_args": ssd.SsdDecodeArgs, "ssd_norm_args": ssd.SsdNormArgs,
-               "ssd_mimo_decode_args": ssd.SsdMimoDecodeArgs, "ssd_scan_bwd_args": ssd.SsdScanBwdArgs}
+               "ssd_mimo_decode_args": ssd.SsdMimoDecodeArgs, "ssd_scan_bwd_args": ssd.SsdScanBwdArgs,
+               "ssd_conv_scan_args": ssd.SsdConvScanArgs}
     lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "ssd.h"', "int main(void) {"]
     for cname, py in structs.items():
         lines.append(f'printf("{cname} sizeof %zu\\n", sizeof({cname}));')
@@ -123,6 +124,61 @@ def test_workspace_sizes_and_too_small():
     assert lib.ssd_chunk_scan_workspace_size(ctypes.byref(p)) > 0
     bad = scan_args(headdim=16)
     assert lib.ssd_chunk_scan_workspace_size(ctypes.byref(bad)) == ctypes.c_size_t(-1).value
+
+
+def conv_scan_args(**kw):
+    a = ssd.SsdConvScanArgs()
+    a.struct_size = ctypes.sizeof(ssd.SsdConvScanArgs)
+    a.dtype = ssd.SSD_DTYPE_BF16
+    a.batch, a.seqlen, a.nheads, a.headdim, a.dstate, a.ngroups, a.chunk_size = 4, 4096, 128, 64, 128, 8, 128
+    a.conv_width = 4
+    cd = 128 * 64 + 2 * 8 * 128
+    a.xBC, a.xBC_stride_batch, a.xBC_stride_token = FAKE, 4096 * cd, cd
+    a.y, a.y_stride_batch, a.y_stride_token = FAKE, 4096 * 8192, 8192
+    a.conv_weight = FAKE
+    a.dt, a.dt_stride_batch, a.dt_stride_token = FAKE, 4096 * 128, 128
+    a.A = FAKE
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def conv_scan_rc(a, ws=None, ws_bytes=1 << 40):
+    return ssd.load_library().ssd_conv_scan_fwd(ctypes.byref(a), ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("struct_size", 8, 1), ("dtype", 7, 2), ("conv_width", 3, 2), ("conv_weight", None, 1), ("xBC", None, 1),
+    ("xBC", FAKE + 2, 4), ("xBC_stride_token", 8192, 1), ("xBC_stride_token", 10240 + 2, 4),
+    ("conv_weight", FAKE + 4, 4), ("conv_state_in", FAKE + 8, 4), ("conv_state_out", FAKE + 8, 4),
+    ("batch", 0, 1), ("ngroups", 3, 1), ("headdim", 32, 2), ("A", None, 1), ("y", None, 1), ("dt", None, 1),
+    ("y_stride_token", 1024, 1), ("final_state", FAKE + 8, 4),
+])
+def test_conv_scan_argument_errors(field, value, code):
+    a = conv_scan_args(**{field: value})
+    assert conv_scan_rc(a) == code
+    assert ssd.load_library().ssd_last_error().decode()
+
+
+def test_conv_scan_workspace():
+    """The workspace holds the B|C conv output (bf16; every channel for fp32) and the scan's own."""
+    lib = ssd.load_library()
+    need = lib.ssd_conv_scan_workspace_size(ctypes.byref(conv_scan_args()))
+    assert need == 4 * 4096 * 2 * 8 * 128 * 2  # no scan workspace at this shape
+    need32 = lib.ssd_conv_scan_workspace_size(ctypes.byref(conv_scan_args(dtype=ssd.SSD_DTYPE_F32,
+                                                                             xBC_stride_batch=4096 * 10240)))
+    assert need32 == 4 * 4096 * 10240 * 4
+    a = conv_scan_args()
+    assert conv_scan_rc(a, ws=FAKE, ws_bytes=need - 1) == 3
+    assert conv_scan_rc(a, ws=None, ws_bytes=need) == 3
+    assert conv_scan_rc(a, ws=FAKE + 16, ws_bytes=need) == 4
+    # segmented: the scan's per-segment states come after the conv output
+    seg = conv_scan_args(batch=1, seqlen=16384, nheads=64, xBC_stride_batch=16384 * (64 * 64 + 2048),
+                         xBC_stride_token=64 * 64 + 2048, y_stride_token=64 * 64,
+                         dt_stride_batch=16384 * 64, dt_stride_token=64)
+    conv_part = 16384 * 2048 * 2
+    assert lib.ssd_conv_scan_workspace_size(ctypes.byref(seg)) > conv_part
+    assert lib.ssd_conv_scan_workspace_size(ctypes.byref(conv_scan_args(headdim=16))) == ctypes.c_size_t(-1).value
 
 
 def conv_args(**kw):

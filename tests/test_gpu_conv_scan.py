@@ -1,0 +1,202 @@
+"""ssd_conv_scan_fwd (conv1d(4) + SiLU fused into the chunked scan) on the GPU.
+
+Two bars, through the C ABI:
+  * the fused call equals ssd_conv1d_silu followed by ssd_chunk_scan_fwd bit
+    for bit (y, final states, conv-state export): the bf16 kernel repeats the
+    conv's fp32 arithmetic in the same order and rounds where the conv would
+    have stored, and fp32 runs those two kernels;
+  * against the oracle's conv + scan: max|gpu - oracle| / max|oracle| <= 2e-2
+    (bf16 inputs) or 1e-4 (fp32); the conv-state export exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from state_space_sequence_ssd_amd import inputs, ssd
+from tests.gpu_helpers import BF, DEV, rel, split_xbc, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+TOL = {True: 2e-2, False: 1e-4}
+
+
+def W(name, batch, L, H, G, bf16=True, init=0.0, lens=None):
+    if lens is not None:
+        L = int(np.sum(lens))
+    return inputs.ScanWorkload(name, batch, L, H, G, bf16=bf16, conv=True, final_state=True,
+                               packed_lengths=None if lens is None else np.asarray(lens), init_std=init)
+
+
+def make(w, seed, conv_bias=True, state_in=True):
+    d = inputs.make_scan_inputs(w, seed=seed)
+    if conv_bias:
+        d["conv_b"] = (np.random.default_rng(seed + 100).standard_normal(w.conv_dim) * 0.1).astype(np.float32)
+    if state_in:
+        d["conv_state_in"] = inputs.normal((w.num_seqs, 3, w.conv_dim), 1.0, seed, 6, w.bf16)
+    return d
+
+
+def _dev_args(d, w):
+    dt_t = BF if w.bf16 else torch.float32
+    seq = to_dev(d["seq_idx"]) if "seq_idx" in d else None
+    return dict(
+        dt_t=dt_t, seq=seq, nseq=w.num_seqs if seq is not None else None,
+        xbc=to_dev(d["xBC"], dt_t), cw=to_dev(d["conv_w"]),
+        cb=to_dev(d["conv_b"]) if "conv_b" in d else None,
+        si=to_dev(d["conv_state_in"], dt_t) if "conv_state_in" in d else None,
+        dt=to_dev(d["dt"], dt_t), A=to_dev(d["A"]), dtb=to_dev(d["dt_bias"]), D=to_dev(d["D"]),
+        init=to_dev(d["initial_state"]) if "initial_state" in d else None)
+
+
+def run_fused(d, w, seg_chunks=0):
+    a = _dev_args(d, w)
+    H, G = w.nheads, w.ngroups
+    fs = torch.full((w.num_seqs, H, 64, 128), float("nan"), device=DEV)
+    so = torch.full((w.num_seqs, 3, w.conv_dim), float("nan"), dtype=a["dt_t"], device=DEV)
+    y = ssd.ssd_conv_scan_fwd(a["xbc"], a["cw"], a["dt"], a["A"], H, G, conv_bias=a["cb"], dt_bias=a["dtb"],
+                              D=a["D"], seq_idx=a["seq"], num_seqs=a["nseq"], conv_state_in=a["si"],
+                              conv_state_out=so, initial_state=a["init"], final_state=fs, seg_chunks=seg_chunks)
+    torch.cuda.synchronize()
+    return y, fs, so
+
+
+def run_unfused(d, w, seg_chunks=0):
+    a = _dev_args(d, w)
+    H, G = w.nheads, w.ngroups
+    fs = torch.full((w.num_seqs, H, 64, 128), float("nan"), device=DEV)
+    so = torch.full((w.num_seqs, 3, w.conv_dim), float("nan"), dtype=a["dt_t"], device=DEV)
+    v = ssd.ssd_conv1d_silu(a["xbc"], a["cw"], bias=a["cb"], seq_idx=a["seq"], num_seqs=a["nseq"],
+                            conv_state_in=a["si"], conv_state_out=so)
+    x, B, C = split_xbc(v, H, G)
+    y = ssd.ssd_chunk_scan_fwd(x, a["dt"], a["A"], B, C, dt_bias=a["dtb"], D=a["D"], seq_idx=a["seq"],
+                               num_seqs=a["nseq"], initial_state=a["init"], final_state=fs,
+                               seg_chunks=seg_chunks)
+    torch.cuda.synchronize()
+    return y, fs, so
+
+
+def oracle_ref(d, w):
+    H, G = w.nheads, w.ngroups
+    seq = d.get("seq_idx")
+    nseq = w.num_seqs if seq is not None else None
+    v, so = oracle.conv1d_silu(d["xBC"], d["conv_w"], bias=d.get("conv_b"), seq_idx=seq, num_seqs=nseq,
+                               conv_state_in=d.get("conv_state_in"), want_state_out=True)
+    x, B, C = split_xbc(v, H, G)
+    y, fs = oracle.ssd_scan(x, d["dt"], d["dt_bias"], d["A"], B, C, d["D"], seq_idx=seq, num_seqs=nseq,
+                            initial_state=d.get("initial_state"), want_final_state=True)
+    return y, fs, so
+
+
+def assert_same(a, b, what):
+    for u, v, name in zip(a, b, ("y", "final_state", "conv_state_out")):
+        assert torch.equal(u, v), f"{what}: fused and unfused {name} differ"
+
+
+CASES = [
+    # (workload, seg_chunks, conv bias, conv state in)
+    (W("cs_b2_l300_h8_g2_init", 2, 300, 8, 2, init=0.3), 0, True, True),
+    (W("cs_b2_l300_h8_g2_nostate", 2, 300, 8, 2), 0, False, False),
+    # 128-token segments: every segment after the first takes its halo from the previous one
+    (W("cs_seg1_b1_l700_h8_g2_init", 1, 700, 8, 2, init=0.3), 1, True, True),
+    (W("cs_b1_l1_h8_g1", 1, 1, 8, 1), 0, True, True),
+    (W("cs_b1_l3_h8_g1_nostate", 1, 3, 8, 1), 0, True, False),
+    # packed: sequences of 1..3 tokens take their whole window from the conv state;
+    # starts in the middle of 128-token tiles
+    (W("cs_packed_h8_g2_init", 1, 0, 8, 2, init=0.3, lens=[1, 3, 200, 129, 128, 64, 300, 2]), 0, True, True),
+    (W("cs_packed_seg1_h16_g8", 1, 0, 16, 8, lens=[77, 5, 260, 0, 400]), 1, True, True),
+    (W("cs_packed_nostate_h8_g2", 1, 0, 8, 2, lens=[2, 130, 1, 50]), 0, False, False),
+    # fp32 runs conv then scan through the workspace
+    (W("cs_fp32_b2_l200_h8_g2_init", 2, 200, 8, 2, bf16=False, init=0.3), 0, True, True),
+    (W("cs_fp32_packed_h8_g2", 1, 0, 8, 2, bf16=False, lens=[3, 1200, 17]), 0, True, True),
+]
+
+
+@pytest.mark.parametrize("w,seg,bias,state", CASES, ids=[c[0].name for c in CASES])
+def test_conv_scan_small(w, seg, bias, state):
+    print(f"case {w.name} seg={seg} bias={bias} state={state}", flush=True)
+    d = make(w, seed=11, conv_bias=bias, state_in=state)
+    fused = run_fused(d, w, seg)
+    assert_same(fused, run_unfused(d, w, seg), w.name)
+    ry, rf, rso = oracle_ref(d, w)
+    y, fs, so = (to_np(t) for t in fused)
+    ey, ef = rel(y, ry), rel(fs, rf)
+    print(f"  y rel err {ey:.3e}  final-state rel err {ef:.3e}", flush=True)
+    assert ey <= TOL[w.bf16] and ef <= TOL[w.bf16]
+    assert np.array_equal(so, rso), "conv state export must be exact"
+
+
+def test_conv_scan_empty_sequence():
+    """seqlen 0: the final states are the initial ones, the conv state passes through."""
+    w = W("cs_l0", 2, 0, 8, 2, init=0.3)
+    d = make(w, seed=3)
+    y, fs, so = run_fused(d, w)
+    assert y.shape == (2, 0, 8, 64)
+    assert np.array_equal(to_np(fs), d["initial_state"].astype(np.float64))
+    assert np.array_equal(to_np(so), d["conv_state_in"].astype(np.float64))
+
+
+def test_conv_scan_in_place_conv_state():
+    """conv_state_out may be conv_state_in: the export runs after every read of the input state."""
+    w = W("cs_inplace_packed", 1, 0, 8, 2, lens=[2, 70, 1, 140])
+    d = make(w, seed=5)
+    ref = run_fused(d, w)
+    a = _dev_args(d, w)
+    st = a["si"].clone()
+    fs = torch.empty((w.num_seqs, 8, 64, 128), device=DEV)
+    y = ssd.ssd_conv_scan_fwd(a["xbc"], a["cw"], a["dt"], a["A"], 8, 2, conv_bias=a["cb"], dt_bias=a["dtb"],
+                              D=a["D"], seq_idx=a["seq"], num_seqs=a["nseq"], conv_state_in=st,
+                              conv_state_out=st, final_state=fs)
+    torch.cuda.synchronize()
+    assert torch.equal(y, ref[0]) and torch.equal(fs, ref[1]) and torch.equal(st, ref[2])
+
+
+def test_conv_scan_repeat_bitwise():
+    w = W("cs_repeat", 2, 500, 16, 4, init=0.3)
+    d = make(w, seed=9)
+    a, b = run_fused(d, w), run_fused(d, w)
+    assert_same(a, b, "repeat")
+
+
+def _full_vs_unfused(w, seed):
+    print(f"case {w.name} seed={seed} (fused vs unfused, every element)", flush=True)
+    d = make(w, seed=seed, conv_bias=False, state_in=False)
+    fused = run_fused(d, w)
+    unfused = run_unfused(d, w)
+    assert_same(fused, unfused, w.name)
+
+
+def test_full_nemotron_h_8b_fused():
+    # the unfused path at this shape is checked against the oracle element by
+    # element in test_gpu_parity; equality carries that over
+    _full_vs_unfused(inputs.nemotron_h_8b(), seed=1)
+
+
+def test_full_nemotron3_nano_fused():
+    _full_vs_unfused(inputs.nemotron3_nano(), seed=2)
+
+
+def test_full_packed_3b_conv_fused():
+    """The packed 3B stream with its conv: fused == unfused, and sampled sequences against the oracle."""
+    base = inputs.packed_3b()
+    w = inputs.ScanWorkload("packed_3b_h40_32seqs_conv", 1, base.seqlen, 40, 8, bf16=True, conv=True,
+                            final_state=True, packed_lengths=base.packed_lengths, init_std=base.init_std)
+    print(f"case {w.name} (fused vs unfused; oracle on sampled sequences)", flush=True)
+    d = make(w, seed=3)
+    fused = run_fused(d, w)
+    assert_same(fused, run_unfused(d, w), w.name)
+    y, fs, so = (to_np(t) for t in fused)
+    lens = np.asarray(w.packed_lengths)
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    for s in (0, 7, len(lens) - 1):
+        sl = slice(int(starts[s]), int(starts[s] + lens[s]))
+        sub = {k: d[k][:, sl] for k in ("xBC", "dt")}
+        sub.update({k: d[k] for k in ("conv_w", "conv_b", "dt_bias", "A", "D")})
+        sub["conv_state_in"] = d["conv_state_in"][[s]]
+        sub["initial_state"] = d["initial_state"][[s]]
+        ws = inputs.ScanWorkload("seq", 1, int(lens[s]), 40, 8, bf16=True, conv=True, final_state=True)
+        ry, rf, rso = oracle_ref(sub, ws)
+        ey, ef = rel(y[:, sl], ry), rel(fs[[s]], rf)
+        print(f"  sequence {s} ({lens[s]} tokens): y rel err {ey:.3e}  final-state {ef:.3e}", flush=True)
+        assert ey <= TOL[True] and ef <= TOL[True]
+        assert np.array_equal(so[[s]], rso)
