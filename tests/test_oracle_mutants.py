@@ -80,10 +80,22 @@ def test_mutant_is_caught(name, tmp_path):
     mpath = tmp_path / "mutant.c"
     mpath.write_text(src.replace(old, new))
     lib = oracle._load(build(str(mpath), str(tmp_path / "libmutant.so"), extra=("-Wno-unused",)))
-    caught = []
-    for pin in ALL_PINS:
+    # the pins of the mutant's own part first; the first pin that fails is enough
+    for pin in sorted(ALL_PINS, key=lambda f: not _related(name, f.__name__)):
         try:
             pin(lib)
         except (AssertionError, ValueError, FloatingPointError):
-            caught.append(pin.__name__)
-    assert caught, f"mutant {name} passed every pin"
+            return
+    pytest.fail(f"mutant {name} passed every pin")
+
+
+_PARTS = (("conv", ("conv",)), ("norm", ("norm",)), ("mimo", ("mimo", "trapezoid")),
+          ("trapezoid", ("trapezoid", "mimo")), ("bwd", ("backward",)), ("decode", ("decode",)),
+          ("softplus", ("softplus", "dt_zero")))
+
+
+def _related(mutant, pin):
+    for key, pins in _PARTS:
+        if key in mutant:
+            return any(k in pin for k in pins)
+    return not any(k in pin for _, ks in _PARTS for k in ks)  # scan mutants: the scan pins
