@@ -38,8 +38,9 @@ def _load(path: str = LIB):
         lib.oracle_ssd_scan_bwd.restype = ctypes.c_int
         lib.oracle_decode_step_mimo.argtypes = [i, i, i, i, i, i, i, dp, dp, dp, dp, dp, dp, dp, dp,
                                                 dp, dp, dp, dp]
+        lib.oracle_linear.argtypes = [i, i, i, dp, dp, dp]
         for f in (lib.oracle_conv1d_silu, lib.oracle_ssd_scan, lib.oracle_decode_step,
-                  lib.oracle_gated_rmsnorm, lib.oracle_decode_step_mimo):
+                  lib.oracle_gated_rmsnorm, lib.oracle_decode_step_mimo, lib.oracle_linear):
             f.restype = ctypes.c_int
         if path != LIB:
             return lib
@@ -222,3 +223,19 @@ def ssd_scan_bwd(x, dt_raw, dt_bias, A, B, C, D, dy, initial_state=None, d_final
     if rc:
         raise ValueError("oracle_ssd_scan_bwd: invalid argument")
     return out
+
+
+def linear(x, w, lib=None):
+    """y (M, N) = x (M, K) . w (N, K)^T in float64 (a projection of the mixer)."""
+    lib = lib or _load()
+    x_, xp = _d(x)
+    w_, wp = _d(w)
+    if x_.ndim != 2 or w_.ndim != 2 or x_.shape[1] != w_.shape[1]:
+        raise ValueError("x (M, K) and w (N, K) expected")
+    M, K = x_.shape
+    N = w_.shape[0]
+    y = np.zeros((M, N), np.float64)
+    rc = lib.oracle_linear(M, N, K, xp, wp, y.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
+    if rc != 0:
+        raise ValueError("oracle_linear: invalid arguments")
+    return y

@@ -274,6 +274,29 @@ int oracle_decode_step(int batch, int H, int P, int N, int G, int K,
 }
 
 /*
+ * The mixer's linear projections: in_proj maps each token's d_model
+ * features to the conv input x|B|C, the gate z and dt; out_proj maps the
+ * gated, normalised y back to d_model ("Nemotron-H style Hybrid
+ * Mamba-Transformer 3B feasibility study", the projection parameters of the
+ * Mamba-2 block; "Nemotron-Mamba3 architecture" article, sec. 2.2, the
+ * layer's projections around the conv and scan).  Both are the plain
+ * product with a weight stored like a torch Linear weight, (out, in):
+ *   y[m][n] = sum_k x[m][k] * w[n][k]
+ * Layouts: x (M, K), w (N, K), y (M, N), row-major.
+ */
+int oracle_linear(int M, int N, int K, const double *x, const double *w, double *y) {
+    if (M < 0 || N < 0 || K < 0 || (M > 0 && N > 0 && (!x || !w || !y))) return -1;
+#pragma omp parallel for schedule(static)
+    for (int m = 0; m < M; ++m)
+        for (int n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int k = 0; k < K; ++k) acc += x[(size_t)m * K + k] * w[(size_t)n * K + k];
+            y[(size_t)m * N + n] = acc;
+        }
+    return 0;
+}
+
+/*
  * Gated RMSNorm of the mixer output.  Mamba-2 keeps an RMSNorm together
  * with the output gate z; where the norm sits relative to the gate and
  * whether it is taken per group of channels or over the whole width are

@@ -651,4 +651,36 @@ def pin_backward_linear_parts(lib):
     assert all(np.all(v == 0) for v in z.values())
 
 
+# ---------------------------------------------------------------------------
+# the mixer's projections: y = x w^T
+# ---------------------------------------------------------------------------
+def _linear(lib, x, w):
+    return oracle.linear(x, w, lib=lib)
+
+
+def pin_linear_identity(lib):
+    """w = I: y = x exactly."""
+    x = np.random.default_rng(41).standard_normal((5, 33))
+    assert np.array_equal(_linear(lib, x, np.eye(33)), x)
+
+
+def pin_linear_integer_closed_form(lib):
+    """x[m][k] = 1000 + m, w[n][k] = 1000 + n: y = K (1000 + m)(1000 + n), exact in
+    fp64 and beyond fp32's 24-bit integers; N != K so a transposed w cannot pass."""
+    M, N, K = 3, 5, 4096
+    x = np.repeat(1000.0 + np.arange(M)[:, None], K, axis=1)
+    w = np.repeat(1000.0 + np.arange(N)[:, None], K, axis=1)
+    want = K * np.outer(1000.0 + np.arange(M), 1000.0 + np.arange(N))
+    assert np.array_equal(_linear(lib, x, w), want)
+
+
+def pin_linear_one_hot_rows(lib):
+    """x = e_j picks column j of w: y[n] = w[n][j] for every n (rectangular w)."""
+    r = np.random.default_rng(42)
+    N, K = 7, 11
+    w = r.standard_normal((N, K))
+    x = np.eye(K)[[0, 3, 10]]
+    assert np.array_equal(_linear(lib, x, w), w[:, [0, 3, 10]].T)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

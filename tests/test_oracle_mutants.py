@@ -15,6 +15,12 @@ from oracle.build import SRC, build
 from tests.oracle_pins import ALL_PINS
 
 MUTANTS = {
+    "linear_w_transposed": ("acc += x[(size_t)m * K + k] * w[(size_t)n * K + k];",
+                            "acc += x[(size_t)m * K + k] * w[(size_t)k * N + n];"),
+    "linear_drops_last_k": ("for (int k = 0; k < K; ++k) acc += x[(size_t)m * K + k]",
+                            "for (int k = 0; k < K - 1; ++k) acc += x[(size_t)m * K + k]"),
+    "linear_float_accumulate": ("double acc = 0.0;\n            for (int k = 0; k < K; ++k) acc += x",
+                                "float acc = 0.0f;\n            for (int k = 0; k < K; ++k) acc += x"),
     "no_decay": ("S[p * N + n] = a * S[p * N + n] + dt * xt[p] * Bt[n];\n                    acc += S[p * N + n] * Ct[n];",
                  "S[p * N + n] = S[p * N + n] + dt * xt[p] * Bt[n];\n                    acc += S[p * N + n] * Ct[n];"),
     "no_dt_input_scale": ("S[p * N + n] = a * S[p * N + n] + dt * xt[p] * Bt[n];\n                    acc += S[p * N + n] * Ct[n];",
@@ -91,7 +97,7 @@ def test_mutant_is_caught(name, tmp_path):
 
 _PARTS = (("conv", ("conv",)), ("norm", ("norm",)), ("mimo", ("mimo", "trapezoid")),
           ("trapezoid", ("trapezoid", "mimo")), ("bwd", ("backward",)), ("decode", ("decode",)),
-          ("softplus", ("softplus", "dt_zero")))
+          ("softplus", ("softplus", "dt_zero")), ("linear", ("linear",)))
 
 
 def _related(mutant, pin):
