@@ -757,6 +757,93 @@ class MimoRun:
         return out
 
 
+class MixerRun:
+    """The whole Mamba-2 mixer at the headline layer shape (d_model 4096,
+    d_inner 8192, 128 heads, 8 groups, batch 4 x 4096 tokens): in_proj, the
+    fused conv + scan, the gated RMSNorm and out_proj, each a libssd call on
+    the views of the in_proj output, event-timed per call; the projections
+    against the bf16 matrix-core roofline, with sampled rows against the oracle."""
+    D_MODEL = 4096
+
+    def __init__(self, w):
+        import torch
+        from state_space_sequence_ssd_amd import inputs
+        self.w = w
+        d = inputs.mixer_inputs(w.batch, w.seqlen, self.D_MODEL, w.nheads, w.ngroups, seed=9)
+        self.d = d
+        dev = torch.device("cuda:0")
+        self.t = {k: torch.from_numpy(v).to(dev, torch.bfloat16 if k in ("hidden", "in_proj_w", "out_proj_w")
+                                               else None) for k, v in d.items()}
+
+    def timed(self, steps, warmup, stream):
+        import numpy as np
+        import torch
+        from state_space_sequence_ssd_amd import ssd
+        w, t = self.w, self.t
+        H, G, P, N = w.nheads, w.ngroups, w.headdim, w.dstate
+        d_inner, conv_dim = H * P, H * P + 2 * G * N
+        Bt, L, dm = w.batch, w.seqlen, self.D_MODEL
+        d_in_proj = 2 * d_inner + 2 * G * N + H
+        zx = torch.empty((Bt, L, d_in_proj), dtype=torch.bfloat16, device="cuda")
+        y = torch.empty((Bt, L, H, P), dtype=torch.bfloat16, device="cuda")
+        yn = torch.empty((Bt, L, d_inner), dtype=torch.bfloat16, device="cuda")
+        out = torch.empty((Bt, L, dm), dtype=torch.bfloat16, device="cuda")
+        xbc, dt, z = zx[..., d_inner:d_inner + conv_dim], zx[..., d_inner + conv_dim:], zx[..., :d_inner]
+        wsb = ssd.ssd_conv_scan_workspace_size(xbc, t["conv_w"], dt, t["A"], H, G)
+        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+
+        def step(ev=None):
+            rec = (lambda i: ev[i].record(stream)) if ev is not None else (lambda i: None)
+            rec(0)
+            ssd.ssd_linear(t["hidden"], t["in_proj_w"], y=zx)
+            rec(1)
+            ssd.ssd_conv_scan_fwd(xbc, t["conv_w"], dt, t["A"], H, G, dt_bias=t["dt_bias"], D=t["D"], y=y,
+                                  workspace=ws)
+            rec(2)
+            ssd.ssd_gated_rmsnorm(y.flatten(2), t["norm_w"], d_inner // G, z=z, out=yn)
+            rec(3)
+            ssd.ssd_linear(yn, t["out_proj_w"], y=out)
+            rec(4)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+        for e in evs:
+            step(e)
+        torch.cuda.synchronize()
+        names = ["in_proj", "conv_scan", "gated_rmsnorm", "out_proj"]
+        ms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
+        layer_ms = float(np.mean([e[0].elapsed_time(e[4]) for e in evs]))
+        T = Bt * L
+        fl_in, fl_out = 2.0 * T * d_in_proj * dm, 2.0 * T * dm * d_inner
+
+        def gemm(name, flops, M, Nn, K):
+            tf = flops / (ms[name] * 1e-3) / 1e12
+            return {"avg_ms": round(ms[name], 5), "M": M, "N": Nn, "K": K, "tflops": round(tf, 1),
+                    "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
+                                 "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4)}}
+        res = {"workload": f"Mamba-2 mixer, d_model {dm}, d_inner {d_inner}, {w.name}",
+               "ms_per_layer": round(layer_ms, 5), "tokens_per_s": round(T / (layer_ms * 1e-3), 1),
+               "in_proj": gemm("in_proj", fl_in, T, d_in_proj, dm),
+               "out_proj": gemm("out_proj", fl_out, T, dm, d_inner),
+               "conv_scan_ms": round(ms["conv_scan"], 5), "gated_rmsnorm_ms": round(ms["gated_rmsnorm"], 5)}
+        self.zx, self.out = zx, out
+        return res
+
+    def parity(self, nrows=8):
+        """Sampled token rows of the timed in_proj output against the oracle's
+        product of the same hidden rows (out_proj's parity is in the GPU tests)."""
+        import numpy as np
+        import oracle
+        T = self.w.batch * self.w.seqlen
+        rows = np.random.default_rng(3).choice(T, nrows, replace=False)
+        h = self.d["hidden"].reshape(T, -1)[rows]
+        ref = oracle.linear(h, self.d["in_proj_w"])
+        got = self.zx.reshape(T, -1)[rows].float().cpu().numpy()
+        return {"in_proj_rel_err": float(f"{rel_err(got, ref):.3e}"), "rows": int(nrows), "bar": 2 ** -8}
+
+
 class BwdRun:
     """The scan's backward pass at the headline shape (bf16 inputs, fp32
     arithmetic): gradients of x, dt, B, C, the per-head parameters and the
@@ -822,6 +909,7 @@ def main():
     ap.add_argument("--no-norm", action="store_true", help="skip the gated RMSNorm measurement")
     ap.add_argument("--no-mimo", action="store_true", help="skip the MIMO decode measurement")
     ap.add_argument("--no-bwd", action="store_true", help="skip the scan backward measurement")
+    ap.add_argument("--no-mixer", action="store_true", help="skip the whole-mixer measurement")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other synthetic configs (profiler runs: same kernel names)")
     ap.add_argument("--only", choices=["nemotron_h_8b", "decode", "tiny_fp32", "nemotron3_nano", "packed_3b"],
@@ -873,6 +961,7 @@ def main():
     nrun = NormRun(run.w, run.y) if run is not None and not args.no_norm else None
     mimo_run = MimoRun() if want("decode") and not args.no_decode and not args.no_mimo else None
     brun = BwdRun(run.w) if run is not None and not args.no_bwd else None
+    mrun = MixerRun(run.w) if run is not None and not args.no_mixer else None
     progress("inputs resident")
 
     # ---------------- decode: batch 256 through 29 layers ----------------
@@ -915,6 +1004,9 @@ def main():
     bwd = brun.timed(args.steps, min(args.warmup, 3), stream) if brun is not None else None
     if bwd is not None:
         progress(f"backward timed: {bwd['avg_ms']} ms")
+    mixer = mrun.timed(args.steps, min(args.warmup, 5), stream) if mrun is not None else None
+    if mixer is not None:
+        progress(f"mixer timed: {mixer['ms_per_layer']} ms per layer")
     ms_per_step = total_ms / args.steps
     tokens = w.batch * w.seqlen
     value = tokens / (ms_per_step / 1e3)
@@ -961,6 +1053,8 @@ def main():
         cpu, cpu1 = oracle_beside(run, {"rows": args.cpu_rows}, {"rows": 1})
         if norm is not None:
             norm["parity"] = nrun.parity(512)
+        if mixer is not None:
+            mixer["parity"] = mrun.parity()
     oracle_configs()
     progress("oracle done")
 
@@ -993,6 +1087,7 @@ def main():
         "decode": decode,
         "gated_rmsnorm": norm,
         "scan_backward": bwd,
+        "mixer": mixer,
         "configs": configs,
         "host": host_info(),
     }

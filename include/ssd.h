@@ -265,6 +265,40 @@ int ssd_conv_scan_fwd(const ssd_conv_scan_args *args, void *workspace,
                       size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * ssd_linear -- the mixer's linear projections: y = x w^T.
+ *
+ * Passages: in_proj takes each token's d_model features to the conv input
+ * x|B|C, the gate z and dt; out_proj takes the gated, normalised y back to
+ * d_model ("Nemotron-H style Hybrid Mamba-Transformer 3B feasibility
+ * study", the Mamba-2 block's projection parameters; "Nemotron-Mamba3
+ * architecture" article, sec. 2.2, the layer's projections around the conv
+ * and the scan).
+ *
+ *   y[m][n] = sum_k x[m][k] * w[n][k]
+ *   x (M, K), w (N, K) -- a torch Linear weight, (out, in) --, y (M, N);
+ *   row-major with the given row strides (elements); x, w, y must not
+ *   overlap.
+ *
+ * Precision: bf16 x, w, y; products and sums in fp32 (bf16 matrix cores),
+ * one bf16 rounding of each output.
+ * Supported: dtype BF16; K a positive multiple of 64; 16-byte aligned bases and row
+ * strides multiples of 8 elements (below 2^22); N a multiple of 8.
+ * Errors: SSD_ERR_INVALID_ARG (NULL pointer, negative dims, a row stride
+ * below its row width), SSD_ERR_UNSUPPORTED (dtype, K), SSD_ERR_MISALIGNED,
+ * SSD_ERR_HIP -- all but the last before any HIP call.
+ * ---------------------------------------------------------------------- */
+typedef struct ssd_linear_args {
+  uint32_t struct_size;          /* sizeof(ssd_linear_args) */
+  int32_t dtype;                 /* SSD_DTYPE_BF16 */
+  int32_t M, N, K;
+  const void *x; int64_t x_stride;
+  const void *w; int64_t w_stride;
+  void *y;       int64_t y_stride;
+} ssd_linear_args;
+
+int ssd_linear(const ssd_linear_args *args, void *stream);
+
+/* ------------------------------------------------------------------------
  * ssd_chunk_scan_fwd_noalloc -- ssd_chunk_scan_fwd without a caller
  * workspace, for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc).

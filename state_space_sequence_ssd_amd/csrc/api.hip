@@ -497,6 +497,35 @@ int ssd_chunk_scan_bwd(const ssd_scan_bwd_args *a, void *workspace, size_t ws_by
   return ok();
 }
 
+int ssd_linear(const ssd_linear_args *a, void *stream) {
+  if (!a) return fail(SSD_ERR_INVALID_ARG, "ssd_linear: args is NULL");
+  if (a->struct_size != sizeof(ssd_linear_args))
+    return fail(SSD_ERR_INVALID_ARG, "ssd_linear: struct_size %u != %zu", a->struct_size, sizeof(ssd_linear_args));
+  if (a->dtype != SSD_DTYPE_BF16) return fail(SSD_ERR_UNSUPPORTED, "ssd_linear: dtype %d not supported (bf16)", a->dtype);
+  if (a->M < 0 || a->N < 0 || a->K < 0)
+    return fail(SSD_ERR_INVALID_ARG, "ssd_linear: negative dims (M %d N %d K %d)", a->M, a->N, a->K);
+  if (a->K % 64 != 0) return fail(SSD_ERR_UNSUPPORTED, "ssd_linear: K %d not a multiple of 64", a->K);
+  if (a->N % 8 != 0) return fail(SSD_ERR_UNSUPPORTED, "ssd_linear: N %d not a multiple of 8", a->N);
+  if (a->M == 0 || a->N == 0) return ok();
+  if (!a->x || !a->w || !a->y) return fail(SSD_ERR_INVALID_ARG, "ssd_linear: x, w and y are required");
+  if (a->x_stride < a->K || a->w_stride < a->K || a->y_stride < a->N)
+    return fail(SSD_ERR_INVALID_ARG, "ssd_linear: row strides below the row widths");
+  const int64_t kMaxSt = int64_t(1) << 22;
+  if (a->x_stride >= kMaxSt || a->w_stride >= kMaxSt || a->y_stride >= kMaxSt)
+    return fail(SSD_ERR_INVALID_ARG, "ssd_linear: row strides must be below 2^22 elements");
+  if (!vec_ok(a->x, 0, a->x_stride, 2) || !vec_ok(a->w, 0, a->w_stride, 2) || !vec_ok(a->y, 0, a->y_stride, 2))
+    return fail(SSD_ERR_MISALIGNED, "ssd_linear: 16-byte aligned bases and row strides multiples of 8 elements");
+  ssd::LinearParams p{};
+  p.M = a->M; p.N = a->N; p.K = a->K;
+  p.x = a->x; p.x_st = a->x_stride;
+  p.w = a->w; p.w_st = a->w_stride;
+  p.y = a->y; p.y_st = a->y_stride;
+  if (a->K == 0) return fail(SSD_ERR_UNSUPPORTED, "ssd_linear: K must be positive");
+  const hipError_t e = ssd::launch_linear_bf16(p, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SSD_ERR_HIP, "ssd_linear: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int ssd_gated_rmsnorm(const ssd_norm_args *a, void *stream) {
   if (!a) return fail(SSD_ERR_INVALID_ARG, "ssd_gated_rmsnorm: args is NULL");
   if (a->struct_size != sizeof(ssd_norm_args))

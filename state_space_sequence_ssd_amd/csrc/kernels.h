@@ -124,6 +124,15 @@ struct ScanParams {
   const void *conv_state; int64_t conv_ch;
 };
 
+// y (M, N) = x (M, K) . w (N, K)^T in bf16 with fp32 accumulation (linear_bf16.hip).
+struct LinearParams {
+  int M, N, K;
+  const void *x; int64_t x_st;  // row strides in elements
+  const void *w; int64_t w_st;
+  void *y; int64_t y_st;
+};
+hipError_t launch_linear_bf16(const LinearParams &p, hipStream_t stream);
+
 // fp32 batch-row sequences up to this length run as one masked quadratic form
 // (quad_scan_f32.hip) instead of the chunked kernels.
 constexpr int kQuadMaxL = 1024;

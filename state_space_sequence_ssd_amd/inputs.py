@@ -237,6 +237,26 @@ def norm_inputs(batch: int, seqlen: int, channels: int, seed: int, bf16: bool = 
             "w": (1.0 + normal((channels,), 0.1, seed, 23, False)).astype(np.float32)}
 
 
+def mixer_inputs(batch: int, seqlen: int, d_model: int, nheads: int, ngroups: int, seed: int,
+                 headdim: int = HEADDIM, dstate: int = DSTATE) -> dict:
+    """Hidden states and random-init weights of one Mamba-2 mixer (bf16-exact
+    values): hidden ~ N(0, 1); in_proj and out_proj ~ N(0, 1/fan_in); conv
+    taps ~ N(0, 1/4); norm weight ~ 1 + N(0, 0.01); per-head dt_bias, A, D as
+    for the scan workloads."""
+    d_inner = nheads * headdim
+    conv_dim = d_inner + 2 * ngroups * dstate
+    d_in_proj = 2 * d_inner + 2 * ngroups * dstate + nheads
+    out = {
+        "hidden": normal((batch, seqlen, d_model), 1.0, seed, 31, True),
+        "in_proj_w": normal((d_in_proj, d_model), d_model ** -0.5, seed, 32, True),
+        "out_proj_w": normal((d_model, d_inner), d_inner ** -0.5, seed, 33, True),
+        "conv_w": conv_weight(conv_dim, seed),
+        "norm_w": (1.0 + normal((d_inner,), 0.1, seed, 34, False)).astype(np.float32),
+    }
+    out["dt_bias"], out["A"], out["D"] = head_params(nheads, seed)
+    return out
+
+
 def mimo_decode_inputs(batch: int, nheads: int, ngroups: int, rank: int, seed: int, bf16: bool = True) -> dict:
     """One MIMO decode token: x, previous x ~ N(0, 1) (batch, H, P, R); B, C,
     previous B ~ N(0, 1/128) (batch, G, N, R); dt_raw ~ N(0, 1); lam ~ U(0, 1);

@@ -51,6 +51,11 @@ class SsdScanArgs(ctypes.Structure):
 _SCAN_ARGS_SIZE = ctypes.sizeof(SsdScanArgs)
 
 
+class SsdLinearArgs(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("dtype", _i32), ("M", _i32), ("N", _i32), ("K", _i32),
+                ("x", _vp), ("x_stride", _i64), ("w", _vp), ("w_stride", _i64), ("y", _vp), ("y_stride", _i64)]
+
+
 class SsdConvScanArgs(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("dtype", _i32),
                 ("batch", _i32), ("seqlen", _i32), ("nheads", _i32), ("headdim", _i32),
@@ -106,7 +111,7 @@ class SsdScanBwdArgs(ctypes.Structure):
 
 
 EXPORTS = ["ssd_conv1d_silu", "ssd_chunk_scan_workspace_size", "ssd_chunk_scan_fwd",
-           "ssd_chunk_scan_fwd_noalloc", "ssd_conv_scan_workspace_size", "ssd_conv_scan_fwd", "ssd_chunk_scan_bwd_workspace_size", "ssd_chunk_scan_bwd",
+           "ssd_chunk_scan_fwd_noalloc", "ssd_conv_scan_workspace_size", "ssd_conv_scan_fwd", "ssd_linear", "ssd_chunk_scan_bwd_workspace_size", "ssd_chunk_scan_bwd",
            "ssd_gated_rmsnorm", "ssd_decode_step", "ssd_decode_step_mimo", "ssd_last_error", "ssd_version"]
 NOALLOC_SCRATCH_BYTES = 96 * 1024 * 1024   # SSD_NOALLOC_SCRATCH_BYTES
 
@@ -134,6 +139,8 @@ def load_library(path: str = LIB_PATH):
     lib.ssd_conv_scan_workspace_size.restype = ctypes.c_size_t
     lib.ssd_conv_scan_fwd.argtypes = [ctypes.POINTER(SsdConvScanArgs), _vp, ctypes.c_size_t, _vp]
     lib.ssd_conv_scan_fwd.restype = ctypes.c_int
+    lib.ssd_linear.argtypes = [ctypes.POINTER(SsdLinearArgs), _vp]
+    lib.ssd_linear.restype = ctypes.c_int
     lib.ssd_gated_rmsnorm.argtypes = [ctypes.POINTER(SsdNormArgs), _vp]
     lib.ssd_gated_rmsnorm.restype = ctypes.c_int
     lib.ssd_chunk_scan_bwd_workspace_size.argtypes = [ctypes.POINTER(SsdScanBwdArgs)]
@@ -463,6 +470,67 @@ def ssd_conv_scan_fwd(xBC: torch.Tensor, conv_weight: torch.Tensor, dt: torch.Te
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.ssd_conv_scan_fwd(ctypes.byref(a), _ptr(workspace), ws_bytes, _stream(stream)))
     return y
+
+
+def ssd_linear(x: torch.Tensor, w: torch.Tensor, y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """y = x w^T (a projection of the mixer).  x (..., K) with packed leading dims
+    and a unit-stride last dim, w (N, K) (a torch Linear weight), bf16.
+    Returns y (..., N)."""
+    lib = load_library()
+    if x.dim() < 1 or w.dim() != 2:
+        raise ValueError("x (..., K) and w (N, K) expected")
+    K = x.shape[-1]
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError(f"w must be (N, K={K})")
+    _dtype_code(x)
+    _same_dtype(x, w=w, y=y)
+    x2 = x.reshape(-1, K) if x.dim() != 2 else x
+    if x2.data_ptr() != x.data_ptr():
+        raise ValueError("x's leading dims must be packed (a view, not a copy)")
+    M = x2.shape[0]
+    if y is None:
+        y = torch.empty((*x.shape[:-1], N), dtype=x.dtype, device=x.device)
+    _shape(y, "y", (*x.shape[:-1], N))
+    y2 = y.reshape(-1, N) if y.dim() != 2 else y
+    if y2.data_ptr() != y.data_ptr():
+        raise ValueError("y's leading dims must be packed")
+    for t, name in ((x2, "x"), (w, "w"), (y2, "y")):
+        if t.shape[0] > 1 and t.stride(1) != 1:
+            raise ValueError(f"{name} must have a unit-stride last dim")
+    _on_gpu(x, w=w, y=y)
+    a = SsdLinearArgs(ctypes.sizeof(SsdLinearArgs), _dtype_code(x), M, N, K,
+                      x2.data_ptr(), x2.stride(0), w.data_ptr(), w.stride(0), y2.data_ptr(), y2.stride(0))
+    _check(lib.ssd_linear(ctypes.byref(a), _stream(stream)))
+    return y
+
+
+def mamba2_mixer_fwd(hidden: torch.Tensor, in_proj_w: torch.Tensor, conv_w: torch.Tensor,
+                     dt_bias: torch.Tensor, A: torch.Tensor, D: torch.Tensor, norm_w: torch.Tensor,
+                     out_proj_w: torch.Tensor, nheads: int, ngroups: int, headdim: int = 64,
+                     dstate: int = 128, norm_group_size: Optional[int] = None, eps: float = 1e-5,
+                     conv_bias: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """The whole Mamba-2 mixer forward as a sequence of this library's calls:
+    in_proj -> [z | xBC | dt] column views -> conv1d + SiLU fused into the
+    chunked scan -> gated RMSNorm(y, z), norm after the gate -> out_proj.
+    hidden (batch, L, d_model) bf16.  Only views and the calls' outputs are
+    made here; every step is a libssd call.  Returns (batch, L, d_model)."""
+    batch, L, _ = hidden.shape
+    d_inner = nheads * headdim
+    conv_dim = d_inner + 2 * ngroups * dstate
+    d_in_proj = 2 * d_inner + 2 * ngroups * dstate + nheads
+    if in_proj_w.shape[0] != d_in_proj:
+        raise ValueError(f"in_proj_w must have {d_in_proj} rows (z, x, B, C, dt)")
+    zxbcdt = ssd_linear(hidden, in_proj_w, stream=stream)
+    z = zxbcdt[..., :d_inner]
+    xBC = zxbcdt[..., d_inner:d_inner + conv_dim]
+    dt = zxbcdt[..., d_inner + conv_dim:]
+    y = ssd_conv_scan_fwd(xBC, conv_w, dt, A, nheads, ngroups, headdim, dstate, conv_bias=conv_bias,
+                          dt_bias=dt_bias, D=D, final_state=final_state, workspace=workspace, stream=stream)
+    gs = norm_group_size or d_inner // ngroups
+    yn = ssd_gated_rmsnorm(y.flatten(2), norm_w, gs, z=z, eps=eps, stream=stream)
+    return ssd_linear(yn, out_proj_w, stream=stream)
 
 
 def _flat3(t: torch.Tensor, name: str):

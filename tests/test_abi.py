@@ -35,7 +35,7 @@ def test_struct_layouts_match_header(tmp_path):
     structs = {"ssd_conv_args": ssd.SsdConvArgs, "ssd_scan_args": ssd.SsdScanArgs,
                "ssd_decode_args": ssd.SsdDecodeArgs, "ssd_norm_args": ssd.SsdNormArgs,
                "ssd_mimo_decode_args": ssd.SsdMimoDecodeArgs, "ssd_scan_bwd_args": ssd.SsdScanBwdArgs,
-               "ssd_conv_scan_args": ssd.SsdConvScanArgs}
+               "ssd_conv_scan_args": ssd.SsdConvScanArgs, "ssd_linear_args": ssd.SsdLinearArgs}
     lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "ssd.h"', "int main(void) {"]
     for cname, py in structs.items():
         lines.append(f'printf("{cname} sizeof %zu\\n", sizeof({cname}));')
@@ -179,6 +179,36 @@ def test_conv_scan_workspace():
     conv_part = 16384 * 2048 * 2
     assert lib.ssd_conv_scan_workspace_size(ctypes.byref(seg)) > conv_part
     assert lib.ssd_conv_scan_workspace_size(ctypes.byref(conv_scan_args(headdim=16))) == ctypes.c_size_t(-1).value
+
+
+def linear_args(**kw):
+    a = ssd.SsdLinearArgs()
+    a.struct_size = ctypes.sizeof(ssd.SsdLinearArgs)
+    a.dtype = ssd.SSD_DTYPE_BF16
+    a.M, a.N, a.K = 16384, 18560, 4096
+    a.x, a.x_stride = FAKE, 4096
+    a.w, a.w_stride = FAKE, 4096
+    a.y, a.y_stride = FAKE, 18560
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("struct_size", 4, 1), ("dtype", ssd.SSD_DTYPE_F32, 2), ("M", -1, 1), ("K", 100, 2), ("K", 0, 2),
+    ("N", 12, 2), ("x", None, 1), ("w", None, 1), ("y", None, 1), ("x_stride", 4000, 1),
+    ("y_stride", 1 << 22, 1), ("x", FAKE + 8, 4), ("w_stride", 4096 + 4, 4),
+])
+def test_linear_argument_errors(field, value, code):
+    assert ssd.load_library().ssd_linear(ctypes.byref(linear_args(**{field: value})), None) == code
+    assert ssd.load_library().ssd_last_error().decode()
+
+
+def test_linear_empty_is_a_no_op():
+    """M = 0 or N = 0: nothing to compute, success before any HIP call."""
+    lib = ssd.load_library()
+    assert lib.ssd_linear(ctypes.byref(linear_args(M=0, x=None, y=None)), None) == 0
+    assert lib.ssd_linear(ctypes.byref(linear_args(N=0, w=None, y=None)), None) == 0
 
 
 def conv_args(**kw):

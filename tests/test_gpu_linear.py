@@ -1,0 +1,84 @@
+"""ssd_linear (y = x w^T, the mixer's projections) against the fp64 oracle.
+
+Bar, per element: |gpu - oracle| <= 2^-8 |oracle| + 2^-12 max|oracle| --
+one bf16 rounding of the output (relative 2^-9) with margin, plus the fp32
+accumulation of up to 8192 products (far below 2^-12 of the largest output).
+Inputs are bf16 values, so bf16 -> fp64 is exact on the oracle side.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from state_space_sequence_ssd_amd import inputs, ssd
+from tests.gpu_helpers import BF, DEV, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def bf16_normal(shape, std, seed, stream):
+    return inputs.normal(shape, std, seed, stream, True)
+
+
+def check(y, ref, what):
+    y, ref = np.asarray(y, np.float64), np.asarray(ref, np.float64)
+    err = np.abs(y - ref)
+    bound = 2.0 ** -8 * np.abs(ref) + 2.0 ** -12 * np.max(np.abs(ref))
+    worst = float(np.max(err / bound))
+    print(f"  {what}: max err {np.max(err):.3e}, max |ref| {np.max(np.abs(ref)):.3e}, worst err/bound {worst:.3f}",
+          flush=True)
+    assert np.all(err <= bound), what
+
+
+CASES = [(1, 8, 64), (7, 136, 64), (128, 128, 128), (300, 200, 512), (257, 1032, 4096), (1000, 64, 8192)]
+
+
+@pytest.mark.parametrize("M,N,K", CASES, ids=[f"{m}x{n}x{k}" for m, n, k in CASES])
+def test_linear_small(M, N, K):
+    print(f"case linear M={M} N={N} K={K}", flush=True)
+    x = bf16_normal((M, K), 1.0, 21, 1)
+    w = bf16_normal((N, K), K ** -0.5, 21, 2)
+    y = ssd.ssd_linear(to_dev(x, BF), to_dev(w, BF))
+    torch.cuda.synchronize()
+    check(to_np(y), oracle.linear(x, w), f"{M}x{N}x{K}")
+
+
+def test_linear_strided_views():
+    """x and y as column slices of wider rows (as in the in_proj output split), with
+    3-d leading dims that merge into one row index."""
+    print("case linear strided views", flush=True)
+    x_full = bf16_normal((2, 150, 640), 1.0, 22, 1)
+    w = bf16_normal((264, 512), 512 ** -0.5, 22, 2)
+    xt = to_dev(x_full, BF)[..., 64:576]          # (2, 150, 512), row stride 640
+    y_full = torch.full((2, 150, 400), 7.0, dtype=BF, device=DEV)
+    y = y_full[..., 8:272]                          # (2, 150, 264), row stride 400
+    ssd.ssd_linear(xt, to_dev(w, BF), y=y)
+    torch.cuda.synchronize()
+    check(to_np(y).reshape(300, 264), oracle.linear(x_full.reshape(300, 640)[:, 64:576], w), "strided")
+    # the columns around the slice are untouched
+    assert torch.all(y_full[..., :8] == 7.0) and torch.all(y_full[..., 272:] == 7.0)
+
+
+def test_linear_repeat_bitwise():
+    x = to_dev(bf16_normal((333, 1024), 1.0, 23, 1), BF)
+    w = to_dev(bf16_normal((520, 1024), 1 / 32, 23, 2), BF)
+    a, b = ssd.ssd_linear(x, w), ssd.ssd_linear(x, w)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("name,M,N,K", [("in_proj_nemotron_h_8b", 16384, 18560, 4096),
+                                       ("out_proj_nemotron_h_8b", 16384, 4096, 8192)])
+def test_linear_full_size_sampled(name, M, N, K):
+    """The projections of the Nemotron-H 8B mixer at their full shapes; every
+    column of 24 sampled rows (first, last, tile edges, random) against the oracle."""
+    print(f"case {name} M={M} N={N} K={K}", flush=True)
+    x = bf16_normal((M, K), 1.0, 24, 1)
+    w = bf16_normal((N, K), K ** -0.5, 24, 2)
+    y = ssd.ssd_linear(to_dev(x, BF), to_dev(w, BF))
+    torch.cuda.synchronize()
+    rows = sorted({0, 1, 127, 128, 255, 8191, 8192, M - 129, M - 128, M - 1}
+                  | set(np.random.default_rng(5).integers(0, M, 14).tolist()))
+    yg = to_np(y[rows])
+    assert np.all(np.isfinite(to_np(y)))
+    check(yg, oracle.linear(x[rows], w), name)
