@@ -24,12 +24,12 @@
 //
 // Three launches:
 //   1. bwd_states_kernel: one workgroup per (row, head) walks the chunks
-//      forward and stores the state entering each one (fp32, in the
-//      workspace).
+//      forward with the state in the matrix-core accumulators and stores the
+//      state entering each chunk (fp32, in the workspace).
 //   2. bwd_chunks_kernel: one workgroup per (row, head) walks the chunks in
 //      reverse; the adjoint G, the entering state and every chunk operand
-//      live in LDS, and each product above is a loop over LDS rows.  dB and
-//      dC are written per head, the per-head scalars per (row, head).
+//      live in LDS, and each product above is a tile loop of fp32 MFMAs.  dB
+//      and dC are written per head, the per-head scalars per (row, head).
 //   3. bwd_reduce_kernel: dB, dC summed over the heads of each group and
 //      dA, dD, ddt_bias over the rows, in a fixed order (no float atomics,
 //      repeat runs are bitwise identical).
@@ -75,66 +75,144 @@ __device__ __forceinline__ void chunk_dt(const BwdParams &p, int b, int h, int t
   }
 }
 
+__device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Chunk operands move as 16-byte pieces: every thread issues all of its loads
+// of a chunk before the first one is used, so a chunk waits for one memory
+// latency, not one per element.
+template <typename T> constexpr int kVec = 16 / sizeof(T);  // elements per 16-byte piece
+
+template <typename T>
+__device__ __forceinline__ u32x4 ld16(const void *base, int64_t elem) {
+  return *reinterpret_cast<const u32x4 *>(reinterpret_cast<const T *>(base) + elem);
+}
+
+// the fp32 values of one piece into LDS (dst 16-byte aligned)
+template <typename T> __device__ __forceinline__ void st_piece(float *dst, u32x4 v, float scale = 1.f);
+template <> __device__ __forceinline__ void st_piece<float>(float *dst, u32x4 v, float scale) {
+  f32x4 f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) f[k] = __uint_as_float(v[k]) * scale;
+  *reinterpret_cast<f32x4 *>(dst) = f;
+}
+template <> __device__ __forceinline__ void st_piece<bf16_t>(float *dst, u32x4 v, float scale) {
+  f32x4 lo, hi;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    lo[2 * k] = __uint_as_float(v[k] << 16) * scale;
+    lo[2 * k + 1] = __uint_as_float(v[k] & 0xffff0000u) * scale;
+    hi[2 * k] = __uint_as_float(v[k + 2] << 16) * scale;
+    hi[2 * k + 1] = __uint_as_float(v[k + 2] & 0xffff0000u) * scale;
+  }
+  *reinterpret_cast<f32x4 *>(dst) = lo;
+  *reinterpret_cast<f32x4 *>(dst + 4) = hi;
+}
+
+// rows of `width` elements of one chunk (token rows t0 .. t0 + kQ - 1, row r
+// at element offset r * row_st); piece i of this thread covers row
+// (v * kVec) / width, columns (v * kVec) % width .., v = tid + kT i.  Rows
+// past nv read nothing and hold zeros.
+template <typename T, int width>
+struct ChunkRows {
+  static constexpr int kPieces = kQ * width / kVec<T> / kT;
+  u32x4 v[kPieces];
+  __device__ __forceinline__ void load(const void *base, int64_t first, int64_t row_st, int nv, int tid) {
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+      const int e = (tid + kT * i) * kVec<T>, j = e / width, q = e % width;
+      v[i] = j < nv ? ld16<T>(base, first + j * row_st + q) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  // into an LDS tile with row pitch `pitch` floats; scale(j) weights row j
+  template <int pitch, typename F>
+  __device__ __forceinline__ void store(float *tile, int tid, F scale) const {
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+      const int e = (tid + kT * i) * kVec<T>, j = e / width, q = e % width;
+      st_piece<T>(tile + j * pitch + q, v[i], scale(j));
+    }
+  }
+};
+
 // -------------------------------------------------------------------------
 // 1. the state entering every chunk
 // -------------------------------------------------------------------------
+// S <- e^{cs_Q} S + sum_j w_j x_j B_j^T on the fp32 matrix cores: the state
+// (64 x 128) is 32 tiles of 16 x 16, eight per wave, kept in the
+// accumulators; per chunk each tile takes 8 steps of v_mfma_f32_16x16x4_f32
+// (k = token).  Lane roles: operand row l16, k slot kq; the accumulator
+// holds rows 4 kq .. 4 kq + 3, column l16.
+constexpr int kXSP = kP + 4;   // padded rows of the staged x (w x) and B tiles
+constexpr int kBSP = kN + 4;
 template <typename T>
 __global__ __launch_bounds__(kT) void bwd_states_kernel(BwdParams p) {
-  __shared__ float sX[kQ * kP], sB[kQ * kN], s_dt[kQ], s_cs[kQ], s_z[kQ];
+  __shared__ __attribute__((aligned(16))) float sX[kQ * kXSP], sB[kQ * kBSP];
+  __shared__ float s_dt[kQ], s_cs[kQ], s_z[kQ];
   const int b = blockIdx.x / p.H, h = blockIdx.x % p.H, g = h / (p.H / p.G);
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, kq = lane >> 4;
   float *states = p.ws_states + ((int64_t)b * p.H + h) * p.nchunks * kPN;
-  // this thread's 32 state values: row p = tid / 4, columns n = 32 (tid % 4) + 0..31
-  const int pr = tid >> 2, n0 = 32 * (tid & 3);
-  float s[32];
+  // this wave's tiles: rows p in [16 wave, +16), columns n in [16 t, +16), t = 0..7
+  f32x4 acc[8];
+  const float *h0 = p.init ? p.init + ((int64_t)b * p.H + h) * kPN : nullptr;
 #pragma unroll
-  for (int k = 0; k < 32; ++k) s[k] = p.init ? p.init[((int64_t)b * p.H + h) * kPN + pr * kN + n0 + k] : 0.f;
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[t][r] = h0 ? h0[(16 * wave + 4 * kq + r) * kN + 16 * t + l16] : 0.f;
   for (int c = 0; c < p.nchunks; ++c) {
     const int t0 = c * kQ, nv = min(kQ, p.L - t0);
+    // the state entering this chunk
 #pragma unroll
-    for (int k = 0; k < 32; ++k) states[(int64_t)c * kPN + pr * kN + n0 + k] = s[k];
-    for (int e = tid; e < kQ * kP; e += kT) {
-      const int j = e / kP, q = e % kP;
-      sX[e] = j < nv ? ld<T>(p.x, (((int64_t)b * p.L + t0 + j) * p.H + h) * kP + q) : 0.f;
-    }
-    for (int e = tid; e < kQ * kN; e += kT) {
-      const int j = e / kN, q = e % kN;
-      sB[e] = j < nv ? ld<T>(p.B, (((int64_t)b * p.L + t0 + j) * p.G + g) * kN + q) : 0.f;
-    }
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) states[(int64_t)c * kPN + (16 * wave + 4 * kq + r) * kN + 16 * t + l16] = acc[t][r];
+    ChunkRows<T, kN> rb;
+    ChunkRows<T, kP> rx;
+    rb.load(p.B, (((int64_t)b * p.L + t0) * p.G + g) * kN, (int64_t)p.G * kN, nv, tid);
+    rx.load(p.x, (((int64_t)b * p.L + t0) * p.H + h) * kP, (int64_t)p.H * kP, nv, tid);
     chunk_dt<T>(p, b, h, t0, nv, s_dt, s_cs, s_z);
+    rb.template store<kBSP>(sB, tid, [](int) { return 1.f; });
+    __syncthreads();  // dt, cs
+    const float last = s_cs[kQ - 1];
+    rx.template store<kXSP>(sX, tid, [&](int j) { return __expf(last - s_cs[j]) * s_dt[j]; });  // w_j x_j
     __syncthreads();
-    const float last = s_cs[kQ - 1], dec = __expf(last);
+    const float dec = __expf(last);
 #pragma unroll
-    for (int k = 0; k < 32; ++k) s[k] *= dec;
-    for (int j = 0; j < nv; ++j) {
-      const float wx = __expf(last - s_cs[j]) * s_dt[j] * sX[j * kP + pr];
+    for (int t = 0; t < 8; ++t) acc[t] *= dec;
 #pragma unroll
-      for (int k = 0; k < 32; ++k) s[k] = fmaf(wx, sB[j * kN + n0 + k], s[k]);
+    for (int k0 = 0; k0 < kQ; k0 += 4) {
+      const float a = sX[(k0 + kq) * kXSP + 16 * wave + l16];  // (w x)^T: row p, k = token
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc[t] = mfma16(a, sB[(k0 + kq) * kBSP + 16 * t + l16], acc[t]);
     }
-    __syncthreads();
+    __syncthreads();  // the tiles are rewritten by the next chunk
   }
 }
 
 // -------------------------------------------------------------------------
 // 2. the chunks in reverse
 // -------------------------------------------------------------------------
-// Rows are padded by one float (129 and 65 floats), so lanes that walk down
-// a column of one of these tiles hit different LDS banks.
-constexpr int kNP = kN + 1, kPP = kP + 1;
+// Every product of the chunked formulas runs on the fp32 matrix cores
+// (v_mfma_f32_16x16x4_f32: fp32 products, fp32 sums).  Rows of the LDS tiles
+// are padded to 4 (mod 64) floats, so the 16 rows x 4 k values of one
+// operand read fall on 64 different banks.
+constexpr int kNP = kN + 4, kPP = kP + 4, kQP = kQ + 4;
 __device__ __forceinline__ int gi(int q, int n) { return q * kNP + n; }   // G, S0: [p][n]
 __device__ __forceinline__ int bi(int j, int n) { return j * kNP + n; }   // B, C: [token][n]
-__device__ __forceinline__ int xi(int j, int q) { return j * kPP + q; }   // X, DY, GB, S0C: [token][p]
+__device__ __forceinline__ int xi(int j, int q) { return j * kPP + q; }   // X, DY: [token][p]
+__device__ __forceinline__ int qi(int i, int j) { return i * kQP + j; }   // CB, DYX, Lm, W: [token][token]
 
 struct BwdSmem {
   float G[kP * kNP];   // adjoint dL/dS leaving the chunk (G1), then entering (G0)
   float S0[kP * kNP];  // state entering the chunk
   float X[kQ * kPP], DY[kQ * kPP], B[kQ * kNP], C[kQ * kNP];
-  float CB[kQ * kQ], DYX[kQ * kQ];                 // C_i . B_j, dy_i . x_j
-  float Lm[kQ * kQ];                               // e^{cs_i - cs_j} for j <= i, else 0
-  float GB[kQ * kPP];                              // (G1 B_j)[p]
-  float XG[kQ * kN];                               // (G1^T x_j)[n]
-  float S0C[kQ * kPP];                             // (S0 C_i)[p]
-  float dt[kQ], cs[kQ], z[kQ], ei[kQ], fj[kQ], dcs[kQ], ddt[kQ], xgb[kQ], red[kT / 64];
+  float CB[kQ * kQP], DYX[kQ * kQP];               // C_i . B_j, dy_i . x_j
+  float Lm[kQ * kQP];                              // e^{cs_i - cs_j} for j <= i, else 0
+  float W[kQ * kQP];                               // Lm o CB o DYX
+  float xgb_part[8][kQ];                           // per 16-column block: x_j . (G1 B_j)
+  float ey_part[4][kQ];                            // per 16-column block: dy_j . (S0 C_j)
+  float dt[kQ], cs[kQ], z[kQ], ei[kQ], fj[kQ], red[kT / 64];
 };
 
 template <typename T>
@@ -142,159 +220,261 @@ __global__ __launch_bounds__(kT) void bwd_chunks_kernel(BwdParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   BwdSmem &s = *reinterpret_cast<BwdSmem *>(smem_raw);
   const int b = blockIdx.x / p.H, h = blockIdx.x % p.H, g = h / (p.H / p.G);
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, kq = lane >> 4;
   const float Ah = p.A[h], Dh = p.D ? p.D[h] : 0.f;
   const float *states = p.ws_states + ((int64_t)b * p.H + h) * p.nchunks * kPN;
   for (int e = tid; e < kPN; e += kT)
     s.G[gi(e / kN, e % kN)] = p.dfinal ? p.dfinal[((int64_t)b * p.H + h) * kPN + e] : 0.f;
   float accA = 0.f, accD = 0.f, accBias = 0.f;
+  // this wave's token-row block and column blocks: rows j in [16 mj, +16);
+  // dx / G1 B: columns 16 (2 (w % 2) + t), t < 2; dB / dC / X G1: 16 (4 (w % 2) + t), t < 4
+  const int mj = wave >> 1, cb2 = 2 * (wave & 1), cb4 = 4 * (wave & 1);
   __syncthreads();
 
   for (int c = p.nchunks - 1; c >= 0; --c) {
     const int t0 = c * kQ, nv = min(kQ, p.L - t0);
     // operands of the chunk (rows past the end are zero; their dt is 0)
-    for (int e = tid; e < kPN; e += kT) s.S0[gi(e / kN, e % kN)] = states[(int64_t)c * kPN + e];
-    for (int e = tid; e < kQ * kP; e += kT) {
-      const int j = e / kP, q = e % kP;
-      const int64_t o = (((int64_t)b * p.L + t0 + j) * p.H + h) * kP + q;
-      s.X[xi(j, q)] = j < nv ? ld<T>(p.x, o) : 0.f;
-      s.DY[xi(j, q)] = j < nv ? ld<T>(p.dy, o) : 0.f;
+    {
+      constexpr int kS0 = kPN / 4 / kT;
+      f32x4 s0[kS0];
+#pragma unroll
+      for (int i = 0; i < kS0; ++i)
+        s0[i] = *reinterpret_cast<const f32x4 *>(states + (int64_t)c * kPN + 4 * (tid + kT * i));
+      ChunkRows<T, kP> rx, rdy;
+      ChunkRows<T, kN> rb, rc;
+      const int64_t xo = (((int64_t)b * p.L + t0) * p.H + h) * kP, bo = (((int64_t)b * p.L + t0) * p.G + g) * kN;
+      rx.load(p.x, xo, (int64_t)p.H * kP, nv, tid);
+      rdy.load(p.dy, xo, (int64_t)p.H * kP, nv, tid);
+      rb.load(p.B, bo, (int64_t)p.G * kN, nv, tid);
+      rc.load(p.C, bo, (int64_t)p.G * kN, nv, tid);
+      chunk_dt<T>(p, b, h, t0, nv, s.dt, s.cs, s.z);
+#pragma unroll
+      for (int i = 0; i < kS0; ++i) {
+        const int e = 4 * (tid + kT * i);
+        *reinterpret_cast<f32x4 *>(&s.S0[gi(e / kN, e % kN)]) = s0[i];
+      }
+      const auto one = [](int) { return 1.f; };
+      rx.template store<kPP>(s.X, tid, one);
+      rdy.template store<kPP>(s.DY, tid, one);
+      rb.template store<kNP>(s.B, tid, one);
+      rc.template store<kNP>(s.C, tid, one);
     }
-    for (int e = tid; e < kQ * kN; e += kT) {
-      const int j = e / kN, q = e % kN;
-      const int64_t o = (((int64_t)b * p.L + t0 + j) * p.G + g) * kN + q;
-      s.B[bi(j, q)] = j < nv ? ld<T>(p.B, o) : 0.f;
-      s.C[bi(j, q)] = j < nv ? ld<T>(p.C, o) : 0.f;
-    }
-    chunk_dt<T>(p, b, h, t0, nv, s.dt, s.cs, s.z);
     __syncthreads();
     for (int e = tid; e < kQ * kQ; e += kT) {
       const int i = e / kQ, j = e % kQ;
-      s.Lm[e] = j <= i ? __expf(s.cs[i] - s.cs[j]) : 0.f;
+      s.Lm[qi(i, j)] = j <= i ? __expf(s.cs[i] - s.cs[j]) : 0.f;
     }
     if (tid < kQ) {
       s.ei[tid] = __expf(s.cs[tid]);
       s.fj[tid] = __expf(s.cs[kQ - 1] - s.cs[tid]);
     }
 
-    // first products: CB, dyX (Q x Q), G1 B (Q x P), G1^T x (Q x N), S0 C (Q x P), <G1, S0>
-    for (int e = tid; e < kQ * kQ; e += kT) {
-      const int i = e / kQ, j = e % kQ;
-      float cb = 0.f, dx = 0.f;
-      for (int n = 0; n < kN; ++n) cb = fmaf(s.C[bi(i, n)], s.B[bi(j, n)], cb);
-      for (int q = 0; q < kP; ++q) dx = fmaf(s.DY[xi(i, q)], s.X[xi(j, q)], dx);
-      s.CB[e] = cb;
-      s.DYX[e] = dx;
-    }
-    for (int e = tid; e < kQ * kP; e += kT) {
-      const int j = e / kP, q = e % kP;
-      float gb = 0.f, sc = 0.f;
-      for (int n = 0; n < kN; ++n) {
-        gb = fmaf(s.G[gi(q, n)], s.B[bi(j, n)], gb);
-        sc = fmaf(s.S0[gi(q, n)], s.C[bi(j, n)], sc);
+    // ---- phase 1: C B^T, dy x^T (one 16 x 16 tile of each per wave), G1 B and
+    // S0 C (rows j, columns p), x G1 (rows j, columns n) ----
+    {
+      const int mi = wave >> 1, ni = wave & 1;
+      f32x4 cb = f32x4{}, dyx = f32x4{};
+#pragma unroll 4
+      for (int k0 = 0; k0 < kN; k0 += 4)
+        cb = mfma16(s.C[bi(16 * mi + l16, k0 + kq)], s.B[bi(16 * ni + l16, k0 + kq)], cb);
+#pragma unroll 4
+      for (int k0 = 0; k0 < kP; k0 += 4)
+        dyx = mfma16(s.DY[xi(16 * mi + l16, k0 + kq)], s.X[xi(16 * ni + l16, k0 + kq)], dyx);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        s.CB[qi(16 * mi + 4 * kq + r, 16 * ni + l16)] = cb[r];
+        s.DYX[qi(16 * mi + 4 * kq + r, 16 * ni + l16)] = dyx[r];
       }
-      s.GB[xi(j, q)] = gb;
-      s.S0C[xi(j, q)] = sc;
     }
-    for (int e = tid; e < kQ * kN; e += kT) {
-      const int j = e / kN, n = e % kN;
-      float xg = 0.f;
-      for (int q = 0; q < kP; ++q) xg = fmaf(s.X[xi(j, q)], s.G[gi(q, n)], xg);
-      s.XG[e] = xg;
+    f32x4 gb[2], xg[4];  // G1 B and x G1 tiles, kept for dx and dB
+    {
+      f32x4 s0c[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) gb[t] = s0c[t] = f32x4{};
+#pragma unroll 2
+      for (int k0 = 0; k0 < kN; k0 += 4) {
+        const float bv = s.B[bi(16 * mj + l16, k0 + kq)], cv = s.C[bi(16 * mj + l16, k0 + kq)];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          gb[t] = mfma16(bv, s.G[gi(16 * (cb2 + t) + l16, k0 + kq)], gb[t]);
+          s0c[t] = mfma16(cv, s.S0[gi(16 * (cb2 + t) + l16, k0 + kq)], s0c[t]);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) xg[t] = f32x4{};
+#pragma unroll 2
+      for (int k0 = 0; k0 < kP; k0 += 4) {
+        const float xv = s.X[xi(16 * mj + l16, k0 + kq)];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) xg[t] = mfma16(xv, s.G[gi(k0 + kq, 16 * (cb4 + t) + l16)], xg[t]);
+      }
+      // per-token partial dot products of this wave's column blocks: the lane
+      // holds rows j = 16 mj + 4 kq + r, column l16 of each block
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * mj + 4 * kq + r;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          float v = s0c[t][r] * s.DY[xi(j, 16 * (cb2 + t) + l16)];
+#pragma unroll
+          for (int off = 8; off >= 1; off >>= 1) v += __shfl_xor(v, off, 16);
+          if (l16 == 0) s.ey_part[cb2 + t][j] = v;
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          float v = xg[t][r] * s.B[bi(j, 16 * (cb4 + t) + l16)];
+#pragma unroll
+          for (int off = 8; off >= 1; off >>= 1) v += __shfl_xor(v, off, 16);
+          if (l16 == 0) s.xgb_part[cb4 + t][j] = v;
+        }
+      }
     }
     float gs = 0.f;  // <G1, S0>
     for (int e = tid; e < kPN; e += kT) gs = fmaf(s.G[gi(e / kN, e % kN)], s.S0[gi(e / kN, e % kN)], gs);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) gs += __shfl_xor(gs, off, 64);
-    if ((tid & 63) == 0) s.red[tid >> 6] = gs;
+    if (lane == 0) s.red[wave] = gs;
+    __syncthreads();
+
+    // ---- phase 2: per-token scalars ----
+    for (int e = tid; e < kQ * kQ; e += kT) {
+      const int i = e / kQ, j = e % kQ;
+      s.W[qi(i, j)] = s.Lm[qi(i, j)] * s.CB[qi(i, j)] * s.DYX[qi(i, j)];
+    }
     __syncthreads();
     const float G1S0 = s.red[0] + s.red[1] + s.red[2] + s.red[3];
     const float eQ = s.ei[kQ - 1];
-
-    // per-token scalars: the explicit dt gradient and dcs (one thread per token)
-    if (tid < kQ) {
-      const int j = tid;
-      const float fj = s.fj[j];
-      float xgb = 0.f;  // x_j . (G1 B_j)
-      for (int q = 0; q < kP; ++q) xgb = fmaf(s.X[xi(j, q)], s.GB[xi(j, q)], xgb);
-      s.xgb[j] = xgb;
-      float dexp = fj * xgb;  // explicit: f_j x_j . G1 B_j + sum_{i>=j} L_ij CB_ij dyX_ij
-      float col = 0.f;        // sum_{i>=j} W_ij
-      for (int i = j; i < kQ; ++i) {
-        const float m = s.Lm[i * kQ + j] * s.CB[i * kQ + j] * s.DYX[i * kQ + j];
-        dexp += m;
-        col = fmaf(m, s.dt[j], col);
-      }
-      float row = 0.f;        // sum_{k<=j} W_jk
-      for (int k = 0; k <= j; ++k)
-        row = fmaf(s.Lm[j * kQ + k] * s.CB[j * kQ + k] * s.DYX[j * kQ + k], s.dt[k], row);
-      float ey = 0.f;         // dy_j . (S0 C_j)
-      for (int q = 0; q < kP; ++q) ey = fmaf(s.DY[xi(j, q)], s.S0C[xi(j, q)], ey);
-      float dcs = s.ei[j] * ey + row - col - fj * s.dt[j] * xgb;
-      s.ddt[j] = dexp;
-      s.dcs[j] = dcs;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      float tot = eQ * G1S0;
-      for (int j = 0; j < kQ; ++j) tot = fmaf(s.fj[j] * s.dt[j], s.xgb[j], tot);
-      s.dcs[kQ - 1] += tot;
-      // through cs: ddt_j += A sum_{k>=j} dcs_k; dA += dt_j sum_{k>=j} dcs_k
-      float suf = 0.f;
-      for (int j = kQ - 1; j >= 0; --j) {
-        suf += s.dcs[j];
-        s.ddt[j] = fmaf(Ah, suf, s.ddt[j]);
-        accA = fmaf(s.dt[j], suf, accA);
-      }
-    }
-    // outputs of the chunk: dx, dB, dC, ddt_raw; dD
-    for (int e = tid; e < kQ * kP; e += kT) {
-      const int j = e / kP, q = e % kP;
-      if (j >= nv) continue;
+    if (wave == 0) {
+      // lanes 0..31: token j; column sums sum_{i>=j} W_ij by lanes 0..31 and the
+      // dt-weighted row sums sum_{k<=j} W_jk dt_k by lanes 32..63
+      const int j = lane & 31;
       float acc = 0.f;
-      for (int i = j; i < kQ; ++i) acc = fmaf(s.Lm[i * kQ + j] * s.CB[i * kQ + j], s.DY[xi(i, q)], acc);
-      const float v = fmaf(Dh, s.DY[xi(j, q)], s.dt[j] * fmaf(s.fj[j], s.GB[xi(j, q)], acc));
-      reinterpret_cast<T *>(p.dx)[(((int64_t)b * p.L + t0 + j) * p.H + h) * kP + q] = from_f32<T>(v);
-    }
-    for (int e = tid; e < kQ * kN; e += kT) {
-      const int j = e / kN, n = e % kN;
-      if (j >= nv) continue;
-      float ab = 0.f, ac = 0.f;
-      for (int i = j; i < kQ; ++i) ab = fmaf(s.Lm[i * kQ + j] * s.DYX[i * kQ + j], s.C[bi(i, n)], ab);
-      for (int k = 0; k <= j; ++k) ac = fmaf(s.Lm[j * kQ + k] * s.dt[k] * s.DYX[j * kQ + k], s.B[bi(k, n)], ac);
-      float dcv = 0.f;  // e_j (S0^T dy_j)[n]
-      for (int q = 0; q < kP; ++q) dcv = fmaf(s.S0[gi(q, n)], s.DY[xi(j, q)], dcv);
-      const int64_t o = (((int64_t)b * p.L + t0 + j) * p.H + h) * kN + n;   // per-head partials
-      p.ws_dB[o] = s.dt[j] * fmaf(s.fj[j], s.XG[e], ab);
-      p.ws_dC[o] = fmaf(s.ei[j], dcv, ac);
-    }
-    if (tid < 64) {
-      float dd = 0.f;
-      for (int j = tid; j < kQ; j += 64) dd += s.DYX[j * kQ + j];
+      if (lane < 32) {
+        for (int i = j; i < kQ; ++i) acc += s.W[qi(i, j)];
+      } else {
+        for (int k = 0; k <= j; ++k) acc = fmaf(s.W[qi(j, k)], s.dt[k], acc);
+      }
+      const float row = __shfl(acc, j + 32, 64);
+      float dcs = 0.f, dexp = 0.f, tot_part = 0.f, dtj = 0.f;
+      if (lane < 32) {
+        const float fj = s.fj[j];
+        dtj = s.dt[j];
+        float xgb = 0.f, ey = 0.f;
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) dd += __shfl_xor(dd, off, 64);
-      accD += dd;  // every lane of wave 0 holds the chunk's sum
-    }
-    __syncthreads();  // ddt complete
-    if (tid < kQ && tid < nv) {
-      const float dz = s.ddt[tid] * __builtin_amdgcn_rcpf(1.f + __expf(-s.z[tid]));
-      reinterpret_cast<T *>(p.ddt)[((int64_t)b * p.L + t0 + tid) * p.H + h] = from_f32<T>(dz);
-    }
-    if (tid < 64) {
-      float dz = 0.f;
-      if (tid < kQ && tid < nv) dz = s.ddt[tid] * __builtin_amdgcn_rcpf(1.f + __expf(-s.z[tid]));
+        for (int t = 0; t < 8; ++t) xgb += s.xgb_part[t][j];
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) dz += __shfl_xor(dz, off, 64);
-      accBias += dz;
+        for (int t = 0; t < 4; ++t) ey += s.ey_part[t][j];
+        dexp = fmaf(fj, xgb, acc);                               // f_j x_j.(G1 B_j) + sum_{i>=j} W_ij
+        dcs = s.ei[j] * ey + row - dtj * acc - fj * dtj * xgb;
+        tot_part = fj * dtj * xgb;
+      }
+      // the last token also carries e^{cs_Q} <G1, S0> + sum_j f_j dt_j x_j.(G1 B_j)
+      float tot = tot_part;
+#pragma unroll
+      for (int off = 16; off >= 1; off >>= 1) tot += __shfl_xor(tot, off, 32);
+      if (lane == kQ - 1) dcs += fmaf(eQ, G1S0, tot);
+      // suffix sums over the chunk's tokens: suf_j = sum_{k>=j} dcs_k
+      float suf = lane < 32 ? dcs : 0.f;
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1) {
+        const float v = __shfl_down(suf, off, 32);
+        if ((lane & 31) + off < 32) suf += v;
+      }
+      float da = lane < 32 ? dtj * suf : 0.f;
+#pragma unroll
+      for (int off = 16; off >= 1; off >>= 1) da += __shfl_xor(da, off, 32);
+      accA += da;  // lanes 0..31 hold the chunk's sum
+      if (lane < 32) {
+        const float ddt = fmaf(Ah, suf, dexp);
+        float dz = 0.f;
+        if (j < nv) {
+          dz = ddt * __builtin_amdgcn_rcpf(1.f + __expf(-s.z[j]));
+          reinterpret_cast<T *>(p.ddt)[((int64_t)b * p.L + t0 + j) * p.H + h] = from_f32<T>(dz);
+        }
+#pragma unroll
+        for (int off = 16; off >= 1; off >>= 1) dz += __shfl_xor(dz, off, 32);
+        accBias += dz;
+        float dd = s.DYX[qi(j, j)];
+#pragma unroll
+        for (int off = 16; off >= 1; off >>= 1) dd += __shfl_xor(dd, off, 32);
+        accD += dd;
+      }
     }
-    // G0 = sum_i e_i dy_i C_i^T + e^{cs_Q} G1, in place (every read of G1 is done)
-    for (int e = tid; e < kPN; e += kT) {
-      const int q = e / kN, n = e % kN;
-      float acc = eQ * s.G[gi(q, n)];
-      for (int i = 0; i < kQ; ++i) acc = fmaf(s.ei[i] * s.DY[xi(i, q)], s.C[bi(i, n)], acc);
-      s.G[gi(q, n)] = acc;
+
+    // ---- phase 3: dx, dB, dC (this wave's tiles) and G0 (rows p in [16 w, +16)) ----
+    {
+      // dx[j][q] = D dy_j[q] + dt_j (f_j (G1 B_j)[q] + sum_{i>=j} Lm_ij CB_ij dy_i[q])
+      f32x4 ax[2] = {f32x4{}, f32x4{}};
+#pragma unroll 2
+      for (int k0 = 0; k0 < kQ; k0 += 4) {
+        const int i = k0 + kq, j = 16 * mj + l16;
+        const float a = s.Lm[qi(i, j)] * s.CB[qi(i, j)];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) ax[t] = mfma16(a, s.DY[xi(i, 16 * (cb2 + t) + l16)], ax[t]);
+      }
+      // dB[j][n] = dt_j (f_j (x_j G1)[n] + sum_{i>=j} Lm_ij DYX_ij C_i[n]);
+      // dC[j][n] = e_j (S0^T dy_j)[n] + sum_{k<=j} Lm_jk dt_k DYX_jk B_k[n]
+      f32x4 ab[4], ac[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) ab[t] = ac[t] = f32x4{};
+#pragma unroll 2
+      for (int k0 = 0; k0 < kQ; k0 += 4) {
+        const int k = k0 + kq, j = 16 * mj + l16;
+        const float a1 = s.Lm[qi(k, j)] * s.DYX[qi(k, j)];
+        const float a2 = s.Lm[qi(j, k)] * s.dt[k] * s.DYX[qi(j, k)];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          ab[t] = mfma16(a1, s.C[bi(k, 16 * (cb4 + t) + l16)], ab[t]);
+          ac[t] = mfma16(a2, s.B[bi(k, 16 * (cb4 + t) + l16)], ac[t]);
+        }
+      }
+#pragma unroll 2
+      for (int k0 = 0; k0 < kP; k0 += 4) {
+        const int q = k0 + kq, j = 16 * mj + l16;
+        const float a = s.ei[j] * s.DY[xi(j, q)];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) ac[t] = mfma16(a, s.S0[gi(q, 16 * (cb4 + t) + l16)], ac[t]);
+      }
+      // G0[q][n] = e^{cs_Q} G1[q][n] + sum_i e_i dy_i[q] C_i[n], in place: this wave
+      // reads and writes only its own tiles of G, and no other product reads G now
+      f32x4 g0[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) g0[t][r] = eQ * s.G[gi(16 * wave + 4 * kq + r, 16 * t + l16)];
+#pragma unroll 2
+      for (int k0 = 0; k0 < kQ; k0 += 4) {
+        const int i = k0 + kq;
+        const float a = s.ei[i] * s.DY[xi(i, 16 * wave + l16)];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) g0[t] = mfma16(a, s.C[bi(i, 16 * t + l16)], g0[t]);
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s.G[gi(16 * wave + 4 * kq + r, 16 * t + l16)] = g0[t][r];
+      // outputs: the lane holds rows j = 16 mj + 4 kq + r, column l16 of each block
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * mj + 4 * kq + r;
+        if (j >= nv) continue;
+        const float dtj = s.dt[j], fj = s.fj[j];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int q = 16 * (cb2 + t) + l16;
+          const float v = fmaf(Dh, s.DY[xi(j, q)], dtj * fmaf(fj, gb[t][r], ax[t][r]));
+          reinterpret_cast<T *>(p.dx)[(((int64_t)b * p.L + t0 + j) * p.H + h) * kP + q] = from_f32<T>(v);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int n = 16 * (cb4 + t) + l16;
+          const int64_t o = (((int64_t)b * p.L + t0 + j) * p.H + h) * kN + n;   // per-head partials
+          p.ws_dB[o] = dtj * fmaf(fj, xg[t][r], ab[t][r]);
+          p.ws_dC[o] = ac[t][r];
+        }
+      }
     }
-    __syncthreads();
+    __syncthreads();  // G0 complete; the chunk's tiles are rewritten by the next chunk
   }
   if (p.dinit)
     for (int e = tid; e < kPN; e += kT) p.dinit[((int64_t)b * p.H + h) * kPN + e] = s.G[gi(e / kN, e % kN)];
