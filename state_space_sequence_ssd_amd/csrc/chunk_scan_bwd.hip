@@ -136,6 +136,25 @@ struct ChunkRows {
   }
 };
 
+// NS k-steps of matrix-core products: load(s) reads step s's operands from
+// LDS into an R, mma(R) issues its products.  Step s + 1's reads go out
+// while step s's products run, so the matrix core does not wait for each
+// step's reads (the last step's operands are read twice rather than
+// branching).
+template <int NS, typename R, typename FL, typename FM>
+__device__ __forceinline__ void pipelined(FL load, FM mma) {
+  R cur = load(0);
+#pragma unroll 2
+  for (int st = 0; st < NS; ++st) {
+    const R nxt = load(st + 1 < NS ? st + 1 : NS - 1);
+    mma(cur);
+    cur = nxt;
+    // keeps each step's reads in their own iteration: without it the
+    // compiler folds the rotation back into read-then-multiply
+    asm volatile("" ::: "memory");
+  }
+}
+
 // -------------------------------------------------------------------------
 // 1. the state entering every chunk
 // -------------------------------------------------------------------------
@@ -144,8 +163,11 @@ struct ChunkRows {
 // accumulators; per chunk each tile takes 8 steps of v_mfma_f32_16x16x4_f32
 // (k = token).  Lane roles: operand row l16, k slot kq; the accumulator
 // holds rows 4 kq .. 4 kq + 3, column l16.
-constexpr int kXSP = kP + 4;   // padded rows of the staged x (w x) and B tiles
-constexpr int kBSP = kN + 4;
+// The tiles are read with the token (k) on the lane's k slot and the column
+// on its 16-lane index: rows padded to 16 (mod 64) floats put the four k
+// slots on four different 16-bank groups.
+constexpr int kXSP = kP + 16;   // padded rows of the staged x (w x) and B tiles
+constexpr int kBSP = kN + 16;
 template <typename T>
 __global__ __launch_bounds__(kT) void bwd_states_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) float sX[kQ * kXSP], sB[kQ * kBSP];
@@ -160,6 +182,15 @@ __global__ __launch_bounds__(kT) void bwd_states_kernel(BwdParams p) {
   for (int t = 0; t < 8; ++t)
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[t][r] = h0 ? h0[(16 * wave + 4 * kq + r) * kN + 16 * t + l16] : 0.f;
+  // B and x of chunk c + 1 are loaded while chunk c is multiplied
+  ChunkRows<T, kN> rb;
+  ChunkRows<T, kP> rx;
+  const auto load_chunk = [&](int c) {
+    const int t0 = c * kQ, nv = min(kQ, p.L - t0);
+    rb.load(p.B, (((int64_t)b * p.L + t0) * p.G + g) * kN, (int64_t)p.G * kN, nv, tid);
+    rx.load(p.x, (((int64_t)b * p.L + t0) * p.H + h) * kP, (int64_t)p.H * kP, nv, tid);
+  };
+  if (p.nchunks > 0) load_chunk(0);
   for (int c = 0; c < p.nchunks; ++c) {
     const int t0 = c * kQ, nv = min(kQ, p.L - t0);
     // the state entering this chunk
@@ -167,16 +198,13 @@ __global__ __launch_bounds__(kT) void bwd_states_kernel(BwdParams p) {
     for (int t = 0; t < 8; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r) states[(int64_t)c * kPN + (16 * wave + 4 * kq + r) * kN + 16 * t + l16] = acc[t][r];
-    ChunkRows<T, kN> rb;
-    ChunkRows<T, kP> rx;
-    rb.load(p.B, (((int64_t)b * p.L + t0) * p.G + g) * kN, (int64_t)p.G * kN, nv, tid);
-    rx.load(p.x, (((int64_t)b * p.L + t0) * p.H + h) * kP, (int64_t)p.H * kP, nv, tid);
     chunk_dt<T>(p, b, h, t0, nv, s_dt, s_cs, s_z);
     rb.template store<kBSP>(sB, tid, [](int) { return 1.f; });
     __syncthreads();  // dt, cs
     const float last = s_cs[kQ - 1];
     rx.template store<kXSP>(sX, tid, [&](int j) { return __expf(last - s_cs[j]) * s_dt[j]; });  // w_j x_j
     __syncthreads();
+    if (c + 1 < p.nchunks) load_chunk(c + 1);
     const float dec = __expf(last);
 #pragma unroll
     for (int t = 0; t < 8; ++t) acc[t] *= dec;
@@ -209,9 +237,9 @@ struct BwdSmem {
   float X[kQ * kPP], DY[kQ * kPP], B[kQ * kNP], C[kQ * kNP];
   float CB[kQ * kQP], DYX[kQ * kQP];               // C_i . B_j, dy_i . x_j
   float Lm[kQ * kQP];                              // e^{cs_i - cs_j} for j <= i, else 0
-  float W[kQ * kQP];                               // Lm o CB o DYX
-  float xgb_part[8][kQ];                           // per 16-column block: x_j . (G1 B_j)
-  float ey_part[4][kQ];                            // per 16-column block: dy_j . (S0 C_j)
+  float xgb_part[2][kQ];                           // per 64-column half: x_j . (G1 B_j)
+  float ey_part[2][kQ];                            // per 32-column half: dy_j . (S0 C_j)
+  float wcol[8][kQ], wrow[8][kQ];                  // per 4-token part: column / dt-weighted row sums of W
   float dt[kQ], cs[kQ], z[kQ], ei[kQ], fj[kQ], red[kT / 64];
 };
 
@@ -271,75 +299,119 @@ __global__ __launch_bounds__(kT) void bwd_chunks_kernel(BwdParams p) {
 
     // ---- phase 1: C B^T, dy x^T (one 16 x 16 tile of each per wave), G1 B and
     // S0 C (rows j, columns p), x G1 (rows j, columns n) ----
+    f32x4 gb[2], xg[4];  // G1 B and x G1 tiles, kept for dx and dB
+    f32x4 s0c[2];
     {
       const int mi = wave >> 1, ni = wave & 1;
       f32x4 cb = f32x4{}, dyx = f32x4{};
-#pragma unroll 4
-      for (int k0 = 0; k0 < kN; k0 += 4)
-        cb = mfma16(s.C[bi(16 * mi + l16, k0 + kq)], s.B[bi(16 * ni + l16, k0 + kq)], cb);
-#pragma unroll 4
-      for (int k0 = 0; k0 < kP; k0 += 4)
-        dyx = mfma16(s.DY[xi(16 * mi + l16, k0 + kq)], s.X[xi(16 * ni + l16, k0 + kq)], dyx);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) gb[t] = s0c[t] = f32x4{};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) xg[t] = f32x4{};
+      // contractions over n: C B^T, B G1^T, C S0^T
+      struct RN { float c_i, b_j, b_r, c_r, g[2], s0[2]; };
+      pipelined<kN / 4, RN>(
+          [&](int st) {
+            const int k = 4 * st + kq;
+            RN o;
+            o.c_i = s.C[bi(16 * mi + l16, k)];
+            o.b_j = s.B[bi(16 * ni + l16, k)];
+            o.b_r = s.B[bi(16 * mj + l16, k)];
+            o.c_r = s.C[bi(16 * mj + l16, k)];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              o.g[t] = s.G[gi(16 * (cb2 + t) + l16, k)];
+              o.s0[t] = s.S0[gi(16 * (cb2 + t) + l16, k)];
+            }
+            return o;
+          },
+          [&](const RN &o) {
+            cb = mfma16(o.c_i, o.b_j, cb);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              gb[t] = mfma16(o.b_r, o.g[t], gb[t]);
+              s0c[t] = mfma16(o.c_r, o.s0[t], s0c[t]);
+            }
+          });
+      // contractions over p: dy x^T, x G1
+      struct RP { float dy_i, x_j, x_r, g[4]; };
+      pipelined<kP / 4, RP>(
+          [&](int st) {
+            const int k = 4 * st + kq;
+            RP o;
+            o.dy_i = s.DY[xi(16 * mi + l16, k)];
+            o.x_j = s.X[xi(16 * ni + l16, k)];
+            o.x_r = s.X[xi(16 * mj + l16, k)];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) o.g[t] = s.G[gi(k, 16 * (cb4 + t) + l16)];
+            return o;
+          },
+          [&](const RP &o) {
+            dyx = mfma16(o.dy_i, o.x_j, dyx);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) xg[t] = mfma16(o.x_r, o.g[t], xg[t]);
+          });
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         s.CB[qi(16 * mi + 4 * kq + r, 16 * ni + l16)] = cb[r];
         s.DYX[qi(16 * mi + 4 * kq + r, 16 * ni + l16)] = dyx[r];
       }
     }
-    f32x4 gb[2], xg[4];  // G1 B and x G1 tiles, kept for dx and dB
     {
-      f32x4 s0c[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) gb[t] = s0c[t] = f32x4{};
-#pragma unroll 2
-      for (int k0 = 0; k0 < kN; k0 += 4) {
-        const float bv = s.B[bi(16 * mj + l16, k0 + kq)], cv = s.C[bi(16 * mj + l16, k0 + kq)];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          gb[t] = mfma16(bv, s.G[gi(16 * (cb2 + t) + l16, k0 + kq)], gb[t]);
-          s0c[t] = mfma16(cv, s.S0[gi(16 * (cb2 + t) + l16, k0 + kq)], s0c[t]);
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < 4; ++t) xg[t] = f32x4{};
-#pragma unroll 2
-      for (int k0 = 0; k0 < kP; k0 += 4) {
-        const float xv = s.X[xi(16 * mj + l16, k0 + kq)];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) xg[t] = mfma16(xv, s.G[gi(k0 + kq, 16 * (cb4 + t) + l16)], xg[t]);
-      }
-      // per-token partial dot products of this wave's column blocks: the lane
-      // holds rows j = 16 mj + 4 kq + r, column l16 of each block
+      // per-token partial dot products over this wave's columns: the lane
+      // holds rows j = 16 mj + 4 kq + r, column l16 of each block; its blocks
+      // are summed in the lane, then over the 16 lanes of the row
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = 16 * mj + 4 * kq + r;
+        float ve = 0.f, vx = 0.f;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          float v = s0c[t][r] * s.DY[xi(j, 16 * (cb2 + t) + l16)];
+        for (int t = 0; t < 2; ++t) ve = fmaf(s0c[t][r], s.DY[xi(j, 16 * (cb2 + t) + l16)], ve);
 #pragma unroll
-          for (int off = 8; off >= 1; off >>= 1) v += __shfl_xor(v, off, 16);
-          if (l16 == 0) s.ey_part[cb2 + t][j] = v;
+        for (int t = 0; t < 4; ++t) vx = fmaf(xg[t][r], s.B[bi(j, 16 * (cb4 + t) + l16)], vx);
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1) {
+          ve += __shfl_xor(ve, off, 16);
+          vx += __shfl_xor(vx, off, 16);
         }
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          float v = xg[t][r] * s.B[bi(j, 16 * (cb4 + t) + l16)];
-#pragma unroll
-          for (int off = 8; off >= 1; off >>= 1) v += __shfl_xor(v, off, 16);
-          if (l16 == 0) s.xgb_part[cb4 + t][j] = v;
+        if (l16 == 0) {
+          s.ey_part[wave & 1][j] = ve;
+          s.xgb_part[wave & 1][j] = vx;
         }
       }
     }
-    float gs = 0.f;  // <G1, S0>
-    for (int e = tid; e < kPN; e += kT) gs = fmaf(s.G[gi(e / kN, e % kN)], s.S0[gi(e / kN, e % kN)], gs);
+    {
+      // <G1, S0>, four independent chains of 16-byte reads
+      f32x4 acc4 = f32x4{};
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) gs += __shfl_xor(gs, off, 64);
-    if (lane == 0) s.red[wave] = gs;
+      for (int i = 0; i < kPN / 4 / kT; ++i) {
+        const int e = 4 * (tid + kT * i);
+        const f32x4 gv = *reinterpret_cast<const f32x4 *>(&s.G[gi(e / kN, e % kN)]);
+        const f32x4 sv = *reinterpret_cast<const f32x4 *>(&s.S0[gi(e / kN, e % kN)]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc4[k] = fmaf(gv[k], sv[k], acc4[k]);
+      }
+      float gs = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) gs += __shfl_xor(gs, off, 64);
+      if (lane == 0) s.red[wave] = gs;
+    }
     __syncthreads();
 
     // ---- phase 2: per-token scalars ----
-    for (int e = tid; e < kQ * kQ; e += kT) {
-      const int i = e / kQ, j = e % kQ;
-      s.W[qi(i, j)] = s.Lm[qi(i, j)] * s.CB[qi(i, j)] * s.DYX[qi(i, j)];
+    {
+      // W_ij = Lm_ij CB_ij DYX_ij: thread (part, j) sums column j over rows
+      // i in [4 part, +4) and row j over columns k in [4 part, +4), weighted by dt_k
+      const int j = tid & 31, part = tid >> 5;
+      float cp = 0.f, rp = 0.f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = 4 * part + u;
+        cp = fmaf(s.Lm[qi(i, j)] * s.CB[qi(i, j)], s.DYX[qi(i, j)], cp);
+        rp = fmaf(s.Lm[qi(j, i)] * s.CB[qi(j, i)] * s.DYX[qi(j, i)], s.dt[i], rp);
+      }
+      s.wcol[part][j] = cp;
+      s.wrow[part][j] = rp;
     }
     __syncthreads();
     const float G1S0 = s.red[0] + s.red[1] + s.red[2] + s.red[3];
@@ -348,22 +420,17 @@ __global__ __launch_bounds__(kT) void bwd_chunks_kernel(BwdParams p) {
       // lanes 0..31: token j; column sums sum_{i>=j} W_ij by lanes 0..31 and the
       // dt-weighted row sums sum_{k<=j} W_jk dt_k by lanes 32..63
       const int j = lane & 31;
-      float acc = 0.f;
-      if (lane < 32) {
-        for (int i = j; i < kQ; ++i) acc += s.W[qi(i, j)];
-      } else {
-        for (int k = 0; k <= j; ++k) acc = fmaf(s.W[qi(j, k)], s.dt[k], acc);
-      }
-      const float row = __shfl(acc, j + 32, 64);
       float dcs = 0.f, dexp = 0.f, tot_part = 0.f, dtj = 0.f;
       if (lane < 32) {
+        float acc = 0.f, row = 0.f;  // sum_{i>=j} W_ij and sum_{k<=j} W_jk dt_k
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          acc += s.wcol[t][j];
+          row += s.wrow[t][j];
+        }
         const float fj = s.fj[j];
         dtj = s.dt[j];
-        float xgb = 0.f, ey = 0.f;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) xgb += s.xgb_part[t][j];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) ey += s.ey_part[t][j];
+        const float xgb = s.xgb_part[0][j] + s.xgb_part[1][j], ey = s.ey_part[0][j] + s.ey_part[1][j];
         dexp = fmaf(fj, xgb, acc);                               // f_j x_j.(G1 B_j) + sum_{i>=j} W_ij
         dcs = s.ei[j] * ey + row - dtj * acc - fj * dtj * xgb;
         tot_part = fj * dtj * xgb;
@@ -404,51 +471,67 @@ __global__ __launch_bounds__(kT) void bwd_chunks_kernel(BwdParams p) {
     // ---- phase 3: dx, dB, dC (this wave's tiles) and G0 (rows p in [16 w, +16)) ----
     {
       // dx[j][q] = D dy_j[q] + dt_j (f_j (G1 B_j)[q] + sum_{i>=j} Lm_ij CB_ij dy_i[q])
-      f32x4 ax[2] = {f32x4{}, f32x4{}};
-#pragma unroll 2
-      for (int k0 = 0; k0 < kQ; k0 += 4) {
-        const int i = k0 + kq, j = 16 * mj + l16;
-        const float a = s.Lm[qi(i, j)] * s.CB[qi(i, j)];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) ax[t] = mfma16(a, s.DY[xi(i, 16 * (cb2 + t) + l16)], ax[t]);
-      }
+      // dx[j][q] = D dy_j[q] + dt_j (f_j (G1 B_j)[q] + sum_{i>=j} Lm_ij CB_ij dy_i[q]);
       // dB[j][n] = dt_j (f_j (x_j G1)[n] + sum_{i>=j} Lm_ij DYX_ij C_i[n]);
-      // dC[j][n] = e_j (S0^T dy_j)[n] + sum_{k<=j} Lm_jk dt_k DYX_jk B_k[n]
-      f32x4 ab[4], ac[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) ab[t] = ac[t] = f32x4{};
-#pragma unroll 2
-      for (int k0 = 0; k0 < kQ; k0 += 4) {
-        const int k = k0 + kq, j = 16 * mj + l16;
-        const float a1 = s.Lm[qi(k, j)] * s.DYX[qi(k, j)];
-        const float a2 = s.Lm[qi(j, k)] * s.dt[k] * s.DYX[qi(j, k)];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          ab[t] = mfma16(a1, s.C[bi(k, 16 * (cb4 + t) + l16)], ab[t]);
-          ac[t] = mfma16(a2, s.B[bi(k, 16 * (cb4 + t) + l16)], ac[t]);
-        }
-      }
-#pragma unroll 2
-      for (int k0 = 0; k0 < kP; k0 += 4) {
-        const int q = k0 + kq, j = 16 * mj + l16;
-        const float a = s.ei[j] * s.DY[xi(j, q)];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) ac[t] = mfma16(a, s.S0[gi(q, 16 * (cb4 + t) + l16)], ac[t]);
-      }
+      // dC[j][n] = e_j (S0^T dy_j)[n] + sum_{k<=j} Lm_jk dt_k DYX_jk B_k[n];
       // G0[q][n] = e^{cs_Q} G1[q][n] + sum_i e_i dy_i[q] C_i[n], in place: this wave
       // reads and writes only its own tiles of G, and no other product reads G now
-      f32x4 g0[8];
+      const int jr = 16 * mj + l16;  // the operand row of this lane
+      f32x4 ax[2], ab[4], ac[4], g0[8];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) ax[t] = f32x4{};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) ab[t] = ac[t] = f32x4{};
 #pragma unroll
       for (int t = 0; t < 8; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) g0[t][r] = eQ * s.G[gi(16 * wave + 4 * kq + r, 16 * t + l16)];
-#pragma unroll 2
-      for (int k0 = 0; k0 < kQ; k0 += 4) {
-        const int i = k0 + kq;
-        const float a = s.ei[i] * s.DY[xi(i, 16 * wave + l16)];
+      // contractions over the chunk's tokens (k)
+      struct RQ { float lcb, ldyx, ldt, edy, dy[2], c[8], b[4]; };
+      pipelined<kQ / 4, RQ>(
+          [&](int st) {
+            const int k = 4 * st + kq;
+            RQ o;
+            const float lkj = s.Lm[qi(k, jr)];
+            o.lcb = lkj * s.CB[qi(k, jr)];
+            o.ldyx = lkj * s.DYX[qi(k, jr)];
+            o.ldt = s.Lm[qi(jr, k)] * s.dt[k] * s.DYX[qi(jr, k)];
+            o.edy = s.ei[k] * s.DY[xi(k, 16 * wave + l16)];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) g0[t] = mfma16(a, s.C[bi(i, 16 * t + l16)], g0[t]);
-      }
+            for (int t = 0; t < 2; ++t) o.dy[t] = s.DY[xi(k, 16 * (cb2 + t) + l16)];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) o.c[t] = s.C[bi(k, 16 * t + l16)];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) o.b[t] = s.B[bi(k, 16 * (cb4 + t) + l16)];
+            return o;
+          },
+          [&](const RQ &o) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) ax[t] = mfma16(o.lcb, o.dy[t], ax[t]);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              ab[t] = mfma16(o.ldyx, cb4 ? o.c[4 + t] : o.c[t], ab[t]);
+              ac[t] = mfma16(o.ldt, o.b[t], ac[t]);
+            }
+#pragma unroll
+            for (int t = 0; t < 8; ++t) g0[t] = mfma16(o.edy, o.c[t], g0[t]);
+          });
+      // ... and over p: the e_j S0^T dy_j term of dC
+      const float ej = s.ei[jr];
+      struct RS { float edy, s0[4]; };
+      pipelined<kP / 4, RS>(
+          [&](int st) {
+            const int q = 4 * st + kq;
+            RS o;
+            o.edy = ej * s.DY[xi(jr, q)];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) o.s0[t] = s.S0[gi(q, 16 * (cb4 + t) + l16)];
+            return o;
+          },
+          [&](const RS &o) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) ac[t] = mfma16(o.edy, o.s0[t], ac[t]);
+          });
 #pragma unroll
       for (int t = 0; t < 8; ++t)
 #pragma unroll
