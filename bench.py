@@ -43,6 +43,9 @@ SCAN_SOURCES = ["chunk_scan.hip", "chunk_scan_bf16.hip", "quad_scan_f32.hip", "s
 CONV_SOURCES = ["conv1d_silu.hip", "common.h", "kernels.h"]
 DECODE_SOURCES = ["decode_step.hip", "common.h", "kernels.h"]
 NORM_SOURCES = ["gated_rmsnorm.hip", "common.h", "kernels.h"]
+LINEAR_SOURCES = ["linear_bf16.hip", "common.h", "kernels.h"]
+BWD_SOURCES = ["chunk_scan_bwd.hip", "common.h", "kernels.h"]
+FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix
 
 
 def source_hash(files):
@@ -79,9 +82,10 @@ def read_traffic_all(workload):
     if not os.path.exists(path):
         return None
     out, cur = {}, {}
-    sources = {"chunk_scan": SCAN_SOURCES, "plan": SCAN_SOURCES, "combine": SCAN_SOURCES, "conv1d_silu": CONV_SOURCES,
-               "decode_step": DECODE_SOURCES, "gated_rmsnorm": NORM_SOURCES,
-               "decode_mimo": ["decode_mimo.hip", "common.h", "kernels.h"]}
+    sources = {"chunk_scan": SCAN_SOURCES, "plan": SCAN_SOURCES, "combine": SCAN_SOURCES, "quad_scan": SCAN_SOURCES,
+               "conv1d_silu": CONV_SOURCES, "conv_state_out": CONV_SOURCES, "decode_step": DECODE_SOURCES,
+               "gated_rmsnorm": NORM_SOURCES, "decode_mimo": ["decode_mimo.hip", "common.h", "kernels.h"],
+               "linear": LINEAR_SOURCES, "bwd": BWD_SOURCES}
 
     def flush():
         t = cur.get("tag")
@@ -818,11 +822,16 @@ class MixerRun:
         T = Bt * L
         fl_in, fl_out = 2.0 * T * d_in_proj * dm, 2.0 * T * dm * d_inner
 
+        traffic = read_traffic_all(w.name) or {}
+
         def gemm(name, flops, M, Nn, K):
             tf = flops / (ms[name] * 1e-3) / 1e12
+            # operands and result once: x (M x K) and w (N x K) read, y (M x N) written, bf16
             return {"avg_ms": round(ms[name], 5), "M": M, "N": Nn, "K": K, "tflops": round(tf, 1),
                     "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
-                                 "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4)}}
+                                 "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                                 "traffic": traffic.get(f"linear_bf16_{name}")},
+                    "algorithmic_bytes": 2 * (M * K + Nn * K + M * Nn)}
         res = {"workload": f"Mamba-2 mixer, d_model {dm}, d_inner {d_inner}, {w.name}",
                "ms_per_layer": round(layer_ms, 5), "tokens_per_s": round(T / (layer_ms * 1e-3), 1),
                "in_proj": gemm("in_proj", fl_in, T, d_in_proj, dm),
@@ -842,6 +851,17 @@ class MixerRun:
         ref = oracle.linear(h, self.d["in_proj_w"])
         got = self.zx.reshape(T, -1)[rows].float().cpu().numpy()
         return {"in_proj_rel_err": float(f"{rel_err(got, ref):.3e}"), "rows": int(nrows), "bar": 2 ** -8}
+
+
+def bwd_flops(w, Q=32):
+    """Matrix-core flops of the backward's chunked form (chunks of Q tokens),
+    per (batch row, head, chunk): the forward state walk (x^T B), the token
+    products C B^T and dy x^T, the state-sized products G1 B, S0 C, x G1,
+    S0^T dy and dy C^T, and the in-chunk products of dx, dB and dC."""
+    P, N = w.headdim, w.dstate
+    nch = -(-w.seqlen // Q)
+    per = 2 * (3 * Q * Q * N + 2 * Q * Q * P + 6 * Q * P * N)
+    return per * w.batch * w.nheads * nch
 
 
 class BwdRun:
@@ -890,11 +910,17 @@ class BwdRun:
         ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
         T, H, G, P, N = w.batch * w.seqlen, w.nheads, w.ngroups, w.headdim, w.dstate
         nbytes = T * (2 * (2 * H * P) + 2 * (2 * G * N) + 2 * H) * 2 + 2 * w.batch * H * P * N * 4
+        flops = bwd_flops(w)
+        tf = flops / (ms * 1e-3) / 1e12
+        traffic = read_traffic_all(w.name) or {}
         return {"avg_ms": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
                 "algorithmic_bytes": nbytes, "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
                 "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "roofline": {"bound": "mfma", "dtype": "f32", "achieved": round(tf, 1), "peak": FP32_MFMA_PEAK_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(tf / FP32_MFMA_PEAK_TFLOPS, 4), "flops": flops},
+                "traffic_per_kernel": {k: v for k, v in traffic.items() if k.startswith("bwd")} or None,
                 "note": "launch-inclusive time of the three backward launches (chunk states, reverse chunks, "
-                        "fixed-order reductions); fp32 arithmetic"}
+                        "fixed-order reductions); fp32 arithmetic on the fp32 matrix cores"}
 
 
 def main():

@@ -30,7 +30,9 @@ def check(y, ref, what):
     assert np.all(err <= bound), what
 
 
-CASES = [(1, 8, 64), (7, 136, 64), (128, 128, 128), (300, 200, 512), (257, 1032, 4096), (1000, 64, 8192)]
+# the last three take the 256 x 256 tiles (M and N >= 2048), with ragged edges on both sides
+CASES = [(1, 8, 64), (7, 136, 64), (128, 128, 128), (300, 200, 512), (257, 1032, 4096), (1000, 64, 8192),
+         (2048, 2048, 64), (2125, 2088, 256), (2300, 4104, 128)]
 
 
 @pytest.mark.parametrize("M,N,K", CASES, ids=[f"{m}x{n}x{k}" for m, n, k in CASES])
@@ -77,7 +79,7 @@ def test_linear_full_size_sampled(name, M, N, K):
     w = bf16_normal((N, K), K ** -0.5, 24, 2)
     y = ssd.ssd_linear(to_dev(x, BF), to_dev(w, BF))
     torch.cuda.synchronize()
-    rows = sorted({0, 1, 127, 128, 255, 8191, 8192, M - 129, M - 128, M - 1}
+    rows = sorted({0, 1, 127, 128, 255, 256, 511, 512, 8191, 8192, M - 257, M - 256, M - 129, M - 128, M - 1}
                   | set(np.random.default_rng(5).integers(0, M, 14).tolist()))
     yg = to_np(y[rows])
     assert np.all(np.isfinite(to_np(y)))
