@@ -89,15 +89,16 @@ __device__ __forceinline__ u32x4 ld16(const void *base, int64_t elem) {
   return *reinterpret_cast<const u32x4 *>(reinterpret_cast<const T *>(base) + elem);
 }
 
-// the fp32 values of one piece into LDS (dst 16-byte aligned)
-template <typename T> __device__ __forceinline__ void st_piece(float *dst, u32x4 v, float scale = 1.f);
-template <> __device__ __forceinline__ void st_piece<float>(float *dst, u32x4 v, float scale) {
+// the fp32 values of one piece into LDS, in aligned groups of 4 floats:
+// columns q .. q + 3 to dst0 and (bf16 pieces) q + 4 .. q + 7 to dst1
+template <typename T> __device__ __forceinline__ void st_piece(float *dst0, float *dst1, u32x4 v, float scale);
+template <> __device__ __forceinline__ void st_piece<float>(float *dst0, float *, u32x4 v, float scale) {
   f32x4 f;
 #pragma unroll
   for (int k = 0; k < 4; ++k) f[k] = __uint_as_float(v[k]) * scale;
-  *reinterpret_cast<f32x4 *>(dst) = f;
+  *reinterpret_cast<f32x4 *>(dst0) = f;
 }
-template <> __device__ __forceinline__ void st_piece<bf16_t>(float *dst, u32x4 v, float scale) {
+template <> __device__ __forceinline__ void st_piece<bf16_t>(float *dst0, float *dst1, u32x4 v, float scale) {
   f32x4 lo, hi;
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
@@ -106,33 +107,40 @@ template <> __device__ __forceinline__ void st_piece<bf16_t>(float *dst, u32x4 v
     hi[2 * k] = __uint_as_float(v[k + 2] << 16) * scale;
     hi[2 * k + 1] = __uint_as_float(v[k + 2] & 0xffff0000u) * scale;
   }
-  *reinterpret_cast<f32x4 *>(dst) = lo;
-  *reinterpret_cast<f32x4 *>(dst + 4) = hi;
+  *reinterpret_cast<f32x4 *>(dst0) = lo;
+  *reinterpret_cast<f32x4 *>(dst1) = hi;
 }
 
 // rows of `width` elements of one chunk (token rows t0 .. t0 + kQ - 1, row r
 // at element offset r * row_st); piece i of this thread covers row
 // (v * kVec) / width, columns (v * kVec) % width .., v = tid + kT i.  Rows
 // past nv read nothing and hold zeros.
-template <typename T, int width>
+template <typename T, int width, int kThreads = kT>
 struct ChunkRows {
-  static constexpr int kPieces = kQ * width / kVec<T> / kT;
+  static constexpr int kTotal = kQ * width / kVec<T>;                  // pieces of the chunk
+  static constexpr int kPieces = (kTotal + kThreads - 1) / kThreads;  // per thread
   u32x4 v[kPieces];
   __device__ __forceinline__ void load(const void *base, int64_t first, int64_t row_st, int nv, int tid) {
 #pragma unroll
     for (int i = 0; i < kPieces; ++i) {
-      const int e = (tid + kT * i) * kVec<T>, j = e / width, q = e % width;
-      v[i] = j < nv ? ld16<T>(base, first + j * row_st + q) : u32x4{0u, 0u, 0u, 0u};
+      const int pc = tid + kThreads * i, e = pc * kVec<T>, j = e / width, q = e % width;
+      v[i] = (pc < kTotal && j < nv) ? ld16<T>(base, first + j * row_st + q) : u32x4{0u, 0u, 0u, 0u};
     }
   }
-  // into an LDS tile with row pitch `pitch` floats; scale(j) weights row j
-  template <int pitch, typename F>
-  __device__ __forceinline__ void store(float *tile, int tid, F scale) const {
+  // into an LDS tile: element (j, q) at tile[idx(j, q)], 4-float groups
+  // aligned and contiguous; scale(j) weights row j
+  template <typename FI, typename F>
+  __device__ __forceinline__ void store_at(float *tile, int tid, FI idx, F scale) const {
 #pragma unroll
     for (int i = 0; i < kPieces; ++i) {
-      const int e = (tid + kT * i) * kVec<T>, j = e / width, q = e % width;
-      st_piece<T>(tile + j * pitch + q, v[i], scale(j));
+      const int pc = tid + kThreads * i, e = pc * kVec<T>, j = e / width, q = e % width;
+      if (pc < kTotal) st_piece<T>(tile + idx(j, q), tile + idx(j, q + 4), v[i], scale(j));
     }
+  }
+  // ... with row pitch `pitch` floats
+  template <int pitch, typename F>
+  __device__ __forceinline__ void store(float *tile, int tid, F scale) const {
+    store_at(tile, tid, [](int j, int q) { return j * pitch + q; }, scale);
   }
 };
 
@@ -224,52 +232,62 @@ __global__ __launch_bounds__(kT) void bwd_states_kernel(BwdParams p) {
 // Every product of the chunked formulas runs on the fp32 matrix cores
 // (v_mfma_f32_16x16x4_f32: fp32 products, fp32 sums).  Rows of the LDS tiles
 // are padded to 4 (mod 64) floats, so the 16 rows x 4 k values of one
-// operand read fall on 64 different banks.
+// operand read (rows on the lane's 16-lane index) fall on 64 different
+// banks.  (An XOR swizzle that also spreads the reads with the rows on the
+// k slot cost more in address arithmetic than the bank conflicts it removed.)
 constexpr int kNP = kN + 4, kPP = kP + 4, kQP = kQ + 4;
 __device__ __forceinline__ int gi(int q, int n) { return q * kNP + n; }   // G, S0: [p][n]
 __device__ __forceinline__ int bi(int j, int n) { return j * kNP + n; }   // B, C: [token][n]
 __device__ __forceinline__ int xi(int j, int q) { return j * kPP + q; }   // X, DY: [token][p]
 __device__ __forceinline__ int qi(int i, int j) { return i * kQP + j; }   // CB, DYX, Lm, W: [token][token]
 
+// Eight waves (two per SIMD, so one wave's LDS waits are covered by the
+// other's matrix-core work).  Wave w's tiles, in 16 x 16 blocks:
+//   token x token (C B^T for w < 4, dy x^T for w >= 4): rows 16 ((w % 4) / 2), columns 16 (w % 2)
+//   G1 B, S0 C, dx: token rows 16 mj (mj = w / 4), p columns 16 qb (qb = w % 4)
+//   x G1, dB, dC: token rows 16 mj, n columns 16 (2 qb + t), t < 2
+//   G0: p rows 16 qb, n columns 16 (4 mj + t), t < 4
+constexpr int kTC = 512;
 struct BwdSmem {
   float G[kP * kNP];   // adjoint dL/dS leaving the chunk (G1), then entering (G0)
   float S0[kP * kNP];  // state entering the chunk
   float X[kQ * kPP], DY[kQ * kPP], B[kQ * kNP], C[kQ * kNP];
   float CB[kQ * kQP], DYX[kQ * kQP];               // C_i . B_j, dy_i . x_j
   float Lm[kQ * kQP];                              // e^{cs_i - cs_j} for j <= i, else 0
-  float xgb_part[2][kQ];                           // per 64-column half: x_j . (G1 B_j)
-  float ey_part[2][kQ];                            // per 32-column half: dy_j . (S0 C_j)
-  float wcol[8][kQ], wrow[8][kQ];                  // per 4-token part: column / dt-weighted row sums of W
-  float dt[kQ], cs[kQ], z[kQ], ei[kQ], fj[kQ], red[kT / 64];
+  float xgb_part[4][kQ];                           // per 32-column block: x_j . (G1 B_j)
+  float ey_part[4][kQ];                            // per 16-column block: dy_j . (S0 C_j)
+  float wcol[16][kQ], wrow[16][kQ];                // per 2-token part: column / dt-weighted row sums of W
+  float dt[kQ], cs[kQ], z[kQ], ei[kQ], fj[kQ], red[kTC / 64];
 };
 
 template <typename T>
-__global__ __launch_bounds__(kT) void bwd_chunks_kernel(BwdParams p) {
+__global__ __launch_bounds__(kTC) void bwd_chunks_kernel(BwdParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   BwdSmem &s = *reinterpret_cast<BwdSmem *>(smem_raw);
   const int b = blockIdx.x / p.H, h = blockIdx.x % p.H, g = h / (p.H / p.G);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, kq = lane >> 4;
   const float Ah = p.A[h], Dh = p.D ? p.D[h] : 0.f;
   const float *states = p.ws_states + ((int64_t)b * p.H + h) * p.nchunks * kPN;
-  for (int e = tid; e < kPN; e += kT)
+  for (int e = tid; e < kPN; e += kTC)
     s.G[gi(e / kN, e % kN)] = p.dfinal ? p.dfinal[((int64_t)b * p.H + h) * kPN + e] : 0.f;
   float accA = 0.f, accD = 0.f, accBias = 0.f;
-  // this wave's token-row block and column blocks: rows j in [16 mj, +16);
-  // dx / G1 B: columns 16 (2 (w % 2) + t), t < 2; dB / dC / X G1: 16 (4 (w % 2) + t), t < 4
-  const int mj = wave >> 1, cb2 = 2 * (wave & 1), cb4 = 4 * (wave & 1);
+  const bool has_cb = wave < 4;                             // C B^T (else dy x^T)
+  const int mi = (wave & 3) >> 1, ni = wave & 1;            // its token x token block
+  const int mj = wave >> 2, qb = wave & 3, nb0 = 2 * qb, gn0 = 4 * mj;
+  const int jr = 16 * mj + l16;                             // the lane's operand row in the token blocks
   __syncthreads();
 
   for (int c = p.nchunks - 1; c >= 0; --c) {
     const int t0 = c * kQ, nv = min(kQ, p.L - t0);
     // operands of the chunk (rows past the end are zero; their dt is 0)
     {
-      constexpr int kS0 = kPN / 4 / kT;
+      constexpr int kS0 = kPN / 4 / kTC;
       f32x4 s0[kS0];
 #pragma unroll
       for (int i = 0; i < kS0; ++i)
-        s0[i] = *reinterpret_cast<const f32x4 *>(states + (int64_t)c * kPN + 4 * (tid + kT * i));
-      ChunkRows<T, kP> rx, rdy;
-      ChunkRows<T, kN> rb, rc;
+        s0[i] = *reinterpret_cast<const f32x4 *>(states + (int64_t)c * kPN + 4 * (tid + kTC * i));
+      ChunkRows<T, kP, kTC> rx, rdy;
+      ChunkRows<T, kN, kTC> rb, rc;
       const int64_t xo = (((int64_t)b * p.L + t0) * p.H + h) * kP, bo = (((int64_t)b * p.L + t0) * p.G + g) * kN;
       rx.load(p.x, xo, (int64_t)p.H * kP, nv, tid);
       rdy.load(p.dy, xo, (int64_t)p.H * kP, nv, tid);
@@ -278,17 +296,17 @@ __global__ __launch_bounds__(kT) void bwd_chunks_kernel(BwdParams p) {
       chunk_dt<T>(p, b, h, t0, nv, s.dt, s.cs, s.z);
 #pragma unroll
       for (int i = 0; i < kS0; ++i) {
-        const int e = 4 * (tid + kT * i);
+        const int e = 4 * (tid + kTC * i);
         *reinterpret_cast<f32x4 *>(&s.S0[gi(e / kN, e % kN)]) = s0[i];
       }
       const auto one = [](int) { return 1.f; };
-      rx.template store<kPP>(s.X, tid, one);
-      rdy.template store<kPP>(s.DY, tid, one);
-      rb.template store<kNP>(s.B, tid, one);
-      rc.template store<kNP>(s.C, tid, one);
+      rx.store_at(s.X, tid, xi, one);
+      rdy.store_at(s.DY, tid, xi, one);
+      rb.store_at(s.B, tid, bi, one);
+      rc.store_at(s.C, tid, bi, one);
     }
     __syncthreads();
-    for (int e = tid; e < kQ * kQ; e += kT) {
+    for (int e = tid; e < kQ * kQ; e += kTC) {
       const int i = e / kQ, j = e % kQ;
       s.Lm[qi(i, j)] = j <= i ? __expf(s.cs[i] - s.cs[j]) : 0.f;
     }
@@ -297,95 +315,78 @@ __global__ __launch_bounds__(kT) void bwd_chunks_kernel(BwdParams p) {
       s.fj[tid] = __expf(s.cs[kQ - 1] - s.cs[tid]);
     }
 
-    // ---- phase 1: C B^T, dy x^T (one 16 x 16 tile of each per wave), G1 B and
-    // S0 C (rows j, columns p), x G1 (rows j, columns n) ----
-    f32x4 gb[2], xg[4];  // G1 B and x G1 tiles, kept for dx and dB
-    f32x4 s0c[2];
+    // ---- phase 1: C B^T or dy x^T (one 16 x 16 block), G1 B and S0 C (rows
+    // j, columns p), x G1 (rows j, columns n) ----
+    f32x4 gb, s0c, xg[2];  // G1 B and x G1 are kept for dx and dB
     {
-      const int mi = wave >> 1, ni = wave & 1;
-      f32x4 cb = f32x4{}, dyx = f32x4{};
-#pragma unroll
-      for (int t = 0; t < 2; ++t) gb[t] = s0c[t] = f32x4{};
-#pragma unroll
-      for (int t = 0; t < 4; ++t) xg[t] = f32x4{};
-      // contractions over n: C B^T, B G1^T, C S0^T
-      struct RN { float c_i, b_j, b_r, c_r, g[2], s0[2]; };
+      f32x4 tt = f32x4{};  // the token x token block
+      gb = s0c = xg[0] = xg[1] = f32x4{};
+      // contractions over n: C B^T (waves 0..3), B G1^T, C S0^T
+      struct RN { float c_i, b_j, b_r, c_r, g, s0; };
       pipelined<kN / 4, RN>(
           [&](int st) {
             const int k = 4 * st + kq;
             RN o;
-            o.c_i = s.C[bi(16 * mi + l16, k)];
-            o.b_j = s.B[bi(16 * ni + l16, k)];
-            o.b_r = s.B[bi(16 * mj + l16, k)];
-            o.c_r = s.C[bi(16 * mj + l16, k)];
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-              o.g[t] = s.G[gi(16 * (cb2 + t) + l16, k)];
-              o.s0[t] = s.S0[gi(16 * (cb2 + t) + l16, k)];
-            }
+            o.c_i = has_cb ? s.C[bi(16 * mi + l16, k)] : 0.f;
+            o.b_j = has_cb ? s.B[bi(16 * ni + l16, k)] : 0.f;
+            o.b_r = s.B[bi(jr, k)];
+            o.c_r = s.C[bi(jr, k)];
+            o.g = s.G[gi(16 * qb + l16, k)];
+            o.s0 = s.S0[gi(16 * qb + l16, k)];
             return o;
           },
           [&](const RN &o) {
-            cb = mfma16(o.c_i, o.b_j, cb);
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-              gb[t] = mfma16(o.b_r, o.g[t], gb[t]);
-              s0c[t] = mfma16(o.c_r, o.s0[t], s0c[t]);
-            }
+            if (has_cb) tt = mfma16(o.c_i, o.b_j, tt);
+            gb = mfma16(o.b_r, o.g, gb);
+            s0c = mfma16(o.c_r, o.s0, s0c);
           });
-      // contractions over p: dy x^T, x G1
-      struct RP { float dy_i, x_j, x_r, g[4]; };
+      // contractions over p: dy x^T (waves 4..7), x G1
+      struct RP { float dy_i, x_j, x_r, g[2]; };
       pipelined<kP / 4, RP>(
           [&](int st) {
             const int k = 4 * st + kq;
             RP o;
-            o.dy_i = s.DY[xi(16 * mi + l16, k)];
-            o.x_j = s.X[xi(16 * ni + l16, k)];
-            o.x_r = s.X[xi(16 * mj + l16, k)];
+            o.dy_i = has_cb ? 0.f : s.DY[xi(16 * mi + l16, k)];
+            o.x_j = has_cb ? 0.f : s.X[xi(16 * ni + l16, k)];
+            o.x_r = s.X[xi(jr, k)];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) o.g[t] = s.G[gi(k, 16 * (cb4 + t) + l16)];
+            for (int t = 0; t < 2; ++t) o.g[t] = s.G[gi(k, 16 * (nb0 + t) + l16)];
             return o;
           },
           [&](const RP &o) {
-            dyx = mfma16(o.dy_i, o.x_j, dyx);
+            if (!has_cb) tt = mfma16(o.dy_i, o.x_j, tt);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) xg[t] = mfma16(o.x_r, o.g[t], xg[t]);
+            for (int t = 0; t < 2; ++t) xg[t] = mfma16(o.x_r, o.g[t], xg[t]);
           });
+      float *ttd = has_cb ? s.CB : s.DYX;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        s.CB[qi(16 * mi + 4 * kq + r, 16 * ni + l16)] = cb[r];
-        s.DYX[qi(16 * mi + 4 * kq + r, 16 * ni + l16)] = dyx[r];
-      }
-    }
-    {
+      for (int r = 0; r < 4; ++r) ttd[qi(16 * mi + 4 * kq + r, 16 * ni + l16)] = tt[r];
       // per-token partial dot products over this wave's columns: the lane
       // holds rows j = 16 mj + 4 kq + r, column l16 of each block; its blocks
       // are summed in the lane, then over the 16 lanes of the row
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = 16 * mj + 4 * kq + r;
-        float ve = 0.f, vx = 0.f;
+        float ve = s0c[r] * s.DY[xi(j, 16 * qb + l16)], vx = 0.f;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) ve = fmaf(s0c[t][r], s.DY[xi(j, 16 * (cb2 + t) + l16)], ve);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) vx = fmaf(xg[t][r], s.B[bi(j, 16 * (cb4 + t) + l16)], vx);
+        for (int t = 0; t < 2; ++t) vx = fmaf(xg[t][r], s.B[bi(j, 16 * (nb0 + t) + l16)], vx);
 #pragma unroll
         for (int off = 8; off >= 1; off >>= 1) {
           ve += __shfl_xor(ve, off, 16);
           vx += __shfl_xor(vx, off, 16);
         }
         if (l16 == 0) {
-          s.ey_part[wave & 1][j] = ve;
-          s.xgb_part[wave & 1][j] = vx;
+          s.ey_part[qb][j] = ve;
+          s.xgb_part[qb][j] = vx;
         }
       }
     }
     {
-      // <G1, S0>, four independent chains of 16-byte reads
+      // <G1, S0>, 16-byte reads
       f32x4 acc4 = f32x4{};
 #pragma unroll
-      for (int i = 0; i < kPN / 4 / kT; ++i) {
-        const int e = 4 * (tid + kT * i);
+      for (int i = 0; i < kPN / 4 / kTC; ++i) {
+        const int e = 4 * (tid + kTC * i);
         const f32x4 gv = *reinterpret_cast<const f32x4 *>(&s.G[gi(e / kN, e % kN)]);
         const f32x4 sv = *reinterpret_cast<const f32x4 *>(&s.S0[gi(e / kN, e % kN)]);
 #pragma unroll
@@ -401,12 +402,12 @@ __global__ __launch_bounds__(kT) void bwd_chunks_kernel(BwdParams p) {
     // ---- phase 2: per-token scalars ----
     {
       // W_ij = Lm_ij CB_ij DYX_ij: thread (part, j) sums column j over rows
-      // i in [4 part, +4) and row j over columns k in [4 part, +4), weighted by dt_k
+      // i in [2 part, +2) and row j over columns k in [2 part, +2), weighted by dt_k
       const int j = tid & 31, part = tid >> 5;
       float cp = 0.f, rp = 0.f;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = 4 * part + u;
+      for (int u = 0; u < 2; ++u) {
+        const int i = 2 * part + u;
         cp = fmaf(s.Lm[qi(i, j)] * s.CB[qi(i, j)], s.DYX[qi(i, j)], cp);
         rp = fmaf(s.Lm[qi(j, i)] * s.CB[qi(j, i)] * s.DYX[qi(j, i)], s.dt[i], rp);
       }
@@ -414,23 +415,28 @@ __global__ __launch_bounds__(kT) void bwd_chunks_kernel(BwdParams p) {
       s.wrow[part][j] = rp;
     }
     __syncthreads();
-    const float G1S0 = s.red[0] + s.red[1] + s.red[2] + s.red[3];
+    float G1S0 = 0.f;
+#pragma unroll
+    for (int w = 0; w < kTC / 64; ++w) G1S0 += s.red[w];
     const float eQ = s.ei[kQ - 1];
     if (wave == 0) {
-      // lanes 0..31: token j; column sums sum_{i>=j} W_ij by lanes 0..31 and the
-      // dt-weighted row sums sum_{k<=j} W_jk dt_k by lanes 32..63
       const int j = lane & 31;
       float dcs = 0.f, dexp = 0.f, tot_part = 0.f, dtj = 0.f;
       if (lane < 32) {
         float acc = 0.f, row = 0.f;  // sum_{i>=j} W_ij and sum_{k<=j} W_jk dt_k
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
+        for (int t = 0; t < 16; ++t) {
           acc += s.wcol[t][j];
           row += s.wrow[t][j];
         }
         const float fj = s.fj[j];
         dtj = s.dt[j];
-        const float xgb = s.xgb_part[0][j] + s.xgb_part[1][j], ey = s.ey_part[0][j] + s.ey_part[1][j];
+        float xgb = 0.f, ey = 0.f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          xgb += s.xgb_part[t][j];
+          ey += s.ey_part[t][j];
+        }
         dexp = fmaf(fj, xgb, acc);                               // f_j x_j.(G1 B_j) + sum_{i>=j} W_ij
         dcs = s.ei[j] * ey + row - dtj * acc - fj * dtj * xgb;
         tot_part = fj * dtj * xgb;
@@ -468,26 +474,23 @@ __global__ __launch_bounds__(kT) void bwd_chunks_kernel(BwdParams p) {
       }
     }
 
-    // ---- phase 3: dx, dB, dC (this wave's tiles) and G0 (rows p in [16 w, +16)) ----
+    // ---- phase 3: dx, dB, dC (this wave's blocks) and G0 (rows p in [16 qb, +16)) ----
     {
-      // dx[j][q] = D dy_j[q] + dt_j (f_j (G1 B_j)[q] + sum_{i>=j} Lm_ij CB_ij dy_i[q])
       // dx[j][q] = D dy_j[q] + dt_j (f_j (G1 B_j)[q] + sum_{i>=j} Lm_ij CB_ij dy_i[q]);
       // dB[j][n] = dt_j (f_j (x_j G1)[n] + sum_{i>=j} Lm_ij DYX_ij C_i[n]);
       // dC[j][n] = e_j (S0^T dy_j)[n] + sum_{k<=j} Lm_jk dt_k DYX_jk B_k[n];
       // G0[q][n] = e^{cs_Q} G1[q][n] + sum_i e_i dy_i[q] C_i[n], in place: this wave
-      // reads and writes only its own tiles of G, and no other product reads G now
-      const int jr = 16 * mj + l16;  // the operand row of this lane
-      f32x4 ax[2], ab[4], ac[4], g0[8];
+      // reads and writes only its own blocks of G, and no other product reads G now
+      f32x4 ax = f32x4{}, ab[2], ac[2], g0[4];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) ax[t] = f32x4{};
+      for (int t = 0; t < 2; ++t) ab[t] = ac[t] = f32x4{};
 #pragma unroll
-      for (int t = 0; t < 4; ++t) ab[t] = ac[t] = f32x4{};
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) g0[t][r] = eQ * s.G[gi(16 * wave + 4 * kq + r, 16 * t + l16)];
-      // contractions over the chunk's tokens (k)
-      struct RQ { float lcb, ldyx, ldt, edy, dy[2], c[8], b[4]; };
+        for (int r = 0; r < 4; ++r) g0[t][r] = eQ * s.G[gi(16 * qb + 4 * kq + r, 16 * (gn0 + t) + l16)];
+      // contractions over the chunk's tokens (k); dy_k[16 qb + l16] is both the
+      // B operand of dx and, times e_k, the A operand of G0
+      struct RQ { float lcb, ldyx, ldt, ek, dy, cb[2], cg[4], bb[2]; };
       pipelined<kQ / 4, RQ>(
           [&](int st) {
             const int k = 4 * st + kq;
@@ -496,61 +499,60 @@ __global__ __launch_bounds__(kT) void bwd_chunks_kernel(BwdParams p) {
             o.lcb = lkj * s.CB[qi(k, jr)];
             o.ldyx = lkj * s.DYX[qi(k, jr)];
             o.ldt = s.Lm[qi(jr, k)] * s.dt[k] * s.DYX[qi(jr, k)];
-            o.edy = s.ei[k] * s.DY[xi(k, 16 * wave + l16)];
+            o.ek = s.ei[k];
+            o.dy = s.DY[xi(k, 16 * qb + l16)];
 #pragma unroll
-            for (int t = 0; t < 2; ++t) o.dy[t] = s.DY[xi(k, 16 * (cb2 + t) + l16)];
+            for (int t = 0; t < 2; ++t) {
+              o.cb[t] = s.C[bi(k, 16 * (nb0 + t) + l16)];
+              o.bb[t] = s.B[bi(k, 16 * (nb0 + t) + l16)];
+            }
 #pragma unroll
-            for (int t = 0; t < 8; ++t) o.c[t] = s.C[bi(k, 16 * t + l16)];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) o.b[t] = s.B[bi(k, 16 * (cb4 + t) + l16)];
+            for (int t = 0; t < 4; ++t) o.cg[t] = s.C[bi(k, 16 * (gn0 + t) + l16)];
             return o;
           },
           [&](const RQ &o) {
+            ax = mfma16(o.lcb, o.dy, ax);
 #pragma unroll
-            for (int t = 0; t < 2; ++t) ax[t] = mfma16(o.lcb, o.dy[t], ax[t]);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              ab[t] = mfma16(o.ldyx, cb4 ? o.c[4 + t] : o.c[t], ab[t]);
-              ac[t] = mfma16(o.ldt, o.b[t], ac[t]);
+            for (int t = 0; t < 2; ++t) {
+              ab[t] = mfma16(o.ldyx, o.cb[t], ab[t]);
+              ac[t] = mfma16(o.ldt, o.bb[t], ac[t]);
             }
+            const float edy = o.ek * o.dy;
 #pragma unroll
-            for (int t = 0; t < 8; ++t) g0[t] = mfma16(o.edy, o.c[t], g0[t]);
+            for (int t = 0; t < 4; ++t) g0[t] = mfma16(edy, o.cg[t], g0[t]);
           });
       // ... and over p: the e_j S0^T dy_j term of dC
       const float ej = s.ei[jr];
-      struct RS { float edy, s0[4]; };
+      struct RS { float edy, s0[2]; };
       pipelined<kP / 4, RS>(
           [&](int st) {
             const int q = 4 * st + kq;
             RS o;
             o.edy = ej * s.DY[xi(jr, q)];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) o.s0[t] = s.S0[gi(q, 16 * (cb4 + t) + l16)];
+            for (int t = 0; t < 2; ++t) o.s0[t] = s.S0[gi(q, 16 * (nb0 + t) + l16)];
             return o;
           },
           [&](const RS &o) {
 #pragma unroll
-            for (int t = 0; t < 4; ++t) ac[t] = mfma16(o.edy, o.s0[t], ac[t]);
+            for (int t = 0; t < 2; ++t) ac[t] = mfma16(o.edy, o.s0[t], ac[t]);
           });
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s.G[gi(16 * wave + 4 * kq + r, 16 * t + l16)] = g0[t][r];
+        for (int r = 0; r < 4; ++r) s.G[gi(16 * qb + 4 * kq + r, 16 * (gn0 + t) + l16)] = g0[t][r];
       // outputs: the lane holds rows j = 16 mj + 4 kq + r, column l16 of each block
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = 16 * mj + 4 * kq + r;
         if (j >= nv) continue;
         const float dtj = s.dt[j], fj = s.fj[j];
+        const int q = 16 * qb + l16;
+        const float v = fmaf(Dh, s.DY[xi(j, q)], dtj * fmaf(fj, gb[r], ax[r]));
+        reinterpret_cast<T *>(p.dx)[(((int64_t)b * p.L + t0 + j) * p.H + h) * kP + q] = from_f32<T>(v);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          const int q = 16 * (cb2 + t) + l16;
-          const float v = fmaf(Dh, s.DY[xi(j, q)], dtj * fmaf(fj, gb[t][r], ax[t][r]));
-          reinterpret_cast<T *>(p.dx)[(((int64_t)b * p.L + t0 + j) * p.H + h) * kP + q] = from_f32<T>(v);
-        }
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int n = 16 * (cb4 + t) + l16;
+          const int n = 16 * (nb0 + t) + l16;
           const int64_t o = (((int64_t)b * p.L + t0 + j) * p.H + h) * kN + n;   // per-head partials
           p.ws_dB[o] = dtj * fmaf(fj, xg[t][r], ab[t][r]);
           p.ws_dC[o] = ac[t][r];
@@ -560,7 +562,7 @@ __global__ __launch_bounds__(kT) void bwd_chunks_kernel(BwdParams p) {
     __syncthreads();  // G0 complete; the chunk's tiles are rewritten by the next chunk
   }
   if (p.dinit)
-    for (int e = tid; e < kPN; e += kT) p.dinit[((int64_t)b * p.H + h) * kPN + e] = s.G[gi(e / kN, e % kN)];
+    for (int e = tid; e < kPN; e += kTC) p.dinit[((int64_t)b * p.H + h) * kPN + e] = s.G[gi(e / kN, e % kN)];
   if (tid == 0) {
     p.ws_scalars[((int64_t)b * p.H + h) * 3 + 0] = accA;
     p.ws_scalars[((int64_t)b * p.H + h) * 3 + 1] = accD;
@@ -613,7 +615,7 @@ hipError_t launch_t(const BwdParams &p, hipStream_t stream) {
   const size_t lds = sizeof(BwdSmem);
   e = set_max_dynamic_lds(reinterpret_cast<const void *>(bwd_chunks_kernel<T>), lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_chunks_kernel<T>, dim3(units), dim3(kT), lds, stream, p);
+  hipLaunchKernelGGL(bwd_chunks_kernel<T>, dim3(units), dim3(kTC), lds, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t total = std::max<int64_t>((int64_t)p.batch * p.L * p.G * kN, p.H);

@@ -70,6 +70,24 @@ def test_bwd_dt_zero_heads():
     _check(w, d, 1e-4)
 
 
+def test_bwd_empty_sequence():
+    """seqlen 0: the final state is the initial one, so d_initial_state is
+    d_final_state exactly and every per-head gradient is zero."""
+    H, G = 8, 2
+    x = torch.empty((2, 0, H, 64), dtype=BF, device=DEV)
+    dt = torch.empty((2, 0, H), dtype=BF, device=DEV)
+    B = torch.empty((2, 0, G, 128), dtype=BF, device=DEV)
+    df = to_dev(inputs.normal((2, H, 64, 128), 0.1, 3, 62, False))
+    A = -torch.ones(H, device=DEV)
+    g = ssd.ssd_chunk_scan_bwd(x, dt, A, B, B.clone(), x.clone(), dt_bias=torch.zeros(H, device=DEV),
+                               D=torch.ones(H, device=DEV), d_final_state=df, want_d_initial_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(g["d_initial_state"], df)
+    for k in ("dA", "dD", "d_dt_bias"):
+        assert torch.count_nonzero(g[k]) == 0, k
+    assert g["dx"].shape == x.shape and g["dB"].shape == B.shape
+
+
 def test_bwd_repeat_runs_bitwise_identical():
     w, d = _case(2, 90, 8, 2, True, seed=9)
     args = (to_dev(d["x"], BF), to_dev(d["dt"], BF), to_dev(d["A"]), to_dev(d["B"], BF), to_dev(d["C"], BF),
