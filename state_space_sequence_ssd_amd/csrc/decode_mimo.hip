@@ -163,9 +163,197 @@ __global__ __launch_bounds__(threads_for<R>()) void decode_mimo_kernel(MimoParam
     for (int e = threadIdx.x; e < kDState * R; e += kThreads) pBg[e] = Bg[e];
 }
 
+// bf16 inputs, ranks 2..8: the same stream over the state, with the rank
+// sums x . B_n and x_prev . B_prev,n taken by v_dot2_f32_bf16 on the inputs'
+// own bf16 pairs (exact products, fp32 sums).  That halves both the
+// instructions of those sums and the registers that hold the lane's rows of
+// B and B_prev, and X, X_prev and B, B_prev stay bf16 in LDS; y goes straight
+// from the reducing lanes to HBM.  Per lane about half the registers and per
+// workgroup about a third of the LDS of the kernel above, so two workgroups
+// (16 waves) share a CU.
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, a), __builtin_bit_cast(bf16x2v, b), c, false);
+}
+
+constexpr int kMimoThreads16 = 256;
+template <int R, bool kTrap>
+__global__ __launch_bounds__(kMimoThreads16) void decode_mimo_bf16_kernel(MimoParams p) {
+  constexpr int R2 = R / 2;  // bf16 pairs per row of X, B
+  extern __shared__ __attribute__((aligned(16))) float smem16[];
+  const int b = blockIdx.x / p.G;
+  const int g = blockIdx.x % p.G;
+  const int hpg = p.H / p.G;
+  const int nxw = hpg * kHeadDim * R2;                            // the group's X words (bf16 pairs)
+  uint32_t *sx = reinterpret_cast<uint32_t *>(smem16);            // [hpg][P][R2]
+  uint32_t *spx = sx + nxw;                                       // [hpg][P][R2] previous X (trapezoid)
+  uint32_t *sB = spx + (kTrap ? nxw : 0);                         // [N][R2]
+  uint32_t *spB = sB + kDState * R2;                              // [N][R2] previous B (trapezoid)
+  float *sC = reinterpret_cast<float *>(spB + (kTrap ? kDState * R2 : 0));  // [N][R] fp32
+  float *scoef = sC + kDState * R;                                // [hpg][3]: a, lam dt, (1 - lam) dt a
+
+  const uint32_t *xg = reinterpret_cast<const uint32_t *>(reinterpret_cast<const bf16_t *>(p.x) + (int64_t)b * p.x_sb) +
+                       (int64_t)g * nxw;
+  const uint32_t *Bg =
+      reinterpret_cast<const uint32_t *>(reinterpret_cast<const bf16_t *>(p.B) + (int64_t)b * p.B_sb) +
+      (int64_t)g * kDState * R2;
+  const bf16_t *Cg = reinterpret_cast<const bf16_t *>(p.C) + (int64_t)b * p.C_sb + (int64_t)g * kDState * R;
+  uint32_t *pxg = kTrap ? reinterpret_cast<uint32_t *>(p.prev_x) + ((int64_t)b * p.H + (int64_t)g * hpg) * kHeadDim * R2
+                        : nullptr;
+  uint32_t *pBg = kTrap ? reinterpret_cast<uint32_t *>(p.prev_B) + ((int64_t)b * p.G + g) * kDState * R2 : nullptr;
+  for (int e = threadIdx.x; e < nxw; e += kMimoThreads16) {
+    sx[e] = xg[e];
+    if (kTrap) spx[e] = pxg[e];
+  }
+  for (int e = threadIdx.x; e < kDState * R2; e += kMimoThreads16) {
+    sB[e] = Bg[e];
+    if (kTrap) spB[e] = pBg[e];
+  }
+  for (int e = threadIdx.x; e < kDState * R; e += kMimoThreads16) sC[e] = bf16_to_f32(Cg[e]);
+  const bf16_t *dtp = reinterpret_cast<const bf16_t *>(p.dt) + (int64_t)b * p.dt_sb;
+  const bf16_t *lp = (kTrap && p.lam) ? reinterpret_cast<const bf16_t *>(p.lam) + (int64_t)b * p.lam_sb : nullptr;
+  for (int hl = threadIdx.x; hl < hpg; hl += kMimoThreads16) {
+    const int h = g * hpg + hl;
+    const float dt = softplus_f32(bf16_to_f32(dtp[h]) + (p.dt_bias ? p.dt_bias[h] : 0.f));
+    const float a = __expf(dt * p.A[h]);
+    const float lam = kTrap ? (lp ? bf16_to_f32(lp[h]) : 0.5f) : 1.f;
+    scoef[3 * hl] = a;
+    scoef[3 * hl + 1] = lam * dt;
+    scoef[3 * hl + 2] = (1.f - lam) * dt * a;
+  }
+  __syncthreads();
+
+  // this lane's four state columns n = 4 lane32 + k: their rows of B, B_prev (bf16 pairs) and C
+  const int lane32 = threadIdx.x & 31;
+  uint32_t Bw[4][R2], Pw[kTrap ? 4 : 1][R2];
+  float Cv[4][R];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+#pragma unroll
+    for (int m = 0; m < R2; ++m) {
+      Bw[k][m] = sB[(4 * lane32 + k) * R2 + m];
+      if (kTrap) Pw[k][m] = spB[(4 * lane32 + k) * R2 + m];
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) Cv[k][r] = sC[(4 * lane32 + k) * R + r];
+  }
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  bf16_t *yb = reinterpret_cast<bf16_t *>(p.y) + (int64_t)b * p.y_sb + (int64_t)g * hpg * kHeadDim * R;
+  for (int hl = wave; hl < hpg; hl += kMimoThreads16 / 64) {
+    const int h = g * hpg + hl;
+    f32x4 *S = reinterpret_cast<f32x4 *>(p.ssm_state + ((int64_t)b * p.H + h) * kHeadDim * kDState);
+    const float a = scoef[3 * hl], cE = scoef[3 * hl + 1], cP = scoef[3 * hl + 2];
+    const float dskip = p.D ? p.D[h] : 0.f;
+#pragma unroll 1
+    for (int c = 0; c < 4; ++c) {
+      f32x4 v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = __builtin_nontemporal_load(S + (c * 8 + i) * 64 + lane);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int prow = (c * 8 + i) * 2 + (lane >> 5);
+        const uint32_t *xr = sx + (hl * kHeadDim + prow) * R2;
+        const uint32_t *pr = spx + (hl * kHeadDim + prow) * R2;
+        uint32_t xs[R2], ps[kTrap ? R2 : 1];
+#pragma unroll
+        for (int m = 0; m < R2; ++m) {
+          xs[m] = xr[m];
+          if (kTrap) ps[m] = pr[m];
+        }
+        f32x4 n;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          float cur = 0.f, prev = 0.f;
+#pragma unroll
+          for (int m = 0; m < R2; ++m) {
+            cur = dot2(xs[m], Bw[k][m], cur);
+            if (kTrap) prev = dot2(ps[m], Pw[k][m], prev);
+          }
+          float u = fmaf(a, v[i][k], cE * cur);
+          if (kTrap) u = fmaf(cP, prev, u);
+          n[k] = u;
+        }
+        __builtin_nontemporal_store(n, S + (c * 8 + i) * 64 + lane);
+        float part[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          part[r] = n[0] * Cv[0][r] + n[1] * Cv[1][r] + n[2] * Cv[2][r] + n[3] * Cv[3][r];
+        // the row's R sums over the 32 lanes as a reduce-scatter (as in the
+        // kernel above); afterwards every lane holds the sum of column rsel
+        int rsel = 0;
+#pragma unroll
+        for (int off = 16, cnt = R; off >= 1; off >>= 1) {
+          if (cnt > 1) {
+            const int half = cnt / 2;
+            const bool upper = (lane32 & off) != 0;
+#pragma unroll
+            for (int j = 0; j < half; ++j) {
+              const float send = upper ? part[j] : part[j + half];
+              const float keep = upper ? part[j + half] : part[j];
+              part[j] = keep + __shfl_xor(send, off, 32);
+            }
+            rsel += upper ? half : 0;
+            cnt = half;
+          } else {
+            part[0] += __shfl_xor(part[0], off, 32);
+          }
+        }
+        // lanes of one 32 / R block hold the same sum: its first lane writes it
+        if ((lane32 & (32 / R - 1)) == 0) {
+          const uint32_t xw = xr[rsel >> 1];
+          const float xv = (rsel & 1) ? hi_bf16(xw) : lo_bf16(xw);
+          yb[(hl * kHeadDim + prow) * R + rsel] = f32_to_bf16(fmaf(dskip, xv, part[0]));
+        }
+      }
+    }
+  }
+  if (kTrap) {
+    __syncthreads();  // every read of the previous-input caches is done
+    // the new token's X and B become the previous ones
+    for (int e = threadIdx.x; e < nxw; e += kMimoThreads16) pxg[e] = sx[e];
+    for (int e = threadIdx.x; e < kDState * R2; e += kMimoThreads16) pBg[e] = sB[e];
+  }
+}
+
+size_t mimo_bf16_lds_bytes(int hpg, int R, bool trapezoid) {
+  const size_t nxw = (size_t)hpg * kHeadDim * (R / 2);
+  return 4 * ((trapezoid ? 2 : 1) * nxw + (trapezoid ? 2 : 1) * (size_t)kDState * (R / 2) + (size_t)kDState * R +
+              3 * (size_t)hpg);
+}
+
+template <int R>
+hipError_t launch_bf16(const MimoParams &p, hipStream_t s) {
+  const size_t lds = mimo_bf16_lds_bytes(p.H / p.G, R, p.trapezoid != 0);
+  dim3 grid(p.batch * p.G), block(kMimoThreads16);
+  if (p.trapezoid) {
+    auto fn = decode_mimo_bf16_kernel<R, true>;
+    if (lds > 65536) {
+      const hipError_t e = set_max_dynamic_lds(reinterpret_cast<const void *>(fn), lds);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(fn, grid, block, lds, s, p);
+  } else {
+    auto fn = decode_mimo_bf16_kernel<R, false>;
+    if (lds > 65536) {
+      const hipError_t e = set_max_dynamic_lds(reinterpret_cast<const void *>(fn), lds);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(fn, grid, block, lds, s, p);
+  }
+  return hipGetLastError();
+}
+
 template <typename T, int R>
 hipError_t launch_r(const MimoParams &p, hipStream_t s) {
   const int hpg = p.H / p.G;
+  // the bf16 kernel reads X and B as 4-byte pairs: even batch strides and 4-byte aligned bases
+  const bool pairs = ((reinterpret_cast<uintptr_t>(p.x) | reinterpret_cast<uintptr_t>(p.B) |
+                       reinterpret_cast<uintptr_t>(p.prev_x) | reinterpret_cast<uintptr_t>(p.prev_B)) & 3) == 0 &&
+                     (p.x_sb % 2) == 0 && (p.B_sb % 2) == 0;
+  if constexpr (R >= 2 && std::is_same<T, bf16_t>::value) {
+    if (pairs) return launch_bf16<R>(p, s);
+  }
   const size_t lds = mimo_lds_bytes(hpg, R, p.trapezoid != 0);
   dim3 grid(p.batch * p.G), block(threads_for<R>());
   if (p.trapezoid) {

@@ -78,6 +78,39 @@ def test_mimo_rank1_euler_matches_mamba2_decode():
     assert rel(to_np(y[..., 0]), to_np(y2)) <= 2e-2
 
 
+def _odd_rows(a, dtype):
+    """The same values as a (batch, ...) tensor whose batch stride is odd (each
+    row contiguous, one element of padding after it)."""
+    batch, row = a.shape[0], int(np.prod(a.shape[1:]))
+    buf = torch.zeros(batch * (row + 1), dtype=dtype, device=DEV)
+    t = buf.as_strided(a.shape, (row + 1,) + tuple(torch.empty(a.shape[1:]).stride()))
+    t.copy_(to_dev(a, dtype))
+    return t
+
+
+@pytest.mark.parametrize("R", [2, 8])
+def test_mimo_odd_batch_strides(R):
+    """bf16 x and B with odd batch strides (their bf16 pairs are not 4-byte
+    aligned, so the call takes the elementwise kernel): against the oracle."""
+    batch, H, G = 3, 16, 4
+    print(f"case mimo odd strides R={R}", flush=True)
+    d = inputs.mimo_decode_inputs(batch, H, G, R, seed=40 + R)
+    st = inputs.decode_state_host(inputs.DecodeWorkload("m", batch, H, G, 1), 41, R)
+    state = to_dev(st)
+    x, B = _odd_rows(d["x"], BF), _odd_rows(d["B"], BF)
+    assert x.stride(0) % 2 == 1 and B.stride(0) % 2 == 1
+    px, pb = to_dev(d["prev_x"], BF), to_dev(d["prev_B"], BF)
+    y = ssd.ssd_decode_step_mimo(x, B, to_dev(d["C"], BF), to_dev(d["dt"], BF), to_dev(d["A"]), state,
+                                 dt_bias=to_dev(d["dt_bias"]), D=to_dev(d["D"]), trapezoid=True,
+                                 lam=to_dev(d["lam"], BF), prev_x=px, prev_B=pb)
+    torch.cuda.synchronize()
+    ry, rs, rpx, rpb = oracle.decode_step_mimo(d["x"], d["B"], d["C"], d["dt"], d["dt_bias"], d["A"], d["D"], st,
+                                               trapezoid=True, lam=d["lam"], prev_x=d["prev_x"],
+                                               prev_B=d["prev_B"])
+    assert rel(to_np(y), ry) <= 2e-2 and rel(to_np(state), rs) <= 2e-2
+    assert np.array_equal(to_np(px), rpx) and np.array_equal(to_np(pb), rpb)
+
+
 def test_mimo_trapezoid_chain():
     """Six tokens in a row on the GPU, each step's previous-input caches
     carried on the device, against the oracle's chain."""
