@@ -81,6 +81,32 @@ def test_model_chunk_sizes(q):
     assert torch.equal(y, y128) and torch.equal(fs, fs128)
 
 
+def test_fp32_block_length_invariance():
+    """One fp32 sequence of 1,000 tokens through kernels that cut it into
+    different blocks: the masked quadratic form over the whole row (one block
+    of 1,000), the chunked fp32 kernel as a one-sequence packed stream (64-token
+    sub-chunks), and the same with 128-token segments joined by the combine.
+    The chunked form is exact for any block length, so the three agree to
+    fp32 rounding and each matches the oracle.  Bound 2e-5 of the largest
+    value: the chunked kernel hands the state from chunk to chunk 16 times
+    (an fp32 decay product and sum each, ~2^-24 relative per operation) on
+    top of fp32 cumulative log-decays within a chunk; measured 7.6e-6 for
+    the final state, 2e-7 for y."""
+    w = W("f32_b1_l1000_h8_g2_init", 1, 1000, 8, 2, bf16=False, init=0.3)
+    d = inputs.make_scan_inputs(w, seed=23)
+    ry, rf = oracle_layer(d, w)
+    y_quad, f_quad = gpu_layer(d, w)
+    dp = dict(d, seq_idx=np.zeros(w.seqlen, np.int32))
+    y_chunk, f_chunk = gpu_layer(dp, w)
+    y_seg, f_seg = gpu_layer(dp, w, seg_chunks=1)
+    for name, (y, f) in {"quad": (y_quad, f_quad), "chunk": (y_chunk, f_chunk), "seg": (y_seg, f_seg)}.items():
+        ey, ef = rel(to_np(y), ry), rel(to_np(f), rf)
+        print(f"  {name}: y rel err {ey:.3e}  final-state rel err {ef:.3e}", flush=True)
+        assert ey <= 1e-4 and ef <= 1e-4, name
+    for a_, b_ in ((y_quad, y_chunk), (y_chunk, y_seg), (f_quad, f_chunk), (f_chunk, f_seg)):
+        assert rel(to_np(a_), to_np(b_)) <= 2e-5
+
+
 def test_packed_many_short_sequences():
     """5,000 sequences of 0-3 tokens: more work items than the plan ranks by
     length (they keep list order), empty sequences among them, and chunks
