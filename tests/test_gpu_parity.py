@@ -107,6 +107,19 @@ def test_fp32_block_length_invariance():
         assert rel(to_np(a_), to_np(b_)) <= 2e-5
 
 
+def test_fp32_long_row():
+    """fp32 inputs over 16,384 tokens (256 chunk hand-offs of the fp32 state,
+    automatic segments): y and the final state within the fp32 bar."""
+    w = W("f32_b1_l16384_h8_g2_init", 1, 16384, 8, 2, bf16=False, init=0.3)
+    print(f"case {w.name}", flush=True)
+    d = inputs.make_scan_inputs(w, seed=29)
+    y, fs = gpu_layer(d, w)
+    ry, rf = oracle_layer(d, w)
+    ey, ef = rel(to_np(y), ry), rel(to_np(fs), rf)
+    print(f"  y rel err {ey:.3e}  final-state rel err {ef:.3e}", flush=True)
+    assert ey <= 1e-4 and ef <= 1e-4
+
+
 def test_packed_many_short_sequences():
     """5,000 sequences of 0-3 tokens: more work items than the plan ranks by
     length (they keep list order), empty sequences among them, and chunks
