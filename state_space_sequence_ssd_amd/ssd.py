@@ -496,7 +496,7 @@ def ssd_linear(x: torch.Tensor, w: torch.Tensor, y: Optional[torch.Tensor] = Non
     if y2.data_ptr() != y.data_ptr():
         raise ValueError("y's leading dims must be packed")
     for t, name in ((x2, "x"), (w, "w"), (y2, "y")):
-        if t.shape[0] > 1 and t.stride(1) != 1:
+        if t.shape[1] > 1 and t.stride(1) != 1:
             raise ValueError(f"{name} must have a unit-stride last dim")
     _on_gpu(x, w=w, y=y)
     a = SsdLinearArgs(ctypes.sizeof(SsdLinearArgs), _dtype_code(x), M, N, K,
@@ -665,7 +665,7 @@ def ssd_decode_step_mimo(x: torch.Tensor, B: torch.Tensor, C: torch.Tensor, dt: 
     _shape(prev_x, "prev_x", (batch, H, P, R))
     _shape(prev_B, "prev_B", (batch, G, N, R))
     for name, t in (("x", x), ("B", B), ("C", C), ("y", y)):
-        if t is not None and not t[0].is_contiguous():
+        if t is not None and t.shape[0] > 0 and not t[0].is_contiguous():
             raise ValueError(f"{name}: each batch row must be contiguous")
     for name, t in (("dt", dt), ("lam", lam)):
         if t is not None and t.stride(1) != 1:

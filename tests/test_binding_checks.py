@@ -158,3 +158,22 @@ def test_decode_good_cpu_tensors_refused_as_host_memory():
     for conv in (True, False):
         with pytest.raises(ValueError, match="GPU"):
             call_decode(decode_inputs(conv=conv))
+
+
+def test_linear_single_row_strided_view_raises():
+    """A one-row x whose last dim is not unit-stride is refused (the kernel
+    reads K contiguous elements per row)."""
+    x = torch.zeros(1, 2 * 64, dtype=BF)[:, ::2]
+    w = torch.zeros(32, 64, dtype=BF)
+    with pytest.raises(ValueError, match="unit-stride"):
+        ssd.ssd_linear(x, w)
+
+
+def test_mimo_empty_batch_raises_cleanly():
+    """batch 0 reaches the ordinary checks (here: host tensors) instead of
+    indexing a missing row."""
+    H, G, P, N, R = 4, 2, 64, 128, 2
+    with pytest.raises(ValueError):
+        ssd.ssd_decode_step_mimo(torch.zeros(0, H, P, R, dtype=BF), torch.zeros(0, G, N, R, dtype=BF),
+                                 torch.zeros(0, G, N, R, dtype=BF), torch.zeros(0, H, dtype=BF), torch.zeros(H),
+                                 torch.zeros(0, H, P, N))
