@@ -45,6 +45,30 @@ constexpr int kT = 256;     // threads per workgroup
 constexpr int kP = kHeadDim, kN = kDState;
 constexpr int kPN = kP * kN;
 
+// Inclusive prefix (suffix) sums over the 32 lanes of a half-wave: DPP row
+// shifts within each 16-lane row (a source outside the row reads 0), then the
+// upper (lower) row adds the other row's total.  Lanes 32..63 get no
+// meaningful value.
+template <int kCtrl> __device__ __forceinline__ float dpp_shift(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float prefix32(float v) {
+  v += dpp_shift<0x111>(v);  // row_shr:1
+  v += dpp_shift<0x112>(v);  // row_shr:2
+  v += dpp_shift<0x114>(v);  // row_shr:4
+  v += dpp_shift<0x118>(v);  // row_shr:8
+  const float row0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 15));
+  return (threadIdx.x & 16) ? v + row0 : v;
+}
+__device__ __forceinline__ float suffix32(float v) {
+  v += dpp_shift<0x101>(v);  // row_shl:1
+  v += dpp_shift<0x102>(v);  // row_shl:2
+  v += dpp_shift<0x104>(v);  // row_shl:4
+  v += dpp_shift<0x108>(v);  // row_shl:8
+  const float row1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  return (threadIdx.x & 16) ? v : v + row1;
+}
+
 template <typename T> __device__ __forceinline__ float ld(const void *base, int64_t i) {
   return to_f32<T>(reinterpret_cast<const T *>(base)[i]);
 }
@@ -61,12 +85,8 @@ __device__ __forceinline__ void chunk_dt(const BwdParams &p, int b, int h, int t
       z = ld<T>(p.dt, ((int64_t)b * p.L + t0 + lane) * p.H + h) + (p.dt_bias ? p.dt_bias[h] : 0.f);
       d = softplus_f32(z);
     }
-    float incl = d * p.A[h];
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float t = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += t;
-    }
+    static_assert(kQ == 32, "one half-wave scans the chunk");
+    const float incl = prefix32(d * p.A[h]);
     if (lane < kQ) {
       s_dt[lane] = d;
       s_cs[lane] = incl;
@@ -370,11 +390,8 @@ __global__ __launch_bounds__(kTC) void bwd_chunks_kernel(BwdParams p) {
         float ve = s0c[r] * s.DY[xi(j, 16 * qb + l16)], vx = 0.f;
 #pragma unroll
         for (int t = 0; t < 2; ++t) vx = fmaf(xg[t][r], s.B[bi(j, 16 * (nb0 + t) + l16)], vx);
-#pragma unroll
-        for (int off = 8; off >= 1; off >>= 1) {
-          ve += __shfl_xor(ve, off, 16);
-          vx += __shfl_xor(vx, off, 16);
-        }
+        ve = row_sum16(ve);
+        vx = row_sum16(vx);
         if (l16 == 0) {
           s.ey_part[qb][j] = ve;
           s.xgb_part[qb][j] = vx;
@@ -392,9 +409,7 @@ __global__ __launch_bounds__(kTC) void bwd_chunks_kernel(BwdParams p) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) acc4[k] = fmaf(gv[k], sv[k], acc4[k]);
       }
-      float gs = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) gs += __shfl_xor(gs, off, 64);
+      const float gs = wave_sum((acc4[0] + acc4[1]) + (acc4[2] + acc4[3]));
       if (lane == 0) s.red[wave] = gs;
     }
     __syncthreads();
@@ -442,20 +457,11 @@ __global__ __launch_bounds__(kTC) void bwd_chunks_kernel(BwdParams p) {
         tot_part = fj * dtj * xgb;
       }
       // the last token also carries e^{cs_Q} <G1, S0> + sum_j f_j dt_j x_j.(G1 B_j)
-      float tot = tot_part;
-#pragma unroll
-      for (int off = 16; off >= 1; off >>= 1) tot += __shfl_xor(tot, off, 32);
+      const float tot = half_wave_sum(tot_part);
       if (lane == kQ - 1) dcs += fmaf(eQ, G1S0, tot);
       // suffix sums over the chunk's tokens: suf_j = sum_{k>=j} dcs_k
-      float suf = lane < 32 ? dcs : 0.f;
-#pragma unroll
-      for (int off = 1; off < 32; off <<= 1) {
-        const float v = __shfl_down(suf, off, 32);
-        if ((lane & 31) + off < 32) suf += v;
-      }
-      float da = lane < 32 ? dtj * suf : 0.f;
-#pragma unroll
-      for (int off = 16; off >= 1; off >>= 1) da += __shfl_xor(da, off, 32);
+      const float suf = suffix32(lane < 32 ? dcs : 0.f);
+      const float da = half_wave_sum(lane < 32 ? dtj * suf : 0.f);
       accA += da;  // lanes 0..31 hold the chunk's sum
       if (lane < 32) {
         const float ddt = fmaf(Ah, suf, dexp);
@@ -464,13 +470,8 @@ __global__ __launch_bounds__(kTC) void bwd_chunks_kernel(BwdParams p) {
           dz = ddt * __builtin_amdgcn_rcpf(1.f + __expf(-s.z[j]));
           reinterpret_cast<T *>(p.ddt)[((int64_t)b * p.L + t0 + j) * p.H + h] = from_f32<T>(dz);
         }
-#pragma unroll
-        for (int off = 16; off >= 1; off >>= 1) dz += __shfl_xor(dz, off, 32);
-        accBias += dz;
-        float dd = s.DYX[qi(j, j)];
-#pragma unroll
-        for (int off = 16; off >= 1; off >>= 1) dd += __shfl_xor(dd, off, 32);
-        accD += dd;
+        accBias += half_wave_sum(dz);
+        accD += half_wave_sum(s.DYX[qi(j, j)]);
       }
     }
 

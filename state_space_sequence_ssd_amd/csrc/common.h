@@ -48,6 +48,66 @@ __device__ __forceinline__ float silu_f32(float u) {
   return u * __builtin_amdgcn_rcpf(1.f + __expf(-u));
 }
 
+// The value held by the lane paired with this one across lane bit BIT of a
+// 16-lane row, by a DPP move (a VALU operand modifier, no LDS round trip):
+// the row mirror pairs across bit 3, the half-row mirror across bit 2 (lane
+// i with 7 - i), the quad permutations across bits 1 and 0.  Each pairing
+// keeps the lower bits' partition: lanes paired at one step held the same
+// column set after the steps over the higher bits.
+template <int BIT> __device__ __forceinline__ float row_pair(float v) {
+  constexpr int ctrl = BIT == 3 ? 0x140 : BIT == 2 ? 0x141 : BIT == 1 ? 0x4E : 0xB1;
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, 0xF, 0xF, false));
+}
+
+// Reduce-scatter of CNT sums over the 32 lanes of a half-wave: steps over
+// lane bits 3, 2, 1, 0 (DPP) split the column set in halves while CNT > 1 and
+// add whole sums after; a last step over bit 4 crosses the two rows.  Lane
+// bit b's step leaves the upper lane of each pair with the upper half, so the
+// column a lane ends with is read off the bits it split on (rsel).
+template <int CNT, int BIT> struct RowScatter {
+  static __device__ __forceinline__ void run(float *part, int lane32, int &rsel) {
+    const bool upper = (lane32 >> BIT) & 1;
+    if constexpr (CNT > 1) {
+      constexpr int half = CNT / 2;
+#pragma unroll
+      for (int j = 0; j < half; ++j) {
+        const float send = upper ? part[j] : part[j + half];
+        const float keep = upper ? part[j + half] : part[j];
+        part[j] = keep + row_pair<BIT>(send);
+      }
+      rsel += upper ? half : 0;
+      RowScatter<half, BIT - 1>::run(part, lane32, rsel);
+    } else {
+      part[0] += row_pair<BIT>(part[0]);
+      RowScatter<1, BIT - 1>::run(part, lane32, rsel);
+    }
+  }
+};
+template <int CNT> struct RowScatter<CNT, -1> {
+  static_assert(CNT == 1, "at most 16 sums per row");
+  static __device__ __forceinline__ void run(float *part, int, int &) { part[0] += __shfl_xor(part[0], 16, 32); }
+};
+// lanes holding a finished sum with every all-reduced bit zero: one writer per column
+template <int R> constexpr int kRowWriterMask = 0x10 | ((16 / R) - 1);
+
+// Sum over the 16 lanes of a row (every lane gets it), by DPP moves.
+__device__ __forceinline__ float row_sum16(float v) {
+  v += row_pair<3>(v);
+  v += row_pair<2>(v);
+  v += row_pair<1>(v);
+  return v + row_pair<0>(v);
+}
+// ... over the 32 lanes of a half-wave (the last step crosses the two rows).
+__device__ __forceinline__ float half_wave_sum(float v) {
+  v = row_sum16(v);
+  return v + __shfl_xor(v, 16, 32);
+}
+// ... over the whole wave.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = half_wave_sum(v);
+  return v + __shfl_xor(v, 32, 64);
+}
+
 template <typename T> __device__ __forceinline__ float to_f32(T v);
 template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
 template <> __device__ __forceinline__ float to_f32<bf16_t>(bf16_t v) { return bf16_to_f32(v); }

@@ -126,28 +126,11 @@ __global__ __launch_bounds__(threads_for<R>()) void decode_mimo_kernel(MimoParam
           part[r] = n[0] * Cv[0][r] + n[1] * Cv[1][r] + n[2] * Cv[2][r] + n[3] * Cv[3][r];
         // the row's R sums over the 32 lanes as a reduce-scatter: each halving
         // step sends the half of the values this lane does not keep, so R = 8
-        // takes 4 + 2 + 1 + 1 + 1 shuffles instead of 5 R; afterwards every
-        // lane holds the sum of output column rsel
+        // takes 4 + 2 + 1 + 1 + 1 lane exchanges instead of 5 R; afterwards
+        // every lane holds the sum of output column rsel
         int rsel = 0;
-#pragma unroll
-        for (int off = 16, cnt = R; off >= 1; off >>= 1) {
-          if (cnt > 1) {
-            const int half = cnt / 2;
-            const bool upper = (lane32 & off) != 0;
-#pragma unroll
-            for (int j = 0; j < half; ++j) {
-              const float send = upper ? part[j] : part[j + half];
-              const float keep = upper ? part[j + half] : part[j];
-              part[j] = keep + __shfl_xor(send, off, 32);
-            }
-            rsel += upper ? half : 0;
-            cnt = half;
-          } else {
-            part[0] += __shfl_xor(part[0], off, 32);
-          }
-        }
-        // lanes of one 32 / R block hold the same sum: its first lane writes it
-        if ((lane32 & (32 / R - 1)) == 0)
+        RowScatter<R, 3>::run(part, lane32, rsel);
+        if ((lane32 & kRowWriterMask<R>) == 0)
           sy[(hl * kHeadDim + prow) * R + rsel] = fmaf(dskip, xr[rsel], part[0]);
       }
     }
@@ -175,6 +158,7 @@ typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, a), __builtin_bit_cast(bf16x2v, b), c, false);
 }
+
 
 constexpr int kMimoThreads16 = 256;
 template <int R, bool kTrap>
@@ -279,28 +263,11 @@ __global__ __launch_bounds__(kMimoThreads16) void decode_mimo_bf16_kernel(MimoPa
 #pragma unroll
         for (int r = 0; r < R; ++r)
           part[r] = n[0] * Cv[0][r] + n[1] * Cv[1][r] + n[2] * Cv[2][r] + n[3] * Cv[3][r];
-        // the row's R sums over the 32 lanes as a reduce-scatter (as in the
-        // kernel above); afterwards every lane holds the sum of column rsel
+        // the row's R sums over the 32 lanes as a reduce-scatter; afterwards
+        // every lane holds the sum of column rsel
         int rsel = 0;
-#pragma unroll
-        for (int off = 16, cnt = R; off >= 1; off >>= 1) {
-          if (cnt > 1) {
-            const int half = cnt / 2;
-            const bool upper = (lane32 & off) != 0;
-#pragma unroll
-            for (int j = 0; j < half; ++j) {
-              const float send = upper ? part[j] : part[j + half];
-              const float keep = upper ? part[j + half] : part[j];
-              part[j] = keep + __shfl_xor(send, off, 32);
-            }
-            rsel += upper ? half : 0;
-            cnt = half;
-          } else {
-            part[0] += __shfl_xor(part[0], off, 32);
-          }
-        }
-        // lanes of one 32 / R block hold the same sum: its first lane writes it
-        if ((lane32 & (32 / R - 1)) == 0) {
+        RowScatter<R, 3>::run(part, lane32, rsel);
+        if ((lane32 & kRowWriterMask<R>) == 0) {
           const uint32_t xw = xr[rsel >> 1];
           const float xv = (rsel & 1) ? hi_bf16(xw) : lo_bf16(xw);
           yb[(hl * kHeadDim + prow) * R + rsel] = f32_to_bf16(fmaf(dskip, xv, part[0]));

@@ -16,8 +16,9 @@
 // Then each wave takes one head and streams its 32 KiB of state in four
 // pieces of 8 KiB; every load instruction covers two whole state rows, so
 // the workgroup walks all of its heads' states at once.  A state row (128
-// floats) is 32 lanes x float4, so y[p] is a 32-lane butterfly sum; y is
-// staged in LDS and written once per group.
+// floats) is 32 lanes x float4, so y[p] is a 32-lane sum (DPP moves within
+// each 16-lane row, one exchange across the two); y is staged in LDS and
+// written once per group.
 #include "common.h"
 #include "kernels.h"
 
@@ -116,12 +117,7 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(DecodeParams p) {
         n[2] = fmaf(a, v[i][2], dx * Bv.z);
         n[3] = fmaf(a, v[i][3], dx * Bv.w);
         __builtin_nontemporal_store(n, S + (c * 8 + i) * 64 + lane);
-        float part = n[0] * Cv.x + n[1] * Cv.y + n[2] * Cv.z + n[3] * Cv.w;
-        part += __shfl_xor(part, 16, 32);
-        part += __shfl_xor(part, 8, 32);
-        part += __shfl_xor(part, 4, 32);
-        part += __shfl_xor(part, 2, 32);
-        part += __shfl_xor(part, 1, 32);
+        const float part = half_wave_sum(n[0] * Cv.x + n[1] * Cv.y + n[2] * Cv.z + n[3] * Cv.w);
         if (lane32 == 0) s_y[hl * kHeadDim + prow] = part + dskip * xp;
       }
     }

@@ -25,12 +25,6 @@ namespace {
 
 constexpr int kNormThreads = 256;  // four (token, group) units per workgroup
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
-
 template <typename T> struct Vec;
 template <> struct Vec<bf16_t> {
   static constexpr int N = 8;
