@@ -33,6 +33,8 @@
 //   3. bwd_reduce_kernel: dB, dC summed over the heads of each group and
 //      dA, dD, ddt_bias over the rows, in a fixed order (no float atomics,
 //      repeat runs are bitwise identical).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -241,6 +243,95 @@ __global__ __launch_bounds__(kT) void bwd_states_kernel(BwdParams p) {
       const float a = sX[(k0 + kq) * kXSP + 16 * wave + l16];  // (w x)^T: row p, k = token
 #pragma unroll
       for (int t = 0; t < 8; ++t) acc[t] = mfma16(a, sB[(k0 + kq) * kBSP + 16 * t + l16], acc[t]);
+    }
+    __syncthreads();  // the tiles are rewritten by the next chunk
+  }
+}
+
+// bf16 inputs: the same recurrence on the bf16 matrix cores
+// (v_mfma_f32_16x16x32_bf16: the chunk's 32 tokens are one k-step).  B is
+// exact in bf16; w_j x_j is split into bf16 parts hi = bf16(v) and lo =
+// bf16(v - hi), so the two products carry w x to about 2^-16 of its size,
+// far below the rounding of the bf16 inputs themselves.  The tiles stay
+// token-major in LDS (rows padded by 32 bytes) and the operands, whose K runs
+// over tokens, come from the LDS transpose read: in each 16-lane group (k slot
+// kq: tokens 8 kq .. 8 kq + 7) lane s points at token row k0 + s / 4, columns
+// c0 + 4 (s % 4) .. + 3, and receives tokens k0 .. k0 + 3 of column c0 + s.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+constexpr int kXR = 2 * kP + 32, kBR = 2 * kN + 32;  // bytes per staged row
+__device__ __forceinline__ bf16x8 tr_frag(const uint8_t *tile, int pitch, int k0, int c0, int lane) {
+  const int s = lane & 15;
+  const uint8_t *a = tile + (k0 + (s >> 2)) * pitch + 2 * (c0 + 4 * (s & 3));
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)a);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(a + 4 * pitch));
+  const u32x2 l = __builtin_bit_cast(u32x2, lo), h = __builtin_bit_cast(u32x2, hi);
+  return __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], h[0], h[1]});
+}
+__global__ __launch_bounds__(kT) void bwd_states_bf16_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t sXh[kQ * kXR], sXl[kQ * kXR], sB[kQ * kBR];
+  __shared__ float s_dt[kQ], s_cs[kQ], s_z[kQ];
+  const int b = blockIdx.x / p.H, h = blockIdx.x % p.H, g = h / (p.H / p.G);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, kq = lane >> 4;
+  float *states = p.ws_states + ((int64_t)b * p.H + h) * p.nchunks * kPN;
+  // this wave's tiles: rows p in [16 wave, +16), columns n in [16 t, +16), t = 0..7
+  f32x4 acc[8];
+  const float *h0 = p.init ? p.init + ((int64_t)b * p.H + h) * kPN : nullptr;
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[t][r] = h0 ? h0[(16 * wave + 4 * kq + r) * kN + 16 * t + l16] : 0.f;
+  ChunkRows<bf16_t, kN> rb;
+  ChunkRows<bf16_t, kP> rx;
+  const auto load_chunk = [&](int c) {
+    const int t0 = c * kQ, nv = min(kQ, p.L - t0);
+    rb.load(p.B, (((int64_t)b * p.L + t0) * p.G + g) * kN, (int64_t)p.G * kN, nv, tid);
+    rx.load(p.x, (((int64_t)b * p.L + t0) * p.H + h) * kP, (int64_t)p.H * kP, nv, tid);
+  };
+  if (p.nchunks > 0) load_chunk(0);
+  for (int c = 0; c < p.nchunks; ++c) {
+    const int t0 = c * kQ, nv = min(kQ, p.L - t0);
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) states[(int64_t)c * kPN + (16 * wave + 4 * kq + r) * kN + 16 * t + l16] = acc[t][r];
+    chunk_dt<bf16_t>(p, b, h, t0, nv, s_dt, s_cs, s_z);
+#pragma unroll
+    for (int i = 0; i < rb.kPieces; ++i) {
+      const int pc = tid + kT * i, e = pc * 8, j = e / kN, q = e % kN;
+      if (pc < rb.kTotal) *reinterpret_cast<u32x4 *>(sB + j * kBR + 2 * q) = rb.v[i];
+    }
+    __syncthreads();  // dt, cs
+    const float last = s_cs[kQ - 1];
+#pragma unroll
+    for (int i = 0; i < rx.kPieces; ++i) {
+      const int pc = tid + kT * i, e = pc * 8, j = e / kP, q = e % kP;
+      if (pc < rx.kTotal) {
+        const float w = __expf(last - s_cs[j]) * s_dt[j];
+        u32x4 hv, lv;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float v0 = lo_bf16(rx.v[i][k]) * w, v1 = hi_bf16(rx.v[i][k]) * w;
+          hv[k] = pack2_bf16(v0, v1);
+          lv[k] = pack2_bf16(v0 - lo_bf16(hv[k]), v1 - hi_bf16(hv[k]));
+        }
+        *reinterpret_cast<u32x4 *>(sXh + j * kXR + 2 * q) = hv;
+        *reinterpret_cast<u32x4 *>(sXl + j * kXR + 2 * q) = lv;
+      }
+    }
+    __syncthreads();
+    if (c + 1 < p.nchunks) load_chunk(c + 1);
+    const float dec = __expf(last);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[t] *= dec;
+    // A = (w x)^T (rows p, K = tokens), B = B (K = tokens, columns n)
+    const bf16x8 ah = tr_frag(sXh, kXR, 8 * kq, 16 * wave, lane);
+    const bf16x8 al = tr_frag(sXl, kXR, 8 * kq, 16 * wave, lane);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const bf16x8 bt = tr_frag(sB, kBR, 8 * kq, 16 * t, lane);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bt, acc[t], 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bt, acc[t], 0, 0, 0);
     }
     __syncthreads();  // the tiles are rewritten by the next chunk
   }
@@ -610,7 +701,10 @@ __global__ __launch_bounds__(kT) void bwd_reduce_kernel(BwdParams p) {
 template <typename T>
 hipError_t launch_t(const BwdParams &p, hipStream_t stream) {
   const unsigned units = (unsigned)(p.batch * p.H);
-  hipLaunchKernelGGL(bwd_states_kernel<T>, dim3(units), dim3(kT), 0, stream, p);
+  if constexpr (std::is_same<T, bf16_t>::value)
+    hipLaunchKernelGGL(bwd_states_bf16_kernel, dim3(units), dim3(kT), 0, stream, p);
+  else
+    hipLaunchKernelGGL(bwd_states_kernel<T>, dim3(units), dim3(kT), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t lds = sizeof(BwdSmem);
