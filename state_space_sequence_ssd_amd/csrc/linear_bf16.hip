@@ -131,20 +131,29 @@ __global__ __launch_bounds__(64 * kWM * kWN) void linear_bf16_kernel(LinearParam
     if (kt + 1 < nk) issue(buf ^ 1, (kt + 1) * kBK);
     const lds_u8 *Wt = (const lds_u8 *)lin_smem + kWOff + buf * BN * 128;
     const lds_u8 *Xt = (const lds_u8 *)lin_smem + kXOff + buf * BM * 128;
-#pragma unroll
-    for (int s = 0; s < kBK / 16; ++s) {
-      // operand fragment: row l32 of the 32-row block, K values 16 s + 8 hk .. + 7
-      bf16x8 fw[kTN], fx[kTM];
+    // operand fragments: row l32 of the 32-row block, K values 16 s + 8 hk .. + 7.
+    // Double-buffered: sub-step s + 1's reads go out before sub-step s's
+    // products, so the matrix core never waits for the LDS latency of the
+    // step it is about to run (only the first sub-step after the barrier does).
+    bf16x8 fw[2][kTN], fx[2][kTM];
+    auto read_frags = [&](int s, int slot) {
 #pragma unroll
       for (int a = 0; a < kTN; ++a)
-        fw[a] = *reinterpret_cast<const SSD_LDS bf16x8 *>(Wt + blk_off(wn + 32 * a + l32, 2 * s + hk));
+        fw[slot][a] = *reinterpret_cast<const SSD_LDS bf16x8 *>(Wt + blk_off(wn + 32 * a + l32, 2 * s + hk));
 #pragma unroll
       for (int b = 0; b < kTM; ++b)
-        fx[b] = *reinterpret_cast<const SSD_LDS bf16x8 *>(Xt + blk_off(wm + 32 * b + l32, 2 * s + hk));
+        fx[slot][b] = *reinterpret_cast<const SSD_LDS bf16x8 *>(Xt + blk_off(wm + 32 * b + l32, 2 * s + hk));
+    };
+    read_frags(0, 0);
+#pragma unroll
+    for (int s = 0; s < kBK / 16; ++s) {
+      if (s + 1 < kBK / 16) read_frags(s + 1, (s + 1) & 1);
+      // keeps the next sub-step's reads ahead of this one's products
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int a = 0; a < kTN; ++a)
 #pragma unroll
-        for (int b = 0; b < kTM; ++b) acc[a][b] = mfma32(fw[a], fx[b], acc[a][b]);
+        for (int b = 0; b < kTM; ++b) acc[a][b] = mfma32(fw[s & 1][a], fx[s & 1][b], acc[a][b]);
     }
     __builtin_amdgcn_s_waitcnt(0);  // the next K step has landed (this wave's loads)
     __syncthreads();                // ... every wave's, and this one's reads are done
