@@ -82,6 +82,26 @@ __device__ __forceinline__ float load_dt(const ScanParams &p, int row, int h) {
   return dtg[(int64_t)min((int)threadIdx.x, p.L - 1) * p.dt_st];
 }
 
+// A DPP move of a double (both 32-bit halves with the same control): lanes
+// outside the pattern's rows, or reading outside their row with kBound, get 0.
+template <int kCtrl, int kRowMask, bool kBound> __device__ __forceinline__ double dpp_f64(double v) {
+  const unsigned long long u = __double_as_longlong(v);
+  const unsigned lo = __builtin_amdgcn_update_dpp(0, (int)(unsigned)u, kCtrl, kRowMask, 0xF, kBound);
+  const unsigned hi = __builtin_amdgcn_update_dpp(0, (int)(unsigned)(u >> 32), kCtrl, kRowMask, 0xF, kBound);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+// Inclusive prefix sum over the 64 lanes of a wave: row shifts within each
+// 16-lane row, then the row totals carried by row broadcasts (no LDS traffic).
+__device__ __forceinline__ double wave_incl_scan_f64(double x) {
+  x += dpp_f64<0x111, 0xF, true>(x);   // row_shr:1
+  x += dpp_f64<0x112, 0xF, true>(x);   // row_shr:2
+  x += dpp_f64<0x114, 0xF, true>(x);   // row_shr:4
+  x += dpp_f64<0x118, 0xF, true>(x);   // row_shr:8
+  x += dpp_f64<0x142, 0xA, false>(x);  // row_bcast:15 -> rows 1, 3
+  x += dpp_f64<0x143, 0xC, false>(x);  // row_bcast:31 -> rows 2, 3
+  return x;
+}
+
 // dt and the fp64 inclusive cumsum of dt A over the whole sequence (one token per thread)
 __device__ void row_cumsum(const ScanParams &p, int h, float raw_dt, QuadSmem &s) {
   const int tid = threadIdx.x;
@@ -90,12 +110,7 @@ __device__ void row_cumsum(const ScanParams &p, int h, float raw_dt, QuadSmem &s
   if (tid < kQuadMaxL) s.dt[tid] = d;
   const double v = (double)(d * p.A[h]);
   const int lane = tid & 63, w = tid >> 6;
-  double incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const double u = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += u;
-  }
+  const double incl = wave_incl_scan_f64(v);
   __shared__ double wsum[kWaves];
   if (lane == 63) wsum[w] = incl;
   __syncthreads();
