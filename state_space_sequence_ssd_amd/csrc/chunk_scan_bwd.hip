@@ -101,6 +101,59 @@ __device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// bf16 inputs on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16): lane
+// (l16, kq) holds K values 8 kq .. 8 kq + 7 of its operand row / column, and
+// the accumulator layout is that of v_mfma_f32_16x16x4_f32 (rows 4 kq .. +3,
+// column l16).  Operands that are bf16 numbers (x, dy, B, C) convert exactly;
+// fp32 intermediates (the adjoint, the entering state, the masked token
+// products) go in as bf16 parts hi = bf16(v), lo = bf16(v - hi), two
+// products, so each carries about 16 bits.
+struct F8 {
+  float v[8];
+};
+__device__ __forceinline__ F8 ld8(const float *p) {  // 8 consecutive floats (16-byte aligned)
+  const f32x4 a = *reinterpret_cast<const f32x4 *>(p), b = *reinterpret_cast<const f32x4 *>(p + 4);
+  return F8{{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]}};
+}
+template <int kStride> __device__ __forceinline__ F8 ld8s(const float *p) {  // 8 floats kStride apart
+  F8 f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.v[e] = p[e * kStride];
+  return f;
+}
+__device__ __forceinline__ bf16x8 exact8(const F8 &f) {
+  u32x4 o;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) o[k] = pack2_bf16(f.v[2 * k], f.v[2 * k + 1]);
+  return __builtin_bit_cast(bf16x8, o);
+}
+struct Split8 {
+  bf16x8 hi, lo;
+};
+__device__ __forceinline__ Split8 split8(const F8 &f) {
+  u32x4 h, l;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    h[k] = pack2_bf16(f.v[2 * k], f.v[2 * k + 1]);
+    l[k] = pack2_bf16(f.v[2 * k] - lo_bf16(h[k]), f.v[2 * k + 1] - hi_bf16(h[k]));
+  }
+  return Split8{__builtin_bit_cast(bf16x8, h), __builtin_bit_cast(bf16x8, l)};
+}
+__device__ __forceinline__ f32x4 mfma32k(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// exact operand times split operand (lo part first), either side
+__device__ __forceinline__ f32x4 mfma_es(bf16x8 a, const Split8 &b, f32x4 c) {
+  return mfma32k(a, b.hi, mfma32k(a, b.lo, c));
+}
+__device__ __forceinline__ f32x4 mfma_se(const Split8 &a, bf16x8 b, f32x4 c) {
+  return mfma32k(a.hi, b, mfma32k(a.lo, b, c));
+}
+// split times split: hi hi + hi lo + lo hi (the lo lo term is below 2^-16)
+__device__ __forceinline__ f32x4 mfma_ss(const Split8 &a, const Split8 &b, f32x4 c) {
+  return mfma32k(a.hi, b.hi, mfma32k(a.hi, b.lo, mfma32k(a.lo, b.hi, c)));
+}
+
 // Chunk operands move as 16-byte pieces: every thread issues all of its loads
 // of a chunk before the first one is used, so a chunk waits for one memory
 // latency, not one per element.
@@ -373,6 +426,7 @@ struct BwdSmem {
 
 template <typename T>
 __global__ __launch_bounds__(kTC) void bwd_chunks_kernel(BwdParams p) {
+  constexpr bool kBf = std::is_same<T, bf16_t>::value;  // bf16 inputs: the bf16 matrix cores
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   BwdSmem &s = *reinterpret_cast<BwdSmem *>(smem_raw);
   const int b = blockIdx.x / p.H, h = blockIdx.x % p.H, g = h / (p.H / p.G);
@@ -432,6 +486,25 @@ __global__ __launch_bounds__(kTC) void bwd_chunks_kernel(BwdParams p) {
     {
       f32x4 tt = f32x4{};  // the token x token block
       gb = s0c = xg[0] = xg[1] = f32x4{};
+      if constexpr (kBf) {
+        // over n: 4 k-steps of 32 (rows of every tile, 8 consecutive n per lane)
+#pragma unroll
+        for (int st = 0; st < kN / 32; ++st) {
+          const int n0 = 32 * st + 8 * kq;
+          if (has_cb) tt = mfma32k(exact8(ld8(&s.C[bi(16 * mi + l16, n0)])), exact8(ld8(&s.B[bi(16 * ni + l16, n0)])), tt);
+          gb = mfma_es(exact8(ld8(&s.B[bi(jr, n0)])), split8(ld8(&s.G[gi(16 * qb + l16, n0)])), gb);
+          s0c = mfma_es(exact8(ld8(&s.C[bi(jr, n0)])), split8(ld8(&s.S0[gi(16 * qb + l16, n0)])), s0c);
+        }
+        // over p: 2 k-steps of 32; G1's columns are read down the p rows
+#pragma unroll
+        for (int st = 0; st < kP / 32; ++st) {
+          const int p0 = 32 * st + 8 * kq;
+          if (!has_cb) tt = mfma32k(exact8(ld8(&s.DY[xi(16 * mi + l16, p0)])), exact8(ld8(&s.X[xi(16 * ni + l16, p0)])), tt);
+          const bf16x8 xr = exact8(ld8(&s.X[xi(jr, p0)]));
+#pragma unroll
+          for (int t = 0; t < 2; ++t) xg[t] = mfma_es(xr, split8(ld8s<kNP>(&s.G[gi(p0, 16 * (nb0 + t) + l16)])), xg[t]);
+        }
+      } else {
       // contractions over n: C B^T (waves 0..3), B G1^T, C S0^T
       struct RN { float c_i, b_j, b_r, c_r, g, s0; };
       pipelined<kN / 4, RN>(
@@ -469,6 +542,7 @@ __global__ __launch_bounds__(kTC) void bwd_chunks_kernel(BwdParams p) {
 #pragma unroll
             for (int t = 0; t < 2; ++t) xg[t] = mfma16(o.x_r, o.g[t], xg[t]);
           });
+      }
       float *ttd = has_cb ? s.CB : s.DYX;
 #pragma unroll
       for (int r = 0; r < 4; ++r) ttd[qi(16 * mi + 4 * kq + r, 16 * ni + l16)] = tt[r];
@@ -580,6 +654,42 @@ __global__ __launch_bounds__(kTC) void bwd_chunks_kernel(BwdParams p) {
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) g0[t][r] = eQ * s.G[gi(16 * qb + 4 * kq + r, 16 * (gn0 + t) + l16)];
+      if constexpr (kBf) {
+        // over the chunk's 32 tokens: one k-step, tokens k0 .. k0 + 7 per lane
+        const int k0 = 8 * kq;
+        const F8 lm = ld8s<kQP>(&s.Lm[qi(k0, jr)]), cb = ld8s<kQP>(&s.CB[qi(k0, jr)]),
+                 dyx = ld8s<kQP>(&s.DYX[qi(k0, jr)]), dy = ld8s<kPP>(&s.DY[xi(k0, 16 * qb + l16)]);
+        const F8 lr = ld8(&s.Lm[qi(jr, k0)]), dr = ld8(&s.DYX[qi(jr, k0)]), dtk = ld8(&s.dt[k0]), ek = ld8(&s.ei[k0]);
+        F8 lcb, ldyx, ldt, edy;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          lcb.v[e] = lm.v[e] * cb.v[e];
+          ldyx.v[e] = lm.v[e] * dyx.v[e];
+          ldt.v[e] = lr.v[e] * dtk.v[e] * dr.v[e];
+          edy.v[e] = ek.v[e] * dy.v[e];
+        }
+        ax = mfma_se(split8(lcb), exact8(dy), ax);
+        const Split8 sdyx = split8(ldyx), sdt = split8(ldt), sedy = split8(edy);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          ab[t] = mfma_se(sdyx, exact8(ld8s<kNP>(&s.C[bi(k0, 16 * (nb0 + t) + l16)])), ab[t]);
+          ac[t] = mfma_se(sdt, exact8(ld8s<kNP>(&s.B[bi(k0, 16 * (nb0 + t) + l16)])), ac[t]);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) g0[t] = mfma_se(sedy, exact8(ld8s<kNP>(&s.C[bi(k0, 16 * (gn0 + t) + l16)])), g0[t]);
+        // ... and over p (2 k-steps): the e_j S0^T dy_j term of dC
+        const float ej = s.ei[jr];
+#pragma unroll
+        for (int st = 0; st < kP / 32; ++st) {
+          const int p0 = 32 * st + 8 * kq;
+          F8 a = ld8(&s.DY[xi(jr, p0)]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) a.v[e] *= ej;
+          const Split8 sa = split8(a);
+#pragma unroll
+          for (int t = 0; t < 2; ++t) ac[t] = mfma_ss(sa, split8(ld8s<kNP>(&s.S0[gi(p0, 16 * (nb0 + t) + l16)])), ac[t]);
+        }
+      } else {
       // contractions over the chunk's tokens (k); dy_k[16 qb + l16] is both the
       // B operand of dx and, times e_k, the A operand of G0
       struct RQ { float lcb, ldyx, ldt, ek, dy, cb[2], cg[4], bb[2]; };
@@ -629,6 +739,7 @@ __global__ __launch_bounds__(kTC) void bwd_chunks_kernel(BwdParams p) {
 #pragma unroll
             for (int t = 0; t < 2; ++t) ac[t] = mfma16(o.edy, o.s0[t], ac[t]);
           });
+      }
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
