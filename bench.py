@@ -865,9 +865,10 @@ def bwd_flops(w, Q=32):
 
 
 class BwdRun:
-    """The scan's backward pass at the headline shape (bf16 inputs, fp32
-    arithmetic): gradients of x, dt, B, C, the per-head parameters and the
-    initial state from dy and a final-state gradient."""
+    """The scan's backward pass at the headline shape (bf16 inputs; products
+    on the bf16 matrix cores with fp32 intermediates split into bf16 hi + lo
+    parts, fp32 sums): gradients of x, dt, B, C, the per-head parameters and
+    the initial state from dy and a final-state gradient."""
 
     def __init__(self, w):
         import torch
@@ -913,14 +914,23 @@ class BwdRun:
         flops = bwd_flops(w)
         tf = flops / (ms * 1e-3) / 1e12
         traffic = read_traffic_all(w.name) or {}
-        return {"avg_ms": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
-                "algorithmic_bytes": nbytes, "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
-                "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                "roofline": {"bound": "mfma", "dtype": "f32", "achieved": round(tf, 1), "peak": FP32_MFMA_PEAK_TFLOPS,
-                             "unit": "TFLOP/s", "frac": round(tf / FP32_MFMA_PEAK_TFLOPS, 4), "flops": flops},
-                "traffic_per_kernel": {k: v for k, v in traffic.items() if k.startswith("bwd")} or None,
-                "note": "launch-inclusive time of the three backward launches (chunk states, reverse chunks, "
-                        "fixed-order reductions); fp32 arithmetic on the fp32 matrix cores"}
+        bwd_traffic = {k: v for k, v in traffic.items() if k.startswith("bwd")} or None
+        out = {"avg_ms": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+               "algorithmic_bytes": nbytes, "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+               "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+               "roofline": {"bound": "mfma", "dtype": "bf16", "achieved": round(tf, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
+                            "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4), "flops": flops,
+                            "fp32_matrix_equivalent_frac": round(tf / FP32_MFMA_PEAK_TFLOPS, 4)},
+               "traffic_per_kernel": bwd_traffic,
+               "note": "launch-inclusive time of the three backward launches (chunk states, reverse chunks, "
+                       "fixed-order reductions); flops are those of the chunked form, each counted once, although "
+                       "a product with a split fp32 operand runs as two (or three) bf16 matrix-core products"}
+        if bwd_traffic:
+            moved = sum(bwd_traffic.values())
+            out["measured_traffic"] = {"bytes": moved, "gbs": round(moved / (ms * 1e-3) / 1e9, 1),
+                                       "hbm_frac": round(moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                       "note": "HBM bytes the three launches move, workspace included"}
+        return out
 
 
 def main():

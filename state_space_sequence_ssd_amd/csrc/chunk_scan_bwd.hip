@@ -1,5 +1,5 @@
-// Backward pass of the chunked SSD scan on gfx950 (batch rows, fp32
-// arithmetic).  The training workload of the layer needs the gradient of
+// Backward pass of the chunked SSD scan on gfx950 (batch rows, fp32 sums).
+// The training workload of the layer needs the gradient of
 // every input ("Nemotron-H style Hybrid Mamba-Transformer 3B feasibility
 // study", sec. 3.1, forward/backward verification; sec. 7, Phase 2).
 //
@@ -28,8 +28,10 @@
 //      state entering each chunk (fp32, in the workspace).
 //   2. bwd_chunks_kernel: one workgroup per (row, head) walks the chunks in
 //      reverse; the adjoint G, the entering state and every chunk operand
-//      live in LDS, and each product above is a tile loop of fp32 MFMAs.  dB
-//      and dC are written per head, the per-head scalars per (row, head).
+//      live in LDS (fp32), and each product above is a tile loop of matrix-
+//      core products: bf16 ones for bf16 inputs (fp32 intermediates split
+//      into bf16 hi + lo parts), fp32 ones for fp32 inputs.  dB and dC are
+//      written per head, the per-head scalars per (row, head).
 //   3. bwd_reduce_kernel: dB, dC summed over the heads of each group and
 //      dA, dD, ddt_bias over the rows, in a fixed order (no float atomics,
 //      repeat runs are bitwise identical).
