@@ -56,6 +56,11 @@ def _check(w, d, tol):
     (3, 1, 4, 1, False, True, True),
     (2, 64, 16, 4, True, True, True),
     (1, 257, 8, 8, True, False, True),
+    # bf16 inputs take the bf16 matrix-core products: one token, a ragged
+    # tail without initial state or final-state gradient, several chunks
+    (3, 1, 4, 1, True, True, True),
+    (1, 33, 4, 4, True, False, False),
+    (2, 100, 8, 2, True, True, True),
 ])
 def test_bwd_small(batch, L, H, G, bf16, init, dfinal):
     print(f"case bwd batch={batch} L={L} H={H} G={G} bf16={bf16} init={init} dfinal={dfinal}", flush=True)
@@ -68,6 +73,12 @@ def test_bwd_dt_zero_heads():
     zero and the rest of the gradients still match."""
     w, d = _case(2, 70, 8, 2, False, seed=5, dt_inf_heads=(1, 6))
     _check(w, d, 1e-4)
+
+
+def test_bwd_dt_zero_heads_bf16():
+    """The dt = 0 heads through the bf16 matrix-core products."""
+    w, d = _case(2, 70, 8, 2, True, seed=5, dt_inf_heads=(1, 6))
+    _check(w, d, 2e-2)
 
 
 def test_bwd_empty_sequence():
