@@ -182,6 +182,17 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
 
 
+def _empty(stream, *shape_args, **kw) -> torch.Tensor:
+    """torch.empty on the stream the call launches on (the current one when
+    none is given): the caching allocator then ties the block to that stream,
+    so a temporary freed when the call returns is not handed to another
+    stream while this one's kernels still use it."""
+    if stream is None:
+        return torch.empty(*shape_args, **kw)
+    with torch.cuda.stream(stream):
+        return torch.empty(*shape_args, **kw)
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -265,7 +276,7 @@ def ssd_conv1d_silu(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.
     _on_gpu(x, out=out, weight=weight, bias=bias, seq_idx=seq_idx, conv_state_in=conv_state_in,
             conv_state_out=conv_state_out)
     if out is None:
-        out = torch.empty((batch, L, CH), dtype=x.dtype, device=x.device)
+        out = _empty(stream, (batch, L, CH), dtype=x.dtype, device=x.device)
     a = SsdConvArgs()
     a.struct_size = ctypes.sizeof(SsdConvArgs)
     a.dtype = _dtype_code(x)
@@ -348,7 +359,7 @@ def ssd_chunk_scan_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: to
     """
     lib = load_library()
     if y is None:
-        y = torch.empty(x.shape, dtype=x.dtype, device=x.device)
+        y = _empty(stream, x.shape, dtype=x.dtype, device=x.device)
     a = _scan_args(x, dt, A, B, C, dt_bias, D, seq_idx, num_seqs, initial_state, final_state, y,
                    chunk_size, seg_chunks)
     if workspace is None:
@@ -357,7 +368,7 @@ def ssd_chunk_scan_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: to
         if need == ctypes.c_size_t(-1).value:
             raise SsdError(1, lib.ssd_last_error().decode())
         if need > 0:
-            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+            workspace = _empty(stream, need, dtype=torch.uint8, device=x.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.ssd_chunk_scan_fwd(ctypes.byref(a), _ptr(workspace), ws_bytes, _stream(stream)))
     return y
@@ -457,7 +468,7 @@ def ssd_conv_scan_fwd(xBC: torch.Tensor, conv_weight: torch.Tensor, dt: torch.Te
     conv runs inside the bf16 scan kernel).  Returns y (batch, L, nheads, headdim)."""
     lib = load_library()
     if y is None:
-        y = torch.empty((xBC.shape[0], xBC.shape[1], nheads, headdim), dtype=xBC.dtype, device=xBC.device)
+        y = _empty(stream, (xBC.shape[0], xBC.shape[1], nheads, headdim), dtype=xBC.dtype, device=xBC.device)
     a = _conv_scan_args(xBC, conv_weight, dt, A, nheads, ngroups, headdim, dstate, conv_bias, dt_bias, D,
                         seq_idx, num_seqs, conv_state_in, conv_state_out, initial_state, final_state, y,
                         chunk_size, seg_chunks)
@@ -466,7 +477,7 @@ def ssd_conv_scan_fwd(xBC: torch.Tensor, conv_weight: torch.Tensor, dt: torch.Te
         if need == ctypes.c_size_t(-1).value:
             raise SsdError(1, lib.ssd_last_error().decode())
         if need > 0:
-            workspace = torch.empty(need, dtype=torch.uint8, device=xBC.device)
+            workspace = _empty(stream, need, dtype=torch.uint8, device=xBC.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.ssd_conv_scan_fwd(ctypes.byref(a), _ptr(workspace), ws_bytes, _stream(stream)))
     return y
@@ -490,7 +501,7 @@ def ssd_linear(x: torch.Tensor, w: torch.Tensor, y: Optional[torch.Tensor] = Non
         raise ValueError("x's leading dims must be packed (a view, not a copy)")
     M = x2.shape[0]
     if y is None:
-        y = torch.empty((*x.shape[:-1], N), dtype=x.dtype, device=x.device)
+        y = _empty(stream, (*x.shape[:-1], N), dtype=x.dtype, device=x.device)
     _shape(y, "y", (*x.shape[:-1], N))
     y2 = y.reshape(-1, N) if y.dim() != 2 else y
     if y2.data_ptr() != y.data_ptr():
@@ -566,7 +577,7 @@ def ssd_gated_rmsnorm(y: torch.Tensor, weight: torch.Tensor, group_size: int,
             raise ValueError(f"out must match y's (batch, seqlen, channels) = {(batch, L, CH)}")
     _on_gpu(y, z=z, weight=weight, out=out)
     if out is None:
-        out = torch.empty(y.shape, dtype=y.dtype, device=y.device)
+        out = _empty(stream, y.shape, dtype=y.dtype, device=y.device)
         _, _, _, o_sb, o_st = _flat3(out, "out")
     a = SsdNormArgs()
     a.struct_size = ctypes.sizeof(SsdNormArgs)
@@ -619,7 +630,7 @@ def ssd_decode_step(xBC: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, ssm_st
     _on_gpu(xBC, dt=dt, A=A, ssm_state=ssm_state, dt_bias=dt_bias, D=D, conv_state=conv_state,
             conv_weight=conv_weight, conv_bias=conv_bias, y=y)
     if y is None:
-        y = torch.empty((batch, nheads, headdim), dtype=xBC.dtype, device=xBC.device)
+        y = _empty(stream, (batch, nheads, headdim), dtype=xBC.dtype, device=xBC.device)
     if y.stride(2) != 1 or y.stride(1) != headdim:
         raise ValueError("y must have packed (H, P) rows")
     a = SsdDecodeArgs()
@@ -682,7 +693,7 @@ def ssd_decode_step_mimo(x: torch.Tensor, B: torch.Tensor, C: torch.Tensor, dt: 
     _on_gpu(x, B=B, C=C, dt=dt, lam=lam, A=A, ssm_state=ssm_state, dt_bias=dt_bias, D=D,
             prev_x=prev_x, prev_B=prev_B, y=y)
     if y is None:
-        y = torch.empty((batch, H, P, R), dtype=x.dtype, device=x.device)
+        y = _empty(stream, (batch, H, P, R), dtype=x.dtype, device=x.device)
     a = SsdMimoDecodeArgs()
     a.struct_size = ctypes.sizeof(SsdMimoDecodeArgs)
     a.dtype = _dtype_code(x)
@@ -733,10 +744,12 @@ def ssd_chunk_scan_bwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: to
     _on_gpu(x, dt=dt, A=A, B=B, C=C, dy=dy, dt_bias=dt_bias, D=D, initial_state=initial_state,
             d_final_state=d_final_state, workspace=workspace)
     dev = x.device
-    out = {"dx": torch.empty_like(x), "ddt": torch.empty_like(dt), "dB": torch.empty_like(B),
-           "dC": torch.empty_like(C), "d_dt_bias": torch.empty(H, device=dev),
-           "dA": torch.empty(H, device=dev), "dD": torch.empty(H, device=dev),
-           "d_initial_state": torch.empty((batch, H, P, N), device=dev) if want_d_initial_state else None}
+    out = {"dx": _empty(stream, x.shape, dtype=x.dtype, device=dev),
+           "ddt": _empty(stream, dt.shape, dtype=dt.dtype, device=dev),
+           "dB": _empty(stream, B.shape, dtype=B.dtype, device=dev),
+           "dC": _empty(stream, C.shape, dtype=C.dtype, device=dev), "d_dt_bias": _empty(stream, H, device=dev),
+           "dA": _empty(stream, H, device=dev), "dD": _empty(stream, H, device=dev),
+           "d_initial_state": _empty(stream, (batch, H, P, N), device=dev) if want_d_initial_state else None}
     a = SsdScanBwdArgs()
     a.struct_size = ctypes.sizeof(SsdScanBwdArgs)
     a.dtype = _dtype_code(x)
@@ -751,7 +764,7 @@ def ssd_chunk_scan_bwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: to
     if need == ctypes.c_size_t(-1).value:
         raise SsdError(1, lib.ssd_last_error().decode())
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        workspace = _empty(stream, max(need, 1), dtype=torch.uint8, device=dev)
     if workspace.dtype != torch.uint8 or workspace.numel() < need:
         raise ValueError(f"workspace must be a uint8 tensor of at least {need} bytes")
     _check(lib.ssd_chunk_scan_bwd(ctypes.byref(a), _ptr(workspace), workspace.numel(), _stream(stream)))

@@ -200,3 +200,40 @@ def test_full_packed_3b_conv_fused():
         print(f"  sequence {s} ({lens[s]} tokens): y rel err {ey:.3e}  final-state {ef:.3e}", flush=True)
         assert ey <= TOL[True] and ef <= TOL[True]
         assert np.array_equal(so[[s]], rso)
+
+
+def test_rows_on_separate_streams_match_one_batch_call():
+    """Per-row calls on four streams, each leaving its workspace to the
+    binding: the same y and final states as one batch call.  The binding
+    allocates on the stream it launches on, so the workspace freed when one
+    call returns is not handed to another stream's call while its kernels
+    still run.  One segment per row in both runs (seg_chunks = the whole row),
+    so the arithmetic is the same."""
+    batch, L, H, G = 4, 2048, 32, 4
+    w = W("streams", batch, L, H, G)
+    d = make(w, seed=21, conv_bias=False, state_in=False)
+    xbc = to_dev(d["xBC"], BF)
+    cw, dt = to_dev(d["conv_w"]), to_dev(d["dt"], BF)
+    A, D, dtb = to_dev(d["A"]), to_dev(d["D"]), to_dev(d["dt_bias"])
+    seg = L // 128
+    fs1 = torch.empty((batch, H, 64, 128), device=DEV)
+    y1 = ssd.ssd_conv_scan_fwd(xbc, cw, dt, A, H, G, dt_bias=dtb, D=D, final_state=fs1, seg_chunks=seg)
+    torch.cuda.synchronize()
+    main = torch.cuda.current_stream()
+    streams = [torch.cuda.Stream() for _ in range(batch)]
+    y2 = torch.empty_like(y1)
+    fs2 = torch.empty_like(fs1)
+    for rep in range(3):
+        start = torch.cuda.Event()
+        start.record(main)
+        for r, s in enumerate(streams):
+            s.wait_event(start)
+            ssd.ssd_conv_scan_fwd(xbc[r:r + 1], cw, dt[r:r + 1], A, H, G, dt_bias=dtb, D=D,
+                                  final_state=fs2[r:r + 1], y=y2[r:r + 1], seg_chunks=seg, stream=s)
+        for s in streams:
+            e = torch.cuda.Event()
+            e.record(s)
+            main.wait_event(e)
+        torch.cuda.synchronize()
+        assert torch.equal(y2, y1), f"repeat {rep}"
+        assert torch.equal(fs2, fs1), f"repeat {rep}"
