@@ -104,23 +104,32 @@ __device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
 }
 
 // bf16 inputs on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16): lane
-// (l16, kq) holds K values 8 kq .. 8 kq + 7 of its operand row / column, and
-// the accumulator layout is that of v_mfma_f32_16x16x4_f32 (rows 4 kq .. +3,
+// (l16, kq) holds 8 K values of its operand row / column, and the
+// accumulator layout is that of v_mfma_f32_16x16x4_f32 (rows 4 kq .. +3,
 // column l16).  Operands that are bf16 numbers (x, dy, B, C) convert exactly;
 // fp32 intermediates (the adjoint, the entering state, the masked token
 // products) go in as bf16 parts hi = bf16(v), lo = bf16(v - hi), two
 // products, so each carries about 16 bits.
+// The K values of lane group kq in a 32-wide k-step are, in slot order e,
+// 4 kq + (e & 3) + 16 (e >> 2) (any order works as long as both operands of
+// a product use it).  With rows padded to 4 (mod 64) floats, a column read
+// by the four groups then touches rows 4 apart, 16 banks apart, and the
+// wave's 64 lanes fall on 64 banks; 8 consecutive K values per group put the
+// groups' rows 8 apart, 32 banks apart: a two-way conflict on every read.
 struct F8 {
   float v[8];
 };
-__device__ __forceinline__ F8 ld8(const float *p) {  // 8 consecutive floats (16-byte aligned)
-  const f32x4 a = *reinterpret_cast<const f32x4 *>(p), b = *reinterpret_cast<const f32x4 *>(p + 4);
+// slots 0..7 of group kq from a row whose k-step starts at p (16-byte aligned)
+__device__ __forceinline__ F8 ld8(const float *p, int kq) {
+  const f32x4 a = *reinterpret_cast<const f32x4 *>(p + 4 * kq);
+  const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4 * kq + 16);
   return F8{{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]}};
 }
-template <int kStride> __device__ __forceinline__ F8 ld8s(const float *p) {  // 8 floats kStride apart
+// ... from a column (K rows kStride floats apart) whose k-step starts at p
+template <int kStride> __device__ __forceinline__ F8 ld8s(const float *p, int kq) {
   F8 f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) f.v[e] = p[e * kStride];
+  for (int e = 0; e < 8; ++e) f.v[e] = p[(4 * kq + (e & 3) + 16 * (e >> 2)) * kStride];
   return f;
 }
 __device__ __forceinline__ bf16x8 exact8(const F8 &f) {
@@ -492,19 +501,22 @@ __global__ __launch_bounds__(kTC) void bwd_chunks_kernel(BwdParams p) {
         // over n: 4 k-steps of 32 (rows of every tile, 8 consecutive n per lane)
 #pragma unroll
         for (int st = 0; st < kN / 32; ++st) {
-          const int n0 = 32 * st + 8 * kq;
-          if (has_cb) tt = mfma32k(exact8(ld8(&s.C[bi(16 * mi + l16, n0)])), exact8(ld8(&s.B[bi(16 * ni + l16, n0)])), tt);
-          gb = mfma_es(exact8(ld8(&s.B[bi(jr, n0)])), split8(ld8(&s.G[gi(16 * qb + l16, n0)])), gb);
-          s0c = mfma_es(exact8(ld8(&s.C[bi(jr, n0)])), split8(ld8(&s.S0[gi(16 * qb + l16, n0)])), s0c);
+          const int n0 = 32 * st;
+          if (has_cb)
+            tt = mfma32k(exact8(ld8(&s.C[bi(16 * mi + l16, n0)], kq)), exact8(ld8(&s.B[bi(16 * ni + l16, n0)], kq)), tt);
+          gb = mfma_es(exact8(ld8(&s.B[bi(jr, n0)], kq)), split8(ld8(&s.G[gi(16 * qb + l16, n0)], kq)), gb);
+          s0c = mfma_es(exact8(ld8(&s.C[bi(jr, n0)], kq)), split8(ld8(&s.S0[gi(16 * qb + l16, n0)], kq)), s0c);
         }
         // over p: 2 k-steps of 32; G1's columns are read down the p rows
 #pragma unroll
         for (int st = 0; st < kP / 32; ++st) {
-          const int p0 = 32 * st + 8 * kq;
-          if (!has_cb) tt = mfma32k(exact8(ld8(&s.DY[xi(16 * mi + l16, p0)])), exact8(ld8(&s.X[xi(16 * ni + l16, p0)])), tt);
-          const bf16x8 xr = exact8(ld8(&s.X[xi(jr, p0)]));
+          const int p0 = 32 * st;
+          if (!has_cb)
+            tt = mfma32k(exact8(ld8(&s.DY[xi(16 * mi + l16, p0)], kq)), exact8(ld8(&s.X[xi(16 * ni + l16, p0)], kq)), tt);
+          const bf16x8 xr = exact8(ld8(&s.X[xi(jr, p0)], kq));
 #pragma unroll
-          for (int t = 0; t < 2; ++t) xg[t] = mfma_es(xr, split8(ld8s<kNP>(&s.G[gi(p0, 16 * (nb0 + t) + l16)])), xg[t]);
+          for (int t = 0; t < 2; ++t)
+            xg[t] = mfma_es(xr, split8(ld8s<kNP>(&s.G[gi(p0, 16 * (nb0 + t) + l16)], kq)), xg[t]);
         }
       } else {
       // contractions over n: C B^T (waves 0..3), B G1^T, C S0^T
@@ -657,11 +669,11 @@ __global__ __launch_bounds__(kTC) void bwd_chunks_kernel(BwdParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) g0[t][r] = eQ * s.G[gi(16 * qb + 4 * kq + r, 16 * (gn0 + t) + l16)];
       if constexpr (kBf) {
-        // over the chunk's 32 tokens: one k-step, tokens k0 .. k0 + 7 per lane
-        const int k0 = 8 * kq;
-        const F8 lm = ld8s<kQP>(&s.Lm[qi(k0, jr)]), cb = ld8s<kQP>(&s.CB[qi(k0, jr)]),
-                 dyx = ld8s<kQP>(&s.DYX[qi(k0, jr)]), dy = ld8s<kPP>(&s.DY[xi(k0, 16 * qb + l16)]);
-        const F8 lr = ld8(&s.Lm[qi(jr, k0)]), dr = ld8(&s.DYX[qi(jr, k0)]), dtk = ld8(&s.dt[k0]), ek = ld8(&s.ei[k0]);
+        // over the chunk's 32 tokens: one k-step, 8 tokens per lane group
+        const F8 lm = ld8s<kQP>(&s.Lm[qi(0, jr)], kq), cb = ld8s<kQP>(&s.CB[qi(0, jr)], kq),
+                 dyx = ld8s<kQP>(&s.DYX[qi(0, jr)], kq), dy = ld8s<kPP>(&s.DY[xi(0, 16 * qb + l16)], kq);
+        const F8 lr = ld8(&s.Lm[qi(jr, 0)], kq), dr = ld8(&s.DYX[qi(jr, 0)], kq), dtk = ld8(&s.dt[0], kq),
+                 ek = ld8(&s.ei[0], kq);
         F8 lcb, ldyx, ldt, edy;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -674,22 +686,24 @@ __global__ __launch_bounds__(kTC) void bwd_chunks_kernel(BwdParams p) {
         const Split8 sdyx = split8(ldyx), sdt = split8(ldt), sedy = split8(edy);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          ab[t] = mfma_se(sdyx, exact8(ld8s<kNP>(&s.C[bi(k0, 16 * (nb0 + t) + l16)])), ab[t]);
-          ac[t] = mfma_se(sdt, exact8(ld8s<kNP>(&s.B[bi(k0, 16 * (nb0 + t) + l16)])), ac[t]);
+          ab[t] = mfma_se(sdyx, exact8(ld8s<kNP>(&s.C[bi(0, 16 * (nb0 + t) + l16)], kq)), ab[t]);
+          ac[t] = mfma_se(sdt, exact8(ld8s<kNP>(&s.B[bi(0, 16 * (nb0 + t) + l16)], kq)), ac[t]);
         }
 #pragma unroll
-        for (int t = 0; t < 4; ++t) g0[t] = mfma_se(sedy, exact8(ld8s<kNP>(&s.C[bi(k0, 16 * (gn0 + t) + l16)])), g0[t]);
+        for (int t = 0; t < 4; ++t)
+          g0[t] = mfma_se(sedy, exact8(ld8s<kNP>(&s.C[bi(0, 16 * (gn0 + t) + l16)], kq)), g0[t]);
         // ... and over p (2 k-steps): the e_j S0^T dy_j term of dC
         const float ej = s.ei[jr];
 #pragma unroll
         for (int st = 0; st < kP / 32; ++st) {
-          const int p0 = 32 * st + 8 * kq;
-          F8 a = ld8(&s.DY[xi(jr, p0)]);
+          const int p0 = 32 * st;
+          F8 a = ld8(&s.DY[xi(jr, p0)], kq);
 #pragma unroll
           for (int e = 0; e < 8; ++e) a.v[e] *= ej;
           const Split8 sa = split8(a);
 #pragma unroll
-          for (int t = 0; t < 2; ++t) ac[t] = mfma_ss(sa, split8(ld8s<kNP>(&s.S0[gi(p0, 16 * (nb0 + t) + l16)])), ac[t]);
+          for (int t = 0; t < 2; ++t)
+            ac[t] = mfma_ss(sa, split8(ld8s<kNP>(&s.S0[gi(p0, 16 * (nb0 + t) + l16)], kq)), ac[t]);
         }
       } else {
       // contractions over the chunk's tokens (k); dy_k[16 qb + l16] is both the
