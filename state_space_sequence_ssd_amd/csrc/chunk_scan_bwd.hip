@@ -318,9 +318,13 @@ __global__ __launch_bounds__(kT) void bwd_states_kernel(BwdParams p) {
 // bf16(v - hi), so the two products carry w x to about 2^-16 of its size,
 // far below the rounding of the bf16 inputs themselves.  The tiles stay
 // token-major in LDS (rows padded by 32 bytes) and the operands, whose K runs
-// over tokens, come from the LDS transpose read: in each 16-lane group (k slot
-// kq: tokens 8 kq .. 8 kq + 7) lane s points at token row k0 + s / 4, columns
-// c0 + 4 (s % 4) .. + 3, and receives tokens k0 .. k0 + 3 of column c0 + s.
+// over tokens, come from the LDS transpose read: in each 16-lane group lane s
+// points at token row k0 + s / 4, columns c0 + 4 (s % 4) .. + 3, and receives
+// tokens k0 .. k0 + 3 of column c0 + s.  Group kq takes tokens 4 kq .. + 3
+// and 16 + 4 kq .. + 3 (the same order in both operands), so one read by the
+// four groups covers 16 consecutive rows; with rows 8 or 40 banks apart (288-
+// and 160-byte rows) those fall on distinct banks, where tokens 8 kq .. + 7
+// put rows 8 apart on the same banks.
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 constexpr int kXR = 2 * kP + 32, kBR = 2 * kN + 32;  // bytes per staged row
@@ -328,7 +332,7 @@ __device__ __forceinline__ bf16x8 tr_frag(const uint8_t *tile, int pitch, int k0
   const int s = lane & 15;
   const uint8_t *a = tile + (k0 + (s >> 2)) * pitch + 2 * (c0 + 4 * (s & 3));
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)a);
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(a + 4 * pitch));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(a + 16 * pitch));
   const u32x2 l = __builtin_bit_cast(u32x2, lo), h = __builtin_bit_cast(u32x2, hi);
   return __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], h[0], h[1]});
 }
@@ -389,11 +393,11 @@ __global__ __launch_bounds__(kT) void bwd_states_bf16_kernel(BwdParams p) {
 #pragma unroll
     for (int t = 0; t < 8; ++t) acc[t] *= dec;
     // A = (w x)^T (rows p, K = tokens), B = B (K = tokens, columns n)
-    const bf16x8 ah = tr_frag(sXh, kXR, 8 * kq, 16 * wave, lane);
-    const bf16x8 al = tr_frag(sXl, kXR, 8 * kq, 16 * wave, lane);
+    const bf16x8 ah = tr_frag(sXh, kXR, 4 * kq, 16 * wave, lane);
+    const bf16x8 al = tr_frag(sXl, kXR, 4 * kq, 16 * wave, lane);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const bf16x8 bt = tr_frag(sB, kBR, 8 * kq, 16 * t, lane);
+      const bf16x8 bt = tr_frag(sB, kBR, 4 * kq, 16 * t, lane);
       acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bt, acc[t], 0, 0, 0);
       acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bt, acc[t], 0, 0, 0);
     }
