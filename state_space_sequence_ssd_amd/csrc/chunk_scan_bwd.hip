@@ -260,6 +260,22 @@ __device__ __forceinline__ void pipelined(FL load, FM mma) {
 // The tiles are read with the token (k) on the lane's k slot and the column
 // on its 16-lane index: rows padded to 16 (mod 64) floats put the four k
 // slots on four different 16-bank groups.
+// The workspace keeps each chunk's entering state in the order the states
+// pass holds it: float4 number (8 w + t) 64 + lane is rows 16 w + 4 kq .. + 3
+// of column 16 t + l16 (wave w, tile t, lane = 16 kq + l16), so every store
+// is a whole 16-byte vector and each store instruction writes 1 KiB in a
+// row.  Only the reverse pass reads it back (state_elem gives the element).
+__device__ __forceinline__ void store_state(float *dst, const f32x4 *acc, int wave, int lane) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) *reinterpret_cast<f32x4 *>(dst + 4 * ((8 * wave + t) * 64 + lane)) = acc[t];
+}
+// row p and column n of float4 number f of a stored state (its element r is row p + r)
+__device__ __forceinline__ void state_elem(int f, int &p, int &n) {
+  const int w = f >> 9, t = (f >> 6) & 7, ln = f & 63;
+  p = 16 * w + 4 * (ln >> 4);
+  n = 16 * t + (ln & 15);
+}
+
 constexpr int kXSP = kP + 16;   // padded rows of the staged x (w x) and B tiles
 constexpr int kBSP = kN + 16;
 template <typename T>
@@ -287,11 +303,8 @@ __global__ __launch_bounds__(kT) void bwd_states_kernel(BwdParams p) {
   if (p.nchunks > 0) load_chunk(0);
   for (int c = 0; c < p.nchunks; ++c) {
     const int t0 = c * kQ, nv = min(kQ, p.L - t0);
-    // the state entering this chunk
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) states[(int64_t)c * kPN + (16 * wave + 4 * kq + r) * kN + 16 * t + l16] = acc[t][r];
+    // the state entering this chunk, in the accumulators' own order
+    store_state(states + (int64_t)c * kPN, acc, wave, lane);
     chunk_dt<T>(p, b, h, t0, nv, s_dt, s_cs, s_z);
     rb.template store<kBSP>(sB, tid, [](int) { return 1.f; });
     __syncthreads();  // dt, cs
@@ -359,10 +372,7 @@ __global__ __launch_bounds__(kT) void bwd_states_bf16_kernel(BwdParams p) {
   if (p.nchunks > 0) load_chunk(0);
   for (int c = 0; c < p.nchunks; ++c) {
     const int t0 = c * kQ, nv = min(kQ, p.L - t0);
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) states[(int64_t)c * kPN + (16 * wave + 4 * kq + r) * kN + 16 * t + l16] = acc[t][r];
+    store_state(states + (int64_t)c * kPN, acc, wave, lane);
     chunk_dt<bf16_t>(p, b, h, t0, nv, s_dt, s_cs, s_z);
 #pragma unroll
     for (int i = 0; i < rb.kPieces; ++i) {
@@ -476,8 +486,10 @@ __global__ __launch_bounds__(kTC) void bwd_chunks_kernel(BwdParams p) {
       chunk_dt<T>(p, b, h, t0, nv, s.dt, s.cs, s.z);
 #pragma unroll
       for (int i = 0; i < kS0; ++i) {
-        const int e = 4 * (tid + kTC * i);
-        *reinterpret_cast<f32x4 *>(&s.S0[gi(e / kN, e % kN)]) = s0[i];
+        int sp, sn;
+        state_elem(tid + kTC * i, sp, sn);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s.S0[gi(sp + r, sn)] = s0[i][r];
       }
       const auto one = [](int) { return 1.f; };
       rx.store_at(s.X, tid, xi, one);
@@ -797,25 +809,39 @@ __global__ __launch_bounds__(kTC) void bwd_chunks_kernel(BwdParams p) {
 // 3. fixed-order sums: dB, dC over the heads of a group; the per-head
 //    scalars over the rows
 // -------------------------------------------------------------------------
+// four consecutive outputs (element e, a multiple of 4) in one store
+template <typename T> __device__ __forceinline__ void store4(void *base, int64_t e, f32x4 v);
+template <> __device__ __forceinline__ void store4<float>(void *base, int64_t e, f32x4 v) {
+  *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(base) + e) = v;
+}
+template <> __device__ __forceinline__ void store4<bf16_t>(void *base, int64_t e, f32x4 v) {
+  *reinterpret_cast<u32x2 *>(reinterpret_cast<bf16_t *>(base) + e) = u32x2{pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3])};
+}
+
+// Each thread sums 4 consecutive n of one (row, token, group) over the
+// group's heads, in head order: 16-byte loads of the partials (read once,
+// non-temporal) and one store per output vector.
 template <typename T>
 __global__ __launch_bounds__(kT) void bwd_reduce_kernel(BwdParams p) {
-  const int64_t e = (int64_t)blockIdx.x * kT + threadIdx.x;
+  const int64_t tid = (int64_t)blockIdx.x * kT + threadIdx.x;
   const int hpg = p.H / p.G;
-  const int64_t total = (int64_t)p.batch * p.L * p.G * kN;
-  if (e < total) {
+  const int64_t total4 = (int64_t)p.batch * p.L * p.G * kN / 4;
+  if (tid < total4) {
+    const int64_t e = 4 * tid;
     const int n = (int)(e % kN);
     const int64_t r = e / kN;
     const int gi = (int)(r % p.G);
     const int64_t bt = r / p.G;
-    float sb = 0.f, sc = 0.f;
+    f32x4 sb = f32x4{}, sc = f32x4{};
     for (int k = 0; k < hpg; ++k) {
       const int64_t o = (bt * p.H + gi * hpg + k) * kN + n;
-      sb += p.ws_dB[o];
-      sc += p.ws_dC[o];
+      sb += __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p.ws_dB + o));
+      sc += __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p.ws_dC + o));
     }
-    reinterpret_cast<T *>(p.dB)[e] = from_f32<T>(sb);
-    reinterpret_cast<T *>(p.dC)[e] = from_f32<T>(sc);
+    store4<T>(p.dB, e, sb);
+    store4<T>(p.dC, e, sc);
   }
+  const int64_t e = tid;
   if (e < p.H) {
     float a = 0.f, d = 0.f, bi = 0.f;
     for (int b = 0; b < p.batch; ++b) {
@@ -844,7 +870,7 @@ hipError_t launch_t(const BwdParams &p, hipStream_t stream) {
   hipLaunchKernelGGL(bwd_chunks_kernel<T>, dim3(units), dim3(kTC), lds, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t total = std::max<int64_t>((int64_t)p.batch * p.L * p.G * kN, p.H);
+  const int64_t total = std::max<int64_t>((int64_t)p.batch * p.L * p.G * kN / 4, p.H);
   hipLaunchKernelGGL(bwd_reduce_kernel<T>, dim3((unsigned)((total + kT - 1) / kT)), dim3(kT), 0, stream, p);
   return hipGetLastError();
 }
