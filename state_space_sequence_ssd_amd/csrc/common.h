@@ -83,9 +83,22 @@ template <int CNT, int BIT> struct RowScatter {
     }
   }
 };
+// The sum of the two 16-lane rows of each half-wave, in every lane of both:
+// v_permlane16_swap with the value as both operands leaves row 0 of each
+// half in the first result and row 1 in the second (a VALU op, no LDS).
+__device__ __forceinline__ float cross_row_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// ... and of the two half-waves (v_permlane32_swap).
+__device__ __forceinline__ float cross_half_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <int CNT> struct RowScatter<CNT, -1> {
   static_assert(CNT == 1, "at most 16 sums per row");
-  static __device__ __forceinline__ void run(float *part, int, int &) { part[0] += __shfl_xor(part[0], 16, 32); }
+  static __device__ __forceinline__ void run(float *part, int, int &) { part[0] = cross_row_sum(part[0]); }
 };
 // lanes holding a finished sum with every all-reduced bit zero: one writer per column
 template <int R> constexpr int kRowWriterMask = 0x10 | ((16 / R) - 1);
@@ -98,15 +111,9 @@ __device__ __forceinline__ float row_sum16(float v) {
   return v + row_pair<0>(v);
 }
 // ... over the 32 lanes of a half-wave (the last step crosses the two rows).
-__device__ __forceinline__ float half_wave_sum(float v) {
-  v = row_sum16(v);
-  return v + __shfl_xor(v, 16, 32);
-}
+__device__ __forceinline__ float half_wave_sum(float v) { return cross_row_sum(row_sum16(v)); }
 // ... over the whole wave.
-__device__ __forceinline__ float wave_sum(float v) {
-  v = half_wave_sum(v);
-  return v + __shfl_xor(v, 32, 64);
-}
+__device__ __forceinline__ float wave_sum(float v) { return cross_half_sum(half_wave_sum(v)); }
 
 template <typename T> __device__ __forceinline__ float to_f32(T v);
 template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }

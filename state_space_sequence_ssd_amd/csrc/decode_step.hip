@@ -17,7 +17,7 @@
 // pieces of 8 KiB; every load instruction covers two whole state rows, so
 // the workgroup walks all of its heads' states at once.  A state row (128
 // floats) is 32 lanes x float4, so y[p] is a 32-lane sum (DPP moves within
-// each 16-lane row, one exchange across the two); y is staged in LDS and
+// each 16-lane row, a permlane swap across the two); y is staged in LDS and
 // written once per group.
 #include "common.h"
 #include "kernels.h"
