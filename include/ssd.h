@@ -387,7 +387,10 @@ int ssd_decode_step(const ssd_decode_args *args, void *stream);
  *
  * The workspace (ssd_chunk_scan_bwd_workspace_size bytes, 256-byte aligned)
  * holds the state entering every chunk and per-head partial sums: about
- * batch x nheads x (seqlen / 32 x 32 KiB + seqlen x 1 KiB).
+ * batch x nheads x (seqlen / 32 x 32 KiB + seqlen x 1 KiB).  With BF16
+ * inputs the stored chunk states are rounded to bf16 (the forward pass's
+ * own precision for the state in its state->output product) and use half
+ * of their region; with F32 inputs they stay fp32.
  *
  * Supported: headdim 64, dstate 128, dtype F32 or BF16, batch rows (no
  * seq_idx); x, B, C, dy, dt and the states 16-byte aligned.

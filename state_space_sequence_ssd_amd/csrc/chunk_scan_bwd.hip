@@ -269,6 +269,19 @@ __device__ __forceinline__ void store_state(float *dst, const f32x4 *acc, int wa
 #pragma unroll
   for (int t = 0; t < 8; ++t) *reinterpret_cast<f32x4 *>(dst + 4 * ((8 * wave + t) * 64 + lane)) = acc[t];
 }
+// bf16 inputs: the same order with each float4 rounded to four bf16 (8 bytes,
+// 512 B per store instruction).  The reverse pass's products with the
+// entering state then take it as one bf16 operand, as the forward pass's
+// state->output product takes its bf16 copy of the state.
+__device__ __forceinline__ void store_state_bf16(bf16_t *dst, const f32x4 *acc, int wave, int lane) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    u32x2 v;
+    v[0] = pack2_bf16(acc[t][0], acc[t][1]);
+    v[1] = pack2_bf16(acc[t][2], acc[t][3]);
+    *reinterpret_cast<u32x2 *>(dst + 4 * ((8 * wave + t) * 64 + lane)) = v;
+  }
+}
 // row p and column n of float4 number f of a stored state (its element r is row p + r)
 __device__ __forceinline__ void state_elem(int f, int &p, int &n) {
   const int w = f >> 9, t = (f >> 6) & 7, ln = f & 63;
@@ -354,7 +367,7 @@ __global__ __launch_bounds__(kT) void bwd_states_bf16_kernel(BwdParams p) {
   __shared__ float s_dt[kQ], s_cs[kQ], s_z[kQ];
   const int b = blockIdx.x / p.H, h = blockIdx.x % p.H, g = h / (p.H / p.G);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, kq = lane >> 4;
-  float *states = p.ws_states + ((int64_t)b * p.H + h) * p.nchunks * kPN;
+  bf16_t *states = reinterpret_cast<bf16_t *>(p.ws_states) + ((int64_t)b * p.H + h) * p.nchunks * kPN;
   // this wave's tiles: rows p in [16 wave, +16), columns n in [16 t, +16), t = 0..7
   f32x4 acc[8];
   const float *h0 = p.init ? p.init + ((int64_t)b * p.H + h) * kPN : nullptr;
@@ -372,7 +385,7 @@ __global__ __launch_bounds__(kT) void bwd_states_bf16_kernel(BwdParams p) {
   if (p.nchunks > 0) load_chunk(0);
   for (int c = 0; c < p.nchunks; ++c) {
     const int t0 = c * kQ, nv = min(kQ, p.L - t0);
-    store_state(states + (int64_t)c * kPN, acc, wave, lane);
+    store_state_bf16(states + (int64_t)c * kPN, acc, wave, lane);
     chunk_dt<bf16_t>(p, b, h, t0, nv, s_dt, s_cs, s_z);
 #pragma unroll
     for (int i = 0; i < rb.kPieces; ++i) {
@@ -457,7 +470,7 @@ __global__ __launch_bounds__(kTC) void bwd_chunks_kernel(BwdParams p) {
   const int b = blockIdx.x / p.H, h = blockIdx.x % p.H, g = h / (p.H / p.G);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, kq = lane >> 4;
   const float Ah = p.A[h], Dh = p.D ? p.D[h] : 0.f;
-  const float *states = p.ws_states + ((int64_t)b * p.H + h) * p.nchunks * kPN;
+  const int64_t st0 = ((int64_t)b * p.H + h) * p.nchunks * kPN;  // this (row, head)'s states
   for (int e = tid; e < kPN; e += kTC)
     s.G[gi(e / kN, e % kN)] = p.dfinal ? p.dfinal[((int64_t)b * p.H + h) * kPN + e] : 0.f;
   float accA = 0.f, accD = 0.f, accBias = 0.f;
@@ -473,9 +486,24 @@ __global__ __launch_bounds__(kTC) void bwd_chunks_kernel(BwdParams p) {
     {
       constexpr int kS0 = kPN / 4 / kTC;
       f32x4 s0[kS0];
+      if constexpr (kBf) {
+        // four bf16 per float4 number (the bf16 states pass's format)
+        const bf16_t *states = reinterpret_cast<const bf16_t *>(p.ws_states) + st0 + (int64_t)c * kPN;
+        u32x2 sb[kS0];
 #pragma unroll
-      for (int i = 0; i < kS0; ++i)
-        s0[i] = *reinterpret_cast<const f32x4 *>(states + (int64_t)c * kPN + 4 * (tid + kTC * i));
+        for (int i = 0; i < kS0; ++i) sb[i] = *reinterpret_cast<const u32x2 *>(states + 4 * (tid + kTC * i));
+#pragma unroll
+        for (int i = 0; i < kS0; ++i) {
+          s0[i][0] = lo_bf16(sb[i][0]);
+          s0[i][1] = hi_bf16(sb[i][0]);
+          s0[i][2] = lo_bf16(sb[i][1]);
+          s0[i][3] = hi_bf16(sb[i][1]);
+        }
+      } else {
+        const float *states = p.ws_states + st0 + (int64_t)c * kPN;
+#pragma unroll
+        for (int i = 0; i < kS0; ++i) s0[i] = *reinterpret_cast<const f32x4 *>(states + 4 * (tid + kTC * i));
+      }
       ChunkRows<T, kP, kTC> rx, rdy;
       ChunkRows<T, kN, kTC> rb, rc;
       const int64_t xo = (((int64_t)b * p.L + t0) * p.H + h) * kP, bo = (((int64_t)b * p.L + t0) * p.G + g) * kN;
