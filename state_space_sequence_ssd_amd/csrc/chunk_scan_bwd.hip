@@ -160,10 +160,6 @@ __device__ __forceinline__ f32x4 mfma_es(bf16x8 a, const Split8 &b, f32x4 c) {
 __device__ __forceinline__ f32x4 mfma_se(const Split8 &a, bf16x8 b, f32x4 c) {
   return mfma32k(a.hi, b, mfma32k(a.lo, b, c));
 }
-// split times split: hi hi + hi lo + lo hi (the lo lo term is below 2^-16)
-__device__ __forceinline__ f32x4 mfma_ss(const Split8 &a, const Split8 &b, f32x4 c) {
-  return mfma32k(a.hi, b.hi, mfma32k(a.hi, b.lo, mfma32k(a.lo, b.hi, c)));
-}
 
 // Chunk operands move as 16-byte pieces: every thread issues all of its loads
 // of a chunk before the first one is used, so a chunk waits for one memory
@@ -549,7 +545,8 @@ __global__ __launch_bounds__(kTC) void bwd_chunks_kernel(BwdParams p) {
           if (has_cb)
             tt = mfma32k(exact8(ld8(&s.C[bi(16 * mi + l16, n0)], kq)), exact8(ld8(&s.B[bi(16 * ni + l16, n0)], kq)), tt);
           gb = mfma_es(exact8(ld8(&s.B[bi(jr, n0)], kq)), split8(ld8(&s.G[gi(16 * qb + l16, n0)], kq)), gb);
-          s0c = mfma_es(exact8(ld8(&s.C[bi(jr, n0)], kq)), split8(ld8(&s.S0[gi(16 * qb + l16, n0)], kq)), s0c);
+          // S0 holds the bf16 states pass's values, exact in bf16: one product
+          s0c = mfma32k(exact8(ld8(&s.C[bi(jr, n0)], kq)), exact8(ld8(&s.S0[gi(16 * qb + l16, n0)], kq)), s0c);
         }
         // over p: 2 k-steps of 32; G1's columns are read down the p rows
 #pragma unroll
@@ -747,7 +744,7 @@ __global__ __launch_bounds__(kTC) void bwd_chunks_kernel(BwdParams p) {
           const Split8 sa = split8(a);
 #pragma unroll
           for (int t = 0; t < 2; ++t)
-            ac[t] = mfma_ss(sa, split8(ld8s<kNP>(&s.S0[gi(p0, 16 * (nb0 + t) + l16)], kq)), ac[t]);
+            ac[t] = mfma_se(sa, exact8(ld8s<kNP>(&s.S0[gi(p0, 16 * (nb0 + t) + l16)], kq)), ac[t]);  // S0 exact
         }
       } else {
       // contractions over the chunk's tokens (k); dy_k[16 qb + l16] is both the
